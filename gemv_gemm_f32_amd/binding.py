@@ -1,0 +1,206 @@
+"""ctypes binding of libgemvgemm.so: the C entry points on torch tensors.
+
+Argument marshalling only: every step of every product runs in the HIP
+kernels behind the C ABI (include/gemvgemm.h).  torch supplies device memory
+and the current stream.  If the library has not been built this module
+raises; there is no fallback of any kind.
+
+Each tensor function has the name of its C entry point and takes row-major
+2-D tensors whose last dimension is contiguous; the row stride is passed as
+the leading dimension.  The output is written in place (allocated when not
+given) and returned.  A non-zero status raises ``GGError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgemvgemm.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "gemvgemm.h")
+
+GG_OK = 0
+GG_ERR_INVALID_ARG = -1
+GG_ERR_ALIAS = -2
+GG_ERR_NO_DEVICE = -3
+GG_ERR_LAUNCH = -4
+
+ENTRY_POINTS = ("gemm_f32", "gemm_f32_tn", "gemm_f32_nt", "gemv_f32", "gemv_q2",
+                "gg_strerror")
+
+_lib = None
+
+
+class GGError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, strerror(status), status))
+
+
+def load(path: str = LIB_PATH):
+    """Open the library (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    # torch ships its own HIP runtime (soname libamdhip64.so.7).  Importing it
+    # first makes this library's libamdhip64.so.7 dependency resolve to that
+    # already-loaded copy, so torch's streams and allocations and these
+    # kernels live in one runtime.  (Loaded first on its own, the library
+    # would pull in a second runtime, and torch's stream handles would be
+    # meaningless to it.)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(path):
+        raise RuntimeError(
+            "libgemvgemm.so is not built (%s); run `python -m gemv_gemm_f32_amd.build`"
+            % path)
+    lib = ctypes.CDLL(path)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    for name in ("gemm_f32", "gemm_f32_tn", "gemm_f32_nt"):
+        f = getattr(lib, name)
+        f.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
+        f.restype = ctypes.c_int
+    lib.gemv_f32.argtypes = [i64, i64, vp, i64, vp, vp, vp]
+    lib.gemv_f32.restype = ctypes.c_int
+    lib.gemv_q2.argtypes = [i64, i64, vp, i64, vp, i64, vp, vp, vp]
+    lib.gemv_q2.restype = ctypes.c_int
+    lib.gg_strerror.argtypes = [ctypes.c_int]
+    lib.gg_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load().gg_strerror(int(status)).decode()
+
+
+def header_functions(path: str = HEADER):
+    """Names of the functions declared in the public header."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+# ------------------------------------------------------------ tensor side --
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _mat(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device" % name)
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("%s must have a contiguous last dimension" % name)
+    ld = t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+    return t.data_ptr(), ld
+
+
+def _vec(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.device.type != "cuda":
+        raise TypeError("%s must be a %s GPU tensor" % (name, dtype))
+    if t.dim() != 1 or (t.numel() > 1 and t.stride(0) != 1):
+        raise ValueError("%s must be a contiguous vector" % name)
+    return t.data_ptr()
+
+
+def _check(status, where):
+    if status != GG_OK:
+        raise GGError(status, where)
+
+
+def _gemm(name, A, B, C, M, N, K, stream):
+    torch = _torch()
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if tuple(C.shape) != (M, N):
+        raise ValueError("C must be %d x %d" % (M, N))
+    pa, lda = _mat(A, torch.float32, "A")
+    pb, ldb = _mat(B, torch.float32, "B")
+    pc, ldc = _mat(C, torch.float32, "C")
+    _check(getattr(load(), name)(M, N, K, pa, lda, pb, ldb, pc, ldc, _stream(stream)), name)
+    return C
+
+
+def gemm_f32(A, B, C=None, stream=None):
+    """C = A.B with A (M x K) and B (K x N)."""
+    M, K = A.shape
+    if B.shape[0] != K:
+        raise ValueError("inner dimensions differ")
+    return _gemm("gemm_f32", A, B, C, M, B.shape[1], K, stream)
+
+
+def gemm_f32_tn(A, B, C=None, stream=None):
+    """C = A^T.B with A stored K x M and B (K x N)."""
+    K, M = A.shape
+    if B.shape[0] != K:
+        raise ValueError("inner dimensions differ")
+    return _gemm("gemm_f32_tn", A, B, C, M, B.shape[1], K, stream)
+
+
+def gemm_f32_nt(A, B, C=None, stream=None):
+    """C = A.B^T with A (M x K) and B stored N x K."""
+    M, K = A.shape
+    if B.shape[1] != K:
+        raise ValueError("inner dimensions differ")
+    return _gemm("gemm_f32_nt", A, B, C, M, B.shape[0], K, stream)
+
+
+def gemv_f32(W, x, y=None, stream=None):
+    """y = W.x with W (M x K) fp32 and x (K,) fp32."""
+    torch = _torch()
+    M, K = W.shape
+    if x.shape != (K,):
+        raise ValueError("x must have K entries")
+    if y is None:
+        y = torch.empty(M, dtype=torch.float32, device=W.device)
+    if y.shape != (M,):
+        raise ValueError("y must have M entries")
+    pw, ldw = _mat(W, torch.float32, "W")
+    _check(load().gemv_f32(M, K, pw, ldw, _vec(x, torch.float32, "x"),
+                           _vec(y, torch.float32, "y"), _stream(stream)), "gemv_f32")
+    return y
+
+
+def gemv_q2(Q, S, x, y=None, stream=None):
+    """y = W.x with W as 2-bit codes Q (uint8, M x >= ceil(K/4)) and binary16
+    scales S (float16 or int16 bit patterns, M x >= ceil(K/64)); x (K,) fp32."""
+    torch = _torch()
+    M = Q.shape[0]
+    K = x.shape[0]
+    if S.shape[0] != M:
+        raise ValueError("Q and S must have the same number of rows")
+    if S.dtype in (torch.float16, torch.int16):
+        S = S.view(torch.float16)
+    else:
+        raise TypeError("S must hold binary16 bit patterns (float16 or int16)")
+    if y is None:
+        y = torch.empty(M, dtype=torch.float32, device=Q.device)
+    if y.shape != (M,):
+        raise ValueError("y must have M entries")
+    pq, ldq = _mat(Q, torch.uint8, "Q")
+    ps, lds = _mat(S, torch.float16, "S")
+    _check(load().gemv_q2(M, K, pq, ldq, ps, lds, _vec(x, torch.float32, "x"),
+                          _vec(y, torch.float32, "y"), _stream(stream)), "gemv_q2")
+    return y

@@ -1,0 +1,154 @@
+// api.hip -- the C entry points of libgemvgemm.so (declared in gemvgemm.h).
+//
+// Each entry point validates its arguments before any HIP call and before
+// anything is written, checks once per device that the current device is a
+// gfx950, launches one kernel on the caller's stream, and maps a rejected
+// launch to a status.  No exception or abort leaves this file.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/gemvgemm.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = INT32_MAX;   // sizes must be below 2^31
+constexpr int kMaxDevices = 64;
+
+// Per-device cache of "is gfx950": 0 unknown, 1 yes, 2 no.  Filled without a
+// lock; a race only repeats the query and stores the same answer.
+std::atomic<int> g_device_ok[kMaxDevices];
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GG_ERR_NO_DEVICE;
+    if (dev < kMaxDevices) {
+        const int known = g_device_ok[dev].load(std::memory_order_relaxed);
+        if (known == 1) return GG_OK;
+        if (known == 2) return GG_ERR_NO_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GG_ERR_NO_DEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices) g_device_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? GG_OK : GG_ERR_NO_DEVICE;
+}
+
+// Byte range [lo, hi) of a rows x cols matrix with leading dimension ld.
+struct Span {
+    uintptr_t lo, hi;
+};
+
+Span span(const void *p, int64_t rows, int64_t cols, int64_t ld, int64_t elem) {
+    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+    if (rows <= 0 || cols <= 0) return {b, b};
+    return {b, b + (uintptr_t)(((rows - 1) * ld + cols) * elem)};
+}
+
+bool overlaps(Span a, Span b) {
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool bad_ptr(const void *p, int64_t align) {
+    return p == nullptr || (reinterpret_cast<uintptr_t>(p) % (uintptr_t)align) != 0;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? GG_OK : GG_ERR_LAUNCH; }
+
+int gemm_common(gg::GemmLayout layout, int64_t M, int64_t N, int64_t K, const float *A,
+                int64_t lda, const float *B, int64_t ldb, float *C, int64_t ldc,
+                gg_stream_t stream) {
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return GG_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return GG_OK;
+    // Stored shapes: A is M x K (NN, NT) or K x M (TN); B is K x N (NN, TN)
+    // or N x K (NT).
+    const bool ta = layout == gg::GemmLayout::TN, tb = layout == gg::GemmLayout::NT;
+    const int64_t a_rows = ta ? K : M, a_cols = ta ? M : K;
+    const int64_t b_rows = tb ? N : K, b_cols = tb ? K : N;
+    if (bad_ptr(C, 4)) return GG_ERR_INVALID_ARG;
+    if (K > 0 && (bad_ptr(A, 4) || bad_ptr(B, 4))) return GG_ERR_INVALID_ARG;
+    if (ldc < N || ldc > kMaxDim) return GG_ERR_INVALID_ARG;
+    if (K > 0 && (lda < a_cols || ldb < b_cols || lda > kMaxDim || ldb > kMaxDim))
+        return GG_ERR_INVALID_ARG;
+    const Span c = span(C, M, N, ldc, 4);
+    if (K > 0 && (overlaps(c, span(A, a_rows, a_cols, lda, 4)) ||
+                  overlaps(c, span(B, b_rows, b_cols, ldb, 4))))
+        return GG_ERR_ALIAS;
+    if (int st = check_device()) return st;
+    (void)hipGetLastError();   // clear a stale error so the check below is ours
+    return launch_status(gg::launch_gemm(layout, (int)M, (int)N, (int)K, A, lda, B, ldb, C,
+                                         ldc, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f32(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+             int64_t ldb, float *C, int64_t ldc, gg_stream_t stream) {
+    return gemm_common(gg::GemmLayout::NN, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int gemm_f32_tn(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+                int64_t ldb, float *C, int64_t ldc, gg_stream_t stream) {
+    return gemm_common(gg::GemmLayout::TN, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int gemm_f32_nt(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+                int64_t ldb, float *C, int64_t ldc, gg_stream_t stream) {
+    return gemm_common(gg::GemmLayout::NT, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int gemv_f32(int64_t M, int64_t K, const float *W, int64_t ldw, const float *x, float *y,
+             gg_stream_t stream) {
+    if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim) return GG_ERR_INVALID_ARG;
+    if (M == 0) return GG_OK;
+    if (bad_ptr(y, 4)) return GG_ERR_INVALID_ARG;
+    if (K > 0 && (bad_ptr(W, 4) || bad_ptr(x, 4))) return GG_ERR_INVALID_ARG;
+    if (K > 0 && (ldw < K || ldw > kMaxDim)) return GG_ERR_INVALID_ARG;
+    const Span ys = span(y, 1, M, M, 4);
+    if (K > 0 && (overlaps(ys, span(W, M, K, ldw, 4)) || overlaps(ys, span(x, 1, K, K, 4))))
+        return GG_ERR_ALIAS;
+    if (int st = check_device()) return st;
+    (void)hipGetLastError();
+    return launch_status(gg::launch_gemv_f32((int)M, (int)K, W, ldw, x, y,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+int gemv_q2(int64_t M, int64_t K, const uint8_t *Q, int64_t ldq, const uint16_t *S,
+            int64_t lds, const float *x, float *y, gg_stream_t stream) {
+    if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim) return GG_ERR_INVALID_ARG;
+    if (M == 0) return GG_OK;
+    if (bad_ptr(y, 4)) return GG_ERR_INVALID_ARG;
+    const int64_t qcols = (K + 3) / 4, scols = (K + 63) / 64;
+    if (K > 0 && (bad_ptr(Q, 1) || bad_ptr(S, 2) || bad_ptr(x, 4))) return GG_ERR_INVALID_ARG;
+    if (K > 0 && (ldq < qcols || lds < scols || ldq > kMaxDim || lds > kMaxDim))
+        return GG_ERR_INVALID_ARG;
+    const Span ys = span(y, 1, M, M, 4);
+    if (K > 0 && (overlaps(ys, span(Q, M, qcols, ldq, 1)) ||
+                  overlaps(ys, span(S, M, scols, lds, 2)) || overlaps(ys, span(x, 1, K, K, 4))))
+        return GG_ERR_ALIAS;
+    if (int st = check_device()) return st;
+    (void)hipGetLastError();
+    return launch_status(gg::launch_gemv_q2((int)M, (int)K, Q, ldq, S, lds, x, y,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
+const char *gg_strerror(int status) {
+    switch (status) {
+        case GG_OK: return "success";
+        case GG_ERR_INVALID_ARG:
+            return "invalid argument: negative or oversized size, null or misaligned "
+                   "pointer, or leading dimension smaller than the row width";
+        case GG_ERR_ALIAS: return "output overlaps an input";
+        case GG_ERR_NO_DEVICE: return "no current HIP device, or it is not a gfx950 (MI355X)";
+        case GG_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

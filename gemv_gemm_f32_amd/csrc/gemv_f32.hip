@@ -1,0 +1,125 @@
+// gemv_f32.hip -- fp32 y = W.x, bound by streaming W from HBM.
+//
+// The one-row matrix-vector path of "More Stumbling, This Time in the
+// Browser" (section "Four answers per worker") at the 12,288 x 1,536 shape of
+// "Kernel 0112" (section "What is being measured").  That page finds that the
+// original kernel launched too few threads to keep enough reads in flight and
+// that splitting each dot product over more threads paid (sections "What is
+// being measured" and "The four variants").  On CDNA4 the split is a whole
+// wave64 per row:
+//
+//  * Lane l reads the 16-byte chunks l, l+64, l+128, ... of a row, so each
+//    load instruction covers 1 KiB of contiguous row.  Each wave owns R
+//    consecutive rows and issues all R x U chunk loads of a pass before using
+//    any of them, which keeps R x U KiB per wave in flight.
+//  * The matching chunks of x are loaded once per pass and reused for the R
+//    rows; x is 6 KiB and stays in L2/L1.
+//  * A row's 64 partial sums are added with the DPP/swizzle tree of wave.hpp;
+//    lane 0 writes y.
+//  * Scalar-load specialisation of the same kernel for K, ldw or a base that
+//    is not a multiple of 4 floats.
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+#include "wave.hpp"
+
+namespace gg {
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int THREADS = 256;
+constexpr int WAVES = THREADS / 64;
+
+template <int R, int U, bool VEC>
+__global__ __launch_bounds__(THREADS) void gemv_f32_kernel(
+    int M, int K, const float *__restrict__ W, int64_t ldw,
+    const float *__restrict__ x, float *__restrict__ y) {
+    const int lane = threadIdx.x & 63;
+    const int row0 = (blockIdx.x * WAVES + (threadIdx.x >> 6)) * R;
+    if (row0 >= M) return;   // uniform per wave
+
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+
+    if (VEC) {
+        const int nv = K >> 2;                       // 16-byte chunks per row
+        const v4f *x4 = reinterpret_cast<const v4f *>(x);
+        for (int c0 = 0; c0 < nv; c0 += 64 * U) {
+            v4f xv[U];
+            v4f wv[R][U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + lane + 64 * u;
+                xv[u] = c < nv ? x4[c] : v4f{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const v4f *wr = reinterpret_cast<const v4f *>(W + (int64_t)(row0 + r) * ldw);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + lane + 64 * u;
+                    wv[r][u] = (c < nv && row0 + r < M) ? wr[c] : v4f{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    acc[r] = __builtin_fmaf(wv[r][u].x, xv[u].x, acc[r]);
+                    acc[r] = __builtin_fmaf(wv[r][u].y, xv[u].y, acc[r]);
+                    acc[r] = __builtin_fmaf(wv[r][u].z, xv[u].z, acc[r]);
+                    acc[r] = __builtin_fmaf(wv[r][u].w, xv[u].w, acc[r]);
+                }
+        }
+    } else {
+        for (int k0 = 0; k0 < K; k0 += 64 * U) {
+            float xv[U];
+            float wv[R][U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = k0 + lane + 64 * u;
+                xv[u] = k < K ? x[k] : 0.f;
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int k = k0 + lane + 64 * u;
+                    wv[r][u] = (k < K && row0 + r < M) ? W[(int64_t)(row0 + r) * ldw + k] : 0.f;
+                }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int u = 0; u < U; ++u) acc[r] = __builtin_fmaf(wv[r][u], xv[u], acc[r]);
+        }
+    }
+
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const float s = wave64_sum(acc[r]);
+        if (lane == 0 && row0 + r < M) y[row0 + r] = s;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemv_f32(int M, int K, const float *W, int64_t ldw, const float *x,
+                           float *y, hipStream_t s) {
+    constexpr int R = 4;
+    const int waves = (M + R - 1) / R;
+    const int nwg = (waves + WAVES - 1) / WAVES;
+    const bool vec = (reinterpret_cast<uintptr_t>(W) % 16 == 0) &&
+                     (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (ldw % 4 == 0) &&
+                     (K % 4 == 0);
+    if (vec)
+        hipLaunchKernelGGL((gemv_f32_kernel<R, 6, true>), dim3(nwg), dim3(THREADS), 0, s,
+                           M, K, W, ldw, x, y);
+    else
+        hipLaunchKernelGGL((gemv_f32_kernel<R, 8, false>), dim3(nwg), dim3(THREADS), 0, s,
+                           M, K, W, ldw, x, y);
+    return hipGetLastError();
+}
+
+}  // namespace gg

@@ -1,0 +1,30 @@
+// kernels.hpp -- launch functions exported by the kernel translation units to
+// the C entry points (api.hip).  Internal to libgemvgemm.so.
+//
+// Each launcher assumes its arguments were validated by the caller: sizes in
+// [0, 2^31), non-null aligned pointers for non-empty operands, leading
+// dimensions at least the row width, output not aliasing an input.  It only
+// picks a compile-time specialisation and a grid, and launches.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gg {
+
+enum class GemmLayout { NN, TN, NT };
+
+// C = op(A).op(B) for the three layouts of gemvgemm.h.
+hipError_t launch_gemm(GemmLayout layout, int M, int N, int K,
+                       const float *A, int64_t lda, const float *B, int64_t ldb,
+                       float *C, int64_t ldc, hipStream_t stream);
+
+// y = W.x, fp32.
+hipError_t launch_gemv_f32(int M, int K, const float *W, int64_t ldw,
+                           const float *x, float *y, hipStream_t stream);
+
+// y = W.x, W as 2-bit codes with one binary16 scale per 64 columns.
+hipError_t launch_gemv_q2(int M, int K, const uint8_t *Q, int64_t ldq,
+                          const uint16_t *S, int64_t lds, const float *x,
+                          float *y, hipStream_t stream);
+
+}  // namespace gg

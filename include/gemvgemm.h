@@ -1,0 +1,135 @@
+/*
+ * gemvgemm.h -- C interface of libgemvgemm.so: fp32 matrix products, the fp32
+ * matrix-vector product, and the 2-bit packed-weight matrix-vector product,
+ * as hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every matrix is row-major with an explicit leading dimension (the stride,
+ *    in elements, between the starts of consecutive rows).
+ *  - Every data pointer is a DEVICE pointer on the calling thread's current
+ *    HIP device.  The caller owns all memory; the library allocates nothing and
+ *    keeps no pointer after a call returns.
+ *  - Calls are asynchronous: work is queued on `stream` (NULL = the legacy
+ *    default stream) and results are valid once the caller has synchronised
+ *    that stream.  A fault inside a kernel surfaces at that synchronisation,
+ *    as with any HIP launch.
+ *  - The output is overwritten (no accumulation into it).  With K = 0 the
+ *    output is written with zeros, the empty sum.
+ *  - Each call returns a status.  Arguments are checked before any HIP call
+ *    and before anything is written: a non-zero status means nothing was
+ *    launched.  Checks, in order: sizes non-negative and below 2^31; an empty
+ *    output returns GG_OK at once; non-null pointers, aligned to their element
+ *    size, for every operand of non-zero extent; leading dimensions at least
+ *    the row width; the output's byte range disjoint from every input's; the
+ *    current device is a gfx950.  No exception or abort crosses this
+ *    interface.
+ *  - Results are reproducible bit for bit from run to run on the same shapes
+ *    (fixed reduction trees, no floating-point atomics).  They agree with the
+ *    exact sum to |c - c_exact| <= 1e-4 * sum_k |a_ik * b_kj| per element on
+ *    the supported workloads; fp32 operands are used as IEEE fp32 (no reduced
+ *    precision inputs).
+ *  - Thread safety: the only global state is a per-device property cache
+ *    filled once; every entry point may be called from several threads.
+ */
+#ifndef GEMVGEMM_H
+#define GEMVGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t, declared here so C callers need no HIP headers. */
+typedef struct ihipStream_t *gg_stream_t;
+
+enum gg_status {
+    GG_OK = 0,
+    GG_ERR_INVALID_ARG = -1, /* negative/oversized size, null or misaligned
+                                pointer, leading dimension too small        */
+    GG_ERR_ALIAS = -2,       /* output overlaps an input                     */
+    GG_ERR_NO_DEVICE = -3,   /* no current HIP device, or it is not gfx950   */
+    GG_ERR_LAUNCH = -4       /* the kernel launch itself was rejected        */
+};
+
+/*
+ * C[M x N] = A[M x K] . B[K x N]
+ *
+ * The dense matrix product: each output cell walks the inner dimension,
+ * multiplying an activation by its weight and adding the products ("More
+ * Stumbling, This Time in the Browser", section "Four answers per worker";
+ * the square sizes of "I built a GPT-2 in the browser, then made it
+ * 2.6x-12.1x faster", section "The kernel sweep").
+ *   A[i*lda + k], lda >= K;  B[k*ldb + j], ldb >= N;  C[i*ldc + j], ldc >= N.
+ * M = 1 is legal here and runs the same kernel (gemv_f32 is the one-row path).
+ */
+int gemm_f32(int64_t M, int64_t N, int64_t K,
+             const float *A, int64_t lda,
+             const float *B, int64_t ldb,
+             float *C, int64_t ldc, gg_stream_t stream);
+
+/*
+ * C[M x N] = A^T . B with A stored K x M.
+ *
+ * The weight-gradient product of a hand-derived backward pass, dW = X^T.dY
+ * ("I built a GPT-2 in the browser, then made it 2.6x-12.1x faster",
+ * section "The architecture in 60 seconds").
+ *   A[k*lda + i], lda >= M;  B[k*ldb + j], ldb >= N;  C[i*ldc + j], ldc >= N.
+ */
+int gemm_f32_tn(int64_t M, int64_t N, int64_t K,
+                const float *A, int64_t lda,
+                const float *B, int64_t ldb,
+                float *C, int64_t ldc, gg_stream_t stream);
+
+/*
+ * C[M x N] = A . B^T with B stored N x K.
+ *
+ * The input-gradient product of a hand-derived backward pass, dX = dY.W^T
+ * (same page and section as gemm_f32_tn).
+ *   A[i*lda + k], lda >= K;  B[j*ldb + k], ldb >= K;  C[i*ldc + j], ldc >= N.
+ */
+int gemm_f32_nt(int64_t M, int64_t N, int64_t K,
+                const float *A, int64_t lda,
+                const float *B, int64_t ldb,
+                float *C, int64_t ldc, gg_stream_t stream);
+
+/*
+ * y[M] = W[M x K] . x[K]
+ *
+ * The single-row matrix-vector path kept beside the dense product ("More
+ * Stumbling, This Time in the Browser", section "Four answers per worker"),
+ * at the 12,288 x 1,536 shape of "Kernel 0112", section "What is being
+ * measured".
+ *   W[i*ldw + k], ldw >= K;  x and y contiguous.
+ */
+int gemv_f32(int64_t M, int64_t K, const float *W, int64_t ldw,
+             const float *x, float *y, gg_stream_t stream);
+
+/*
+ * y[M] = W[M x K] . x[K] with W held as 2-bit codes and binary16 scales.
+ *
+ * The 2-bit weight matrix times an input vector of "Kernel 0112", sections
+ * "What is being measured" (12,288 x 1,536 weights, 1,536 inputs, 12,288
+ * outputs) and "The kernel" (2-bit fields unpacked to floating point).  The
+ * pages do not fix the packing; this library reads it as:
+ *   code(i,k) = (Q[i*ldq + k/4] >> (2*(k%4))) & 3     (least significant first)
+ *   s(i,k)    = binary16 S[i*lds + k/64]             (one scale per 64 columns)
+ *   w(i,k)    = (code(i,k) - 1.5) * s(i,k)
+ *   y[i]      = sum_k w(i,k) * x[k]
+ *   Q: ldq >= ceil(K/4) bytes per row;  S: lds >= ceil(K/64) halves per row,
+ *   holding IEEE binary16 bit patterns;  x (fp32) and y (fp32) contiguous.
+ * Bits of Q for columns k >= K and scales past ceil(K/64) are never used.
+ */
+int gemv_q2(int64_t M, int64_t K, const uint8_t *Q, int64_t ldq,
+            const uint16_t *S, int64_t lds,
+            const float *x, float *y, gg_stream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *gg_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMVGEMM_H */

@@ -1,0 +1,132 @@
+"""The C ABI on a CPU-only machine: the library loads, exports every function
+the public header declares, and rejects bad arguments before any HIP call.
+
+Argument checks run before the library touches the HIP runtime, so they can
+be exercised here with made-up (never dereferenced) device addresses.  With no
+GPU present, well-formed calls must report GG_ERR_NO_DEVICE rather than crash.
+"""
+import ctypes
+
+import pytest
+
+from gemv_gemm_f32_amd import binding as bd
+
+lib = bd.load()
+
+# made-up, 256-byte aligned addresses far apart; never dereferenced here
+PA, PB, PC, PX = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def _gpu_present():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+def test_exports_every_header_function():
+    declared = bd.header_functions()
+    assert sorted(declared) == sorted(bd.ENTRY_POINTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_strerror_covers_every_status():
+    for st in (bd.GG_OK, bd.GG_ERR_INVALID_ARG, bd.GG_ERR_ALIAS,
+               bd.GG_ERR_NO_DEVICE, bd.GG_ERR_LAUNCH):
+        msg = bd.strerror(st)
+        assert msg and msg != "unknown status"
+    assert bd.strerror(12345) == "unknown status"
+
+
+GEMMS = ("gemm_f32", "gemm_f32_tn", "gemm_f32_nt")
+
+
+@pytest.mark.parametrize("name", GEMMS)
+def test_gemm_rejects_bad_sizes(name):
+    f = getattr(lib, name)
+    assert f(-1, 4, 4, PA, 4, PB, 4, PC, 4, None) == bd.GG_ERR_INVALID_ARG
+    assert f(4, -1, 4, PA, 4, PB, 4, PC, 4, None) == bd.GG_ERR_INVALID_ARG
+    assert f(4, 4, -1, PA, 4, PB, 4, PC, 4, None) == bd.GG_ERR_INVALID_ARG
+    assert f(1 << 31, 4, 4, PA, 1 << 31, PB, 4, PC, 4, None) == bd.GG_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", GEMMS)
+def test_gemm_empty_output_is_ok_without_pointers(name):
+    f = getattr(lib, name)
+    assert f(0, 5, 7, None, 0, None, 0, None, 0, None) == bd.GG_OK
+    assert f(5, 0, 7, None, 0, None, 0, None, 0, None) == bd.GG_OK
+
+
+@pytest.mark.parametrize("name", GEMMS)
+def test_gemm_rejects_null_and_misaligned(name):
+    f = getattr(lib, name)
+    assert f(4, 4, 4, None, 4, PB, 4, PC, 4, None) == bd.GG_ERR_INVALID_ARG
+    assert f(4, 4, 4, PA, 4, None, 4, PC, 4, None) == bd.GG_ERR_INVALID_ARG
+    assert f(4, 4, 4, PA, 4, PB, 4, None, 4, None) == bd.GG_ERR_INVALID_ARG
+    assert f(4, 4, 4, PA + 2, 4, PB, 4, PC, 4, None) == bd.GG_ERR_INVALID_ARG
+    assert f(4, 4, 4, PA, 4, PB, 4, PC + 1, 4, None) == bd.GG_ERR_INVALID_ARG
+
+
+def test_gemm_leading_dimensions():
+    # NN: lda >= K, ldb >= N, ldc >= N
+    assert lib.gemm_f32(8, 6, 5, PA, 4, PB, 6, PC, 6, None) == bd.GG_ERR_INVALID_ARG
+    assert lib.gemm_f32(8, 6, 5, PA, 5, PB, 5, PC, 6, None) == bd.GG_ERR_INVALID_ARG
+    assert lib.gemm_f32(8, 6, 5, PA, 5, PB, 6, PC, 5, None) == bd.GG_ERR_INVALID_ARG
+    # TN: A stored K x M, so lda >= M
+    assert lib.gemm_f32_tn(8, 6, 5, PA, 7, PB, 6, PC, 6, None) == bd.GG_ERR_INVALID_ARG
+    # NT: B stored N x K, so ldb >= K
+    assert lib.gemm_f32_nt(8, 6, 5, PA, 5, PB, 4, PC, 6, None) == bd.GG_ERR_INVALID_ARG
+
+
+def test_gemm_alias():
+    # C placed inside A's span
+    assert lib.gemm_f32(8, 8, 8, PA, 8, PB, 8, PA + 4 * 8, 8, None) == bd.GG_ERR_ALIAS
+    # C inside B for the transposed layouts
+    assert lib.gemm_f32_tn(8, 8, 8, PA, 8, PB, 8, PB, 8, None) == bd.GG_ERR_ALIAS
+    assert lib.gemm_f32_nt(8, 8, 8, PA, 8, PB, 8, PB + 4 * 63, 8, None) == bd.GG_ERR_ALIAS
+    # adjacent but disjoint is fine (rejected later only for lack of a GPU)
+    st = lib.gemm_f32(8, 8, 8, PA, 8, PB, 8, PA + 4 * 64, 8, None)
+    assert st != bd.GG_ERR_ALIAS
+
+
+def test_gemv_validation():
+    f = lib.gemv_f32
+    assert f(-1, 4, PA, 4, PX, PC, None) == bd.GG_ERR_INVALID_ARG
+    assert f(0, 4, None, 0, None, None, None) == bd.GG_OK
+    assert f(4, 4, PA, 3, PX, PC, None) == bd.GG_ERR_INVALID_ARG
+    assert f(4, 4, None, 4, PX, PC, None) == bd.GG_ERR_INVALID_ARG
+    assert f(4, 4, PA, 4, PX, None, None) == bd.GG_ERR_INVALID_ARG
+    assert f(4, 4, PA, 4, PX, PA + 8, None) == bd.GG_ERR_ALIAS
+    assert f(4, 4, PA, 4, PX, PX, None) == bd.GG_ERR_ALIAS
+
+
+def test_gemv_q2_validation():
+    f = lib.gemv_q2
+    # K = 100: rows need ceil(100/4) = 25 bytes and ceil(100/64) = 2 scales
+    assert f(4, 100, PA, 24, PB, 2, PX, PC, None) == bd.GG_ERR_INVALID_ARG
+    assert f(4, 100, PA, 25, PB, 1, PX, PC, None) == bd.GG_ERR_INVALID_ARG
+    assert f(4, 100, PA, 25, PB + 1, 2, PX, PC, None) == bd.GG_ERR_INVALID_ARG
+    assert f(4, 100, PA, 25, PB, 2, PX + 2, PC, None) == bd.GG_ERR_INVALID_ARG
+    assert f(4, 100, None, 25, PB, 2, PX, PC, None) == bd.GG_ERR_INVALID_ARG
+    assert f(0, 100, None, 0, None, 0, None, None, None) == bd.GG_OK
+    assert f(4, 100, PA, 25, PB, 2, PX, PA + 16, None) == bd.GG_ERR_ALIAS
+    assert f(4, 100, PA, 25, PB, 2, PX, PB + 4, None) == bd.GG_ERR_ALIAS
+
+
+@pytest.mark.skipif(_gpu_present(), reason="checks the no-device path")
+def test_no_device_is_reported():
+    assert lib.gemm_f32(4, 4, 4, PA, 4, PB, 4, PC, 4, None) == bd.GG_ERR_NO_DEVICE
+    assert lib.gemv_f32(4, 4, PA, 4, PX, PC, None) == bd.GG_ERR_NO_DEVICE
+    assert lib.gemv_q2(4, 64, PA, 16, PB, 1, PX, PC, None) == bd.GG_ERR_NO_DEVICE
+
+
+def test_single_hip_runtime_in_process():
+    # The library must share torch's HIP runtime rather than load a second one
+    # (torch's stream handles and allocations are only valid in its own).
+    import re
+    maps = open("/proc/self/maps").read()
+    hip = set(re.findall(r"\S*libamdhip64\S*", maps))
+    assert len(hip) == 1, hip

@@ -1,0 +1,103 @@
+"""GPU parity of gemv_f32 against the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+from gemv_gemm_f32_amd import binding as bd
+from gemv_gemm_f32_amd import inputs
+from golden_io import load
+from gpu_util import assert_close, canaries_intact, dev, guarded, host, torch
+
+pytestmark = pytest.mark.gpu
+
+RNG = np.random.default_rng(88)
+
+
+def _run(W, x):
+    return host(bd.gemv_f32(dev(W), dev(x)))
+
+
+def test_tiny_hand_case():
+    g = load("gemv_tiny_3x4.txt")
+    W = np.asarray(g["W"], np.float64).astype(np.float32)
+    x = np.asarray(g["x"], np.float64).astype(np.float32)[0]
+    assert np.array_equal(_run(W, x), np.asarray(g["y"], np.float64).astype(np.float32)[0])
+
+
+@pytest.mark.parametrize("M,K", [(1, 1), (5, 3), (16, 4), (17, 257), (300, 1536),
+                                 (12288, 1536), (33, 4100), (1000, 61)])
+def test_integer_inputs_bitwise(M, K):
+    W = inputs.integers(RNG, (M, K))
+    x = inputs.integers(RNG, (K,))
+    ref, _ = oracle.gemv(W, x)
+    assert np.array_equal(_run(W, x).astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("r", [0, 1, 47])
+def test_rotation_matrices_full_size(r):
+    W = inputs.gemv_f32_weight(r)
+    x = inputs.gemv_f32_x()
+    y = _run(W, x)
+    ref, bound = oracle.gemv(W, x)
+    assert_close(y, ref, bound, "rotation matrix %d" % r)
+
+
+@pytest.mark.parametrize("M,K", [(1, 7), (13, 1), (129, 1535), (250, 1538), (7, 5000)])
+def test_ragged_shapes(M, K):
+    W = inputs.normal(RNG, (M, K))
+    x = inputs.normal(RNG, (K,))
+    ref, bound = oracle.gemv(W, x)
+    assert_close(_run(W, x), ref, bound, "%dx%d" % (M, K))
+
+
+def test_matches_gemm_with_one_column():
+    W = inputs.normal(RNG, (900, 1536), 0.02)
+    x = inputs.normal(RNG, (1536,))
+    y = _run(W, x)
+    c = host(bd.gemm_f32(dev(W), dev(x.reshape(-1, 1))))[:, 0]
+    ref, bound = oracle.gemv(W, x)
+    assert_close(y, ref, bound, "gemv")
+    assert_close(c, ref, bound, "gemm N=1")
+
+
+def test_padded_rows_and_canaries():
+    t = torch()
+    M, K = 250, 1536
+    W = inputs.normal(RNG, (M, K))
+    Ww = np.zeros((M, K + 12), np.float32)
+    Ww[:, :K] = W
+    x = inputs.normal(RNG, (K,))
+    buf, yv = guarded(1, M)
+    bd.gemv_f32(dev(Ww)[:, :K], dev(x), y=yv[0])
+    ref, bound = oracle.gemv(W, x)
+    assert_close(host(yv)[0], ref, bound, "padded ldw")
+    assert canaries_intact(buf)
+
+
+def test_misaligned_operands_take_scalar_path():
+    M, K = 100, 1536
+    W = inputs.normal(RNG, (M, K))
+    Ww = np.zeros((M, K + 1), np.float32)
+    Ww[:, 1:] = W
+    x = inputs.normal(RNG, (K,))
+    y = host(bd.gemv_f32(dev(Ww)[:, 1:], dev(x)))
+    ref, bound = oracle.gemv(W, x)
+    assert_close(y, ref, bound, "misaligned")
+
+
+def test_deterministic():
+    W = inputs.gemv_f32_weight(3)
+    x = inputs.gemv_f32_x()
+    dW, dx = dev(W), dev(x)
+    a = host(bd.gemv_f32(dW, dx))
+    b = host(bd.gemv_f32(dW, dx))
+    assert np.array_equal(a, b)
+
+
+def test_k_zero_writes_zeros():
+    t = torch()
+    W = t.empty((40, 0), dtype=t.float32, device="cuda")
+    x = t.empty((0,), dtype=t.float32, device="cuda")
+    y = t.full((40,), 3.0, dtype=t.float32, device="cuda")
+    bd.gemv_f32(W, x, y=y)
+    assert np.all(host(y) == 0)

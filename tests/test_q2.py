@@ -1,0 +1,135 @@
+"""GPU parity of gemv_q2 (2-bit codes + binary16 group scales) against the CPU
+oracle's explicit unpack-then-dot, through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+from gemv_gemm_f32_amd import binding as bd
+from gemv_gemm_f32_amd import inputs
+from golden_io import load
+from gpu_util import assert_close, canaries_intact, dev, guarded, host, torch
+
+pytestmark = pytest.mark.gpu
+
+RNG = np.random.default_rng(99)
+
+
+def _run(Q, S, x):
+    t = torch()
+    return host(bd.gemv_q2(dev(Q), dev(S.view(np.int16)), dev(x)))
+
+
+def _pack(codes):
+    M, K = codes.shape
+    nb = (K + 3) // 4
+    p = np.zeros((M, nb * 4), np.uint16)
+    p[:, :K] = codes
+    q = p.reshape(M, nb, 4)
+    return (q[..., 0] | (q[..., 1] << 2) | (q[..., 2] << 4) | (q[..., 3] << 6)).astype(np.uint8)
+
+
+def _scales(M, K):
+    return RNG.uniform(0.01, 0.05, (M, (K + 63) // 64)).astype(np.float16).view(np.uint16)
+
+
+def test_tiny_hand_case():
+    g = load("q2_tiny_2x4.txt")
+    Q = np.array(g["Q"], np.uint8)
+    S = np.array(g["S"], np.uint16)
+    x = np.asarray(g["x"], np.float64).astype(np.float32)[0]
+    y = _run(Q, S, x)
+    assert np.array_equal(y, np.asarray(g["y"], np.float64).astype(np.float32)[0])
+
+
+@pytest.mark.parametrize("M,K", [(1, 16), (7, 64), (48, 1536), (12288, 1536), (13, 100),
+                                 (100, 3072), (5, 1)])
+def test_integer_exact(M, K):
+    # scale 2.0 and integer x: every partial sum is an integer below 2^24
+    codes = RNG.integers(0, 4, (M, K))
+    Q = _pack(codes)
+    S = np.full((M, (K + 63) // 64), 0x4000, np.uint16)
+    x = inputs.integers(RNG, (K,))
+    ref, _ = oracle.gemv_q2(Q, S, x)
+    assert np.array_equal(_run(Q, S, x).astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("r", [0, 1, 63, 127])
+def test_rotation_matrices_full_size(r):
+    Q, S = inputs.q2_weight(r)
+    x = inputs.q2_x()
+    ref, bound = oracle.gemv_q2(Q, S, x)
+    assert_close(_run(Q, S, x), ref, bound, "rotation matrix %d" % r)
+
+
+@pytest.mark.parametrize("M,K", [(1, 1), (3, 5), (37, 70), (100, 1535), (61, 1537),
+                                 (50, 4096), (11, 16 * 97)])
+def test_ragged_shapes(M, K):
+    codes = RNG.integers(0, 4, (M, K))
+    Q = _pack(codes)
+    S = _scales(M, K)
+    x = inputs.normal(RNG, (K,))
+    ref, bound = oracle.gemv_q2(Q, S, x)
+    assert_close(_run(Q, S, x), ref, bound, "%dx%d" % (M, K))
+
+
+def test_matches_gemv_f32_on_dequantised_weights():
+    Q, S = inputs.q2_weight(5, 600, 1536)
+    x = inputs.q2_x()
+    Wd = oracle.q2_unpack(Q, S, 1536)
+    W32 = Wd.astype(np.float32)
+    assert np.array_equal(W32.astype(np.float64), Wd)   # exact in fp32
+    yq = _run(Q, S, x)
+    yf = host(bd.gemv_f32(dev(W32), dev(x)))
+    ref, bound = oracle.gemv(W32, x)
+    assert_close(yq, ref, bound, "q2")
+    assert_close(yf, ref, bound, "f32")
+
+
+def test_padding_bits_and_bytes_ignored():
+    # K = 70: last byte has 2 dead columns, the second scale group is partial,
+    # rows carry garbage bytes/halves beyond their live width
+    M, K = 45, 70
+    codes = RNG.integers(0, 4, (M, K))
+    Q = _pack(codes)
+    S = _scales(M, K)
+    x = inputs.normal(RNG, (K,))
+    y = _run(Q, S, x)
+    Qg = RNG.integers(0, 256, (M, Q.shape[1] + 7)).astype(np.uint8)
+    Qg[:, :Q.shape[1]] = Q
+    Qg[:, Q.shape[1] - 1] |= np.uint8(0b11110000)
+    Sg = RNG.integers(0, 65536, (M, 5)).astype(np.uint16)
+    Sg[:, :2] = S
+    y2 = host(bd.gemv_q2(dev(Qg), dev(Sg.view(np.int16)), dev(x)))
+    assert np.array_equal(y, y2)
+
+
+def test_padded_leading_dims_fast_path():
+    # ldq, lds larger than needed and multiples of 4: the word-load path
+    M, K = 300, 1536
+    Q, S = inputs.q2_weight(9, M, K)
+    Qw = np.zeros((M, 400), np.uint8)
+    Qw[:, :384] = Q
+    Sw = np.zeros((M, 32), np.uint16)
+    Sw[:, :24] = S
+    x = inputs.q2_x()
+    buf, yv = guarded(1, M)
+    bd.gemv_q2(dev(Qw)[:, :384], dev(Sw.view(np.int16))[:, :24], dev(x), y=yv[0])
+    ref, bound = oracle.gemv_q2(Q, S, x)
+    assert_close(host(yv)[0], ref, bound, "padded")
+    assert canaries_intact(buf)
+
+
+def test_scale_doubling_doubles_output_bitwise():
+    Q, S = inputs.q2_weight(11, 500, 1536)
+    x = inputs.q2_x()
+    S2 = (S.view(np.float16) * np.float16(2)).view(np.uint16)
+    assert np.array_equal(_run(Q, S2, x), np.float32(2) * _run(Q, S, x))
+
+
+def test_deterministic():
+    Q, S = inputs.q2_weight(2)
+    x = inputs.q2_x()
+    dQ, dS, dx = dev(Q), dev(S.view(np.int16)), dev(x)
+    a = host(bd.gemv_q2(dQ, dS, dx))
+    b = host(bd.gemv_q2(dQ, dS, dx))
+    assert np.array_equal(a, b)
