@@ -43,6 +43,10 @@ __global__ __launch_bounds__(THREADS) void gemv_f32_kernel(
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.f;
 
+    // Loads are unconditional, from clamped (in-bounds) indices, so a pass
+    // issues all of them back to back; rows past M are computed on the last
+    // row and not stored, chunks past K are zeroed after a scheduling barrier.
+    const int rl = M - 1;
     if (VEC) {
         const int nv = K >> 2;                       // 16-byte chunks per row
         const v4f *x4 = reinterpret_cast<const v4f *>(x);
@@ -50,17 +54,22 @@ __global__ __launch_bounds__(THREADS) void gemv_f32_kernel(
             v4f xv[U];
             v4f wv[R][U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = c0 + lane + 64 * u;
-                xv[u] = c < nv ? x4[c] : v4f{0.f, 0.f, 0.f, 0.f};
-            }
+            for (int u = 0; u < U; ++u) xv[u] = x4[min(c0 + lane + 64 * u, nv - 1)];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const v4f *wr = reinterpret_cast<const v4f *>(W + (int64_t)(row0 + r) * ldw);
+                const v4f *wr = reinterpret_cast<const v4f *>(W + (int64_t)min(row0 + r, rl) * ldw);
+#pragma unroll
+                for (int u = 0; u < U; ++u) wv[r][u] = wr[min(c0 + lane + 64 * u, nv - 1)];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (c0 + 64 * U > nv) {                  // uniform: a partial pass
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int c = c0 + lane + 64 * u;
-                    wv[r][u] = (c < nv && row0 + r < M) ? wr[c] : v4f{0.f, 0.f, 0.f, 0.f};
+                    const bool live = c0 + lane + 64 * u < nv;
+                    xv[u] = live ? xv[u] : v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        wv[r][u] = live ? wv[r][u] : v4f{0.f, 0.f, 0.f, 0.f};
                 }
             }
 #pragma unroll
@@ -78,17 +87,22 @@ __global__ __launch_bounds__(THREADS) void gemv_f32_kernel(
             float xv[U];
             float wv[R][U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int k = k0 + lane + 64 * u;
-                xv[u] = k < K ? x[k] : 0.f;
-            }
+            for (int u = 0; u < U; ++u) xv[u] = x[min(k0 + lane + 64 * u, K - 1)];
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
+                for (int u = 0; u < U; ++u)
+                    wv[r][u] = W[(int64_t)min(row0 + r, rl) * ldw + min(k0 + lane + 64 * u, K - 1)];
+            __builtin_amdgcn_sched_barrier(0);
+            if (k0 + 64 * U > K) {
+#pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int k = k0 + lane + 64 * u;
-                    wv[r][u] = (k < K && row0 + r < M) ? W[(int64_t)(row0 + r) * ldw + k] : 0.f;
+                    const bool live = k0 + lane + 64 * u < K;
+                    xv[u] = live ? xv[u] : 0.f;
+#pragma unroll
+                    for (int r = 0; r < R; ++r) wv[r][u] = live ? wv[r][u] : 0.f;
                 }
+            }
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll

@@ -80,57 +80,96 @@ __global__ __launch_bounds__(THREADS) void gemv_q2_kernel(
     if (wave * (2 * RPL) >= M) return;    // uniform per wave
 
     const int words = (K + 15) >> 4;      // code words per row
+    const int row_last = M - 1;
     float acc[RPL];
 #pragma unroll
     for (int m = 0; m < RPL; ++m) acc[m] = 0.f;
 
+    // Mask of the two code slots, and the binary16 pair (1.0, 1.0).  The
+    // empty asm pins both in VGPRs, so (sh & mask) | one is selected as one
+    // v_and_or_b32: gfx9 VOP3 forms take no literal operand, and with the
+    // constants left visible the compiler splits it into an AND and an OR.
+    unsigned mask = 0x03000300u, one = 0x3C003C00u;
+    asm volatile("" : "+v"(mask));
+    asm volatile("" : "+v"(one));
+
     for (int w0 = 0; w0 < words; w0 += WORDS_PER_PASS) {
-        // x first: later waits on the (slower) code loads then cover it too.
-        float xv[WPL][16];
+        // ---- Loads.  Every load of a pass is issued first, unconditionally,
+        // from clamped (always in-bounds) addresses: x, then codes and scales
+        // row by row, so that the rows can be consumed in the order their
+        // data arrives.  Predicated loads, or selects right after each load,
+        // make the compiler wait for each load before issuing the next.  The
+        // fast path addresses with 32-bit byte offsets from the base pointer.
+        v4f xraw[WPL][4];
+        unsigned craw[RPL][WPL];
+        unsigned sraw[RPL][WPL];          // binary16 bits, zero-extended
 #pragma unroll
         for (int q = 0; q < WPL; ++q) {
             const int wd = w0 + j + 32 * q;
+            const int wdc = wd < words ? wd : words - 1;
             if (FAST) {
-                const v4f *x4 = reinterpret_cast<const v4f *>(x) + wd * 4;
+                const char *xb = reinterpret_cast<const char *>(x) + (unsigned)wdc * 64u;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const v4f v = wd < words ? x4[c] : v4f{0.f, 0.f, 0.f, 0.f};
-                    xv[q][4 * c + 0] = v.x;
-                    xv[q][4 * c + 1] = v.y;
-                    xv[q][4 * c + 2] = v.z;
-                    xv[q][4 * c + 3] = v.w;
-                }
+                for (int c = 0; c < 4; ++c)
+                    xraw[q][c] = *reinterpret_cast<const v4f *>(xb + 16 * c);
             } else {
 #pragma unroll
-                for (int p = 0; p < 16; ++p) {
-                    const int k = wd * 16 + p;
-                    xv[q][p] = (wd < words && k < K) ? x[k] : 0.f;
-                }
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int k = wdc * 16 + 4 * c + e;
+                        xraw[q][c][e] = x[k < K ? k : K - 1];
+                    }
             }
         }
-
-        unsigned code[RPL][WPL];
-        uint16_t sbits[RPL][WPL];
 #pragma unroll
         for (int m = 0; m < RPL; ++m) {
             const int row = row0 + m;
-            const uint8_t *Qrow = Q + (int64_t)row * ldq;
+            const int rowc = row < M ? row : row_last;
 #pragma unroll
             for (int q = 0; q < WPL; ++q) {
                 const int wd = w0 + j + 32 * q;
-                const bool ok = row < M && wd < words;
-                code[m][q] = ok ? load_word<FAST>(Qrow, wd, K) : 0u;
-                sbits[m][q] = ok ? S[(int64_t)row * lds + (wd >> 2)] : (uint16_t)0;
+                const int wdc = wd < words ? wd : words - 1;
+                if (FAST) {
+                    const unsigned qo = (unsigned)rowc * (unsigned)ldq + (unsigned)wdc * 4u;
+                    const unsigned so = ((unsigned)rowc * (unsigned)lds + (unsigned)(wdc >> 2)) * 2u;
+                    craw[m][q] = *reinterpret_cast<const unsigned *>(
+                        reinterpret_cast<const char *>(Q) + qo);
+                    sraw[m][q] = *reinterpret_cast<const uint16_t *>(
+                        reinterpret_cast<const char *>(S) + so);
+                } else {
+                    craw[m][q] = load_word<false>(Q + (int64_t)rowc * ldq, wdc, K);
+                    sraw[m][q] = S[(int64_t)rowc * lds + (wdc >> 2)];
+                }
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
 
-        // Mask of the two code slots, and the binary16 pair (1.0, 1.0).  The
-        // empty asm pins both in VGPRs, so (sh & mask) | one is selected as one
-        // v_and_or_b32: gfx9 VOP3 forms take no literal operand, and with the
-        // constants left visible the compiler splits it into an AND and an OR.
-        unsigned mask = 0x03000300u, one = 0x3C003C00u;
-        asm volatile("" : "+v"(mask));
-        asm volatile("" : "+v"(one));
+        // ---- Dead words (past the row's end, only in a last partial pass)
+        // contribute nothing: their x and scale are zeroed.  Rows past M are
+        // computed on a clamped row and never stored.
+        float xv[WPL][16];
+        unsigned sbits[RPL][WPL];
+        if (w0 + WORDS_PER_PASS <= words && FAST) {      // uniform
+#pragma unroll
+            for (int q = 0; q < WPL; ++q) {
+#pragma unroll
+                for (int p = 0; p < 16; ++p) xv[q][p] = xraw[q][p >> 2][p & 3];
+#pragma unroll
+                for (int m = 0; m < RPL; ++m) sbits[m][q] = sraw[m][q];
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < WPL; ++q) {
+                const int wd = w0 + j + 32 * q;
+                const bool live = wd < words;
+#pragma unroll
+                for (int p = 0; p < 16; ++p)
+                    xv[q][p] = (live && (FAST || wd * 16 + p < K)) ? xraw[q][p >> 2][p & 3] : 0.f;
+#pragma unroll
+                for (int m = 0; m < RPL; ++m) sbits[m][q] = live ? sraw[m][q] : 0u;
+            }
+        }
 
         float init[WPL];
 #pragma unroll
@@ -141,24 +180,32 @@ __global__ __launch_bounds__(THREADS) void gemv_q2_kernel(
             init[q] = -1.375f * X;
         }
 
+        // ---- Row by row; the WPL words of a row are three independent
+        // multiply-add chains, interleaved step by step.
 #pragma unroll
-        for (int m = 0; m < RPL; ++m)
+        for (int m = 0; m < RPL; ++m) {
+            float a[WPL];
 #pragma unroll
-            for (int q = 0; q < WPL; ++q) {
-                const unsigned d = code[m][q];
-                float a = init[q];
+            for (int q = 0; q < WPL; ++q) a[q] = init[q];
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
+            for (int t = 0; t < 8; ++t) {
+#pragma unroll
+                for (int q = 0; q < WPL; ++q) {
+                    const unsigned d = craw[m][q];
                     // codes t and t+8 of the word moved to bits 8-9 and 24-25
                     const unsigned sh = t < 4 ? (d << (8 - 2 * t)) : (d >> (2 * t - 8));
                     const unsigned hb = (sh & mask) | one;
                     const h2 hv = __builtin_bit_cast(h2, hb);
-                    a = __builtin_fmaf((float)hv.x, xv[q][t], a);
-                    a = __builtin_fmaf((float)hv.y, xv[q][t + 8], a);
+                    a[q] = __builtin_fmaf((float)hv.x, xv[q][t], a[q]);
+                    a[q] = __builtin_fmaf((float)hv.y, xv[q][t + 8], a[q]);
                 }
-                const float s = (float)__builtin_bit_cast(_Float16, sbits[m][q]);
-                acc[m] = __builtin_fmaf(s, a, acc[m]);
             }
+#pragma unroll
+            for (int q = 0; q < WPL; ++q) {
+                const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits[m][q]);
+                acc[m] = __builtin_fmaf(s, a[q], acc[m]);
+            }
+        }
     }
 
 #pragma unroll
@@ -175,9 +222,12 @@ hipError_t launch_gemv_q2(int M, int K, const uint8_t *Q, int64_t ldq, const uin
     constexpr int RPL = 6;
     const int rows_per_wg = WAVES * 2 * RPL;
     const int nwg = (M + rows_per_wg - 1) / rows_per_wg;
+    // word loads, 16-byte x loads, and 32-bit byte offsets into Q and S
     const bool fast = (K % 16 == 0) && (ldq % 4 == 0) &&
                       (reinterpret_cast<uintptr_t>(Q) % 4 == 0) &&
-                      (reinterpret_cast<uintptr_t>(x) % 16 == 0);
+                      (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                      (int64_t)M * ldq < (int64_t(1) << 32) &&
+                      (int64_t)M * lds * 2 < (int64_t(1) << 32);
     if (fast)
         hipLaunchKernelGGL((gemv_q2_kernel<RPL, true>), dim3(nwg), dim3(THREADS), 0, s,
                            M, K, Q, ldq, S, lds, x, y);
