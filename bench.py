@@ -13,11 +13,12 @@ A step is one pass of the whole path over one batch of synthetic input:
     call n using weight matrix n mod 128 of a 128-matrix set (648 MiB of codes
     and scales, far above the 256 MB Infinity Cache, as the page's "cold"
     rotation keeps reuse between runs unlikely).
-Every input is generated, hashed and copied to HBM before timing.  Each kind
-of launch is captured once into a HIP graph (through torch.cuda.CUDAGraph)
-so that the timed region replays kernels back to back, without host launch
-gaps; HIP events on the replay stream bracket the GEMM and the token inside
-every step, which gives each kernel's average launch duration.
+Every input is generated, hashed and copied to HBM before timing.  Launches
+are captured into HIP graphs (through torch.cuda.CUDAGraph) so that timed
+regions replay kernels back to back, without host launch gaps.  HIP events on
+the replay stream time K whole steps (ms_per_step), and, for each kernel's
+average launch duration, runs of back-to-back launches of that kernel alone
+(K GEMMs; K tokens of 40 q2 calls).
 
 Output: one JSON line.  `value` is the GEMM's TFLOP/s (2 * 2048^3 flops per
 launch over its average launch duration); the 2-bit GEMV's weight GB/s
@@ -58,6 +59,7 @@ PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
 PAGE_GEMM_2048_TFLOPS = GEMM_FLOPS / 9.12e-3 / 1e12
 
 PROFILES = os.path.join(ROOT, "profiles")
+CALIBRATION_BYTES = 256 << 20      # the copy used to scale byte counters
 
 
 def log(*a):
@@ -122,13 +124,111 @@ def cpu_baseline(A, B, Q, S, x, budget_s=12.0):
     }
 
 
+def _short_name(kernel):
+    k = kernel.replace("void gg::(anonymous namespace)::", "")
+    return k.split("(")[0]
+
+
+def summarize_trace(db_path):
+    """Per-kernel count / total / average / min / max duration (us) from a
+    rocprofv3 results database."""
+    import sqlite3
+    db = sqlite3.connect(db_path)
+    rows = db.execute("select name, duration from kernels").fetchall()
+    by = {}
+    for name, dur in rows:
+        by.setdefault(_short_name(name), []).append(dur / 1e3)
+    lines = ["| kernel | calls | total us | avg us | min us | max us |",
+             "|---|---|---|---|---|---|"]
+    for k, d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        d = np.array(d)
+        lines.append("| %s | %d | %.1f | %.3f | %.3f | %.3f |" %
+                     (k, len(d), d.sum(), d.mean(), d.min(), d.max()))
+    return "\n".join(lines)
+
+
+def _counter_per_kernel(db_path, counter):
+    """Per kernel name: the counter summed over its instances within each
+    dispatch, then the median over dispatches; for copy kernels, the largest
+    dispatch (the calibration copy dwarfs the input uploads)."""
+    import sqlite3
+    db = sqlite3.connect(db_path)
+    rows = db.execute("select kernel_name, dispatch_id, value from counters_collection "
+                      "where counter_name = ?", (counter,)).fetchall()
+    per = {}
+    for name, disp, v in rows:
+        per.setdefault(_short_name(name), {}).setdefault(disp, 0.0)
+        per[_short_name(name)][disp] += v
+    out = {}
+    for k, v in per.items():
+        vals = list(v.values())
+        out[k] = float(max(vals) if "copyBuffer" in k else np.median(vals))
+    return out
+
+
+def write_traffic(fetch_db, write_db):
+    """HBM bytes per launch of the GEMM and the 2-bit GEMV: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch, median over dispatches), each scaled by
+    what the same counter reads for the calibration copy of known size."""
+    fetch = _counter_per_kernel(fetch_db, "FETCH_SIZE")
+    write = _counter_per_kernel(write_db, "WRITE_SIZE")
+    copy = [k for k in fetch if "copyBuffer" in k]
+    if not copy:
+        sys.exit("no copy kernel in the trace: run with --copy-calibration")
+    ck = copy[0]
+    nbytes = CALIBRATION_BYTES
+    f_scale = nbytes / (fetch[ck] * 1024.0)
+    w_scale = nbytes / (write[ck] * 1024.0)
+    out = []
+    for key, fname, srcs, alg in (
+            ("gemm_f32_kernel", "traffic_gemm_f32_2048.json", ("gemm_f32.hip",),
+             3 * 4 * GEMM_N * GEMM_N),
+            ("gemv_q2_kernel", "traffic_gemv_q2_12288x1536.json", ("gemv_q2.hip", "wave.hpp"),
+             Q2_ALG_BYTES)):
+        k = [n for n in fetch if n.startswith(key)]
+        if not k:
+            continue
+        k = k[0]
+        fb = fetch[k] * 1024.0 * f_scale
+        wb = write[k] * 1024.0 * w_scale
+        d = {"kernel": k, "kernel_src_sha": src_sha(*srcs),
+             "fetch_kib_raw": fetch[k], "write_kib_raw": write[k],
+             "copy_bytes": nbytes, "copy_fetch_kib_raw": fetch[ck],
+             "copy_write_kib_raw": write[ck], "fetch_scale": f_scale,
+             "write_scale": w_scale, "hbm_bytes_per_launch": fb + wb,
+             "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+             "algorithmic_bytes_per_launch": alg,
+             "traffic_over_algorithmic": (fb + wb) / alg}
+        with open(os.path.join(PROFILES, fname), "w") as f:
+            json.dump(d, f, indent=1)
+            f.write("\n")
+        out.append(d)
+        print(json.dumps(d))
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="also run one device-to-device copy of BYTES before "
+                         "timing, the reference for rocprofv3 byte counters")
+    ap.add_argument("--summarize-trace", metavar="RESULTS_DB",
+                    help="print the per-kernel summary of a rocprofv3 "
+                         "--kernel-trace --stats database and exit")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="turn two rocprofv3 --pmc databases (FETCH_SIZE, "
+                         "WRITE_SIZE) of a run made with --copy-calibration "
+                         "into per-launch HBM bytes under profiles/, and exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return 0
+    if args.traffic:
+        return write_traffic(*args.traffic)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the products here are not "
               "sharded and no collective is built (asked for --gpus %d)"
@@ -186,59 +286,97 @@ def main():
     log("parity: gemm worst %.3g, q2 worst %.3g (x 1e-4 bound)" %
         (gemm_worst / 1e-4, q2_worst / 1e-4))
 
-    # ---- graphs: one GEMM; 16 tokens of 40 q2 calls cover the 128-set
-    #      rotation (lcm(40, 128) = 640 calls) so call n uses matrix n mod 128
+    if args.copy_calibration > 0:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: %d bytes" % (4 * n))
+        del src, dst
+
+    # ---- graphs.  A token is 40 q2 calls; 16 tokens cover the 128-matrix
+    #      rotation (lcm(40, 128) = 640 calls), so call n uses matrix n mod 128.
+    #      step_graphs[t]: one whole step (the GEMM, then token t).
+    #      gemm_graph: GEMMS_PER_REPLAY back-to-back GEMMs; tok_graphs[t]:
+    #      token t alone.  Those two time each kernel over runs of
+    #      back-to-back launches, so a kernel's average launch duration
+    #      carries no per-replay overhead.
     stream = torch.cuda.Stream(device=dev)
-    n_tok_graphs = 16
+    n_tok = 16
+    gemms_per_replay = 8
     with torch.cuda.stream(stream):
         for _ in range(3):
             bd.gemm_f32(dA, dB, C=dC)
             bd.gemv_q2(Qd[0], Sd[0], dx, y=dy)
     stream.synchronize()
-    g_gemm = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_gemm, stream=stream):
-        bd.gemm_f32(dA, dB, C=dC)
-    g_tok = []
-    for t in range(n_tok_graphs):
+
+    def token(t):
+        for c in range(CALLS_PER_TOKEN):
+            n = t * CALLS_PER_TOKEN + c
+            bd.gemv_q2(Qd[n % Q2_ROTATION], Sd[n % Q2_ROTATION], dx, y=dy)
+
+    def capture(fn):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            for c in range(CALLS_PER_TOKEN):
-                n = t * CALLS_PER_TOKEN + c
-                bd.gemv_q2(Qd[n % Q2_ROTATION], Sd[n % Q2_ROTATION], dx, y=dy)
-        g_tok.append(g)
+            fn()
+        return g
+
+    step_graphs = [capture(lambda t=t: (bd.gemm_f32(dA, dB, C=dC), token(t)))
+                   for t in range(n_tok)]
+    tok_graphs = [capture(lambda t=t: token(t)) for t in range(n_tok)]
+    gemm_graph = capture(lambda: [bd.gemm_f32(dA, dB, C=dC)
+                                  for _ in range(gemms_per_replay)])
     torch.cuda.synchronize()
 
-    def step(s, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        g_gemm.replay()
-        if ev is not None:
-            ev[1].record(stream)
-        g_tok[s % n_tok_graphs].replay()
-        if ev is not None:
-            ev[2].record(stream)
+    def timed(replays, warm):
+        """HIP events on the replay stream around back-to-back replays."""
+        with torch.cuda.stream(stream):
+            for i in range(warm):
+                replays(i)
+            stream.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            t = time.perf_counter()
+            n = replays(None)
+            e1.record(stream)
+            stream.synchronize()
+            t = time.perf_counter() - t
+        return e0.elapsed_time(e1), n, t
 
-    with torch.cuda.stream(stream):
-        for s in range(args.warmup):
-            step(s)
-        stream.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-               for _ in range(args.steps)]
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t_wall = time.perf_counter()
-        start.record(stream)
+    def run_steps(i):
+        if i is not None:
+            step_graphs[i % n_tok].replay()
+            return 1
         for s in range(args.steps):
-            step(args.warmup + s, evs[s])
-        end.record(stream)
-        torch.cuda.synchronize()
-        t_wall = time.perf_counter() - t_wall
-    total_ms = start.elapsed_time(end)
-    gemm_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    tok_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    gemm_us = 1e3 * float(np.mean(gemm_ms))
-    q2_us = 1e3 * float(np.mean(tok_ms)) / CALLS_PER_TOKEN
+            step_graphs[(args.warmup + s) % n_tok].replay()
+        return args.steps
+
+    n_gemm_replays = max(1, (args.steps + gemms_per_replay - 1) // gemms_per_replay)
+
+    def run_gemms(i):
+        if i is not None:
+            gemm_graph.replay()
+            return 1
+        for _ in range(n_gemm_replays):
+            gemm_graph.replay()
+        return n_gemm_replays * gemms_per_replay
+
+    def run_tokens(i):
+        if i is not None:
+            tok_graphs[i % n_tok].replay()
+            return 1
+        for s in range(args.steps):
+            tok_graphs[s % n_tok].replay()
+        return args.steps * CALLS_PER_TOKEN
+
+    total_ms, _, t_wall = timed(run_steps, args.warmup)
+    gemm_ms, n_gemm, _ = timed(run_gemms, max(1, args.warmup // gemms_per_replay))
+    tok_ms, n_q2, _ = timed(run_tokens, args.warmup)
+    gemm_us = 1e3 * gemm_ms / n_gemm
+    q2_us = 1e3 * tok_ms / n_q2
 
     gemm_tflops = GEMM_FLOPS / gemm_us / 1e6
     q2_gbs = Q2_WEIGHT_BYTES / q2_us / 1e3
@@ -277,7 +415,9 @@ def main():
             "q2_gemv": "12288x1536, 2-bit codes + fp16 scale per 64 columns",
             "rotation": Q2_ROTATION,
             "calls_per_token": CALLS_PER_TOKEN,
-            "timing": "HIP graph replay; HIP events on the replay stream per step",
+            "timing": ("HIP graph replay; HIP events on the replay stream around "
+                       "K whole steps, and around runs of back-to-back GEMM and "
+                       "q2 launches for each kernel's average launch duration"),
         },
         "roofline": {
             "kernel": "gemm_f32 (NN, 2048^3)",

@@ -18,22 +18,29 @@ namespace {
 constexpr int64_t kMaxDim = INT32_MAX;   // sizes must be below 2^31
 constexpr int kMaxDevices = 64;
 
-// Per-device cache of "is gfx950": 0 unknown, 1 yes, 2 no.  Filled without a
-// lock; a race only repeats the query and stores the same answer.
-std::atomic<int> g_device_ok[kMaxDevices];
+// Per-device cache: 0 unknown, else 1 + compute-unit count for a gfx950 and
+// -1 for any other device.  Filled without a lock; a race only repeats the
+// query and stores the same answer.
+std::atomic<int> g_device_info[kMaxDevices];
 
-int check_device() {
+// GG_OK and the current device's CU count, or an error status.
+int check_device(int *num_cus) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GG_ERR_NO_DEVICE;
     if (dev < kMaxDevices) {
-        const int known = g_device_ok[dev].load(std::memory_order_relaxed);
-        if (known == 1) return GG_OK;
-        if (known == 2) return GG_ERR_NO_DEVICE;
+        const int known = g_device_info[dev].load(std::memory_order_relaxed);
+        if (known > 0) {
+            *num_cus = known - 1;
+            return GG_OK;
+        }
+        if (known < 0) return GG_ERR_NO_DEVICE;
     }
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GG_ERR_NO_DEVICE;
     const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-    if (dev < kMaxDevices) g_device_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    const int cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
+    if (dev < kMaxDevices) g_device_info[dev].store(ok ? 1 + cus : -1, std::memory_order_relaxed);
+    *num_cus = cus;
     return ok ? GG_OK : GG_ERR_NO_DEVICE;
 }
 
@@ -78,10 +85,11 @@ int gemm_common(gg::GemmLayout layout, int64_t M, int64_t N, int64_t K, const fl
     if (K > 0 && (overlaps(c, span(A, a_rows, a_cols, lda, 4)) ||
                   overlaps(c, span(B, b_rows, b_cols, ldb, 4))))
         return GG_ERR_ALIAS;
-    if (int st = check_device()) return st;
+    int cus = 0;
+    if (int st = check_device(&cus)) return st;
     (void)hipGetLastError();   // clear a stale error so the check below is ours
     return launch_status(gg::launch_gemm(layout, (int)M, (int)N, (int)K, A, lda, B, ldb, C,
-                                         ldc, reinterpret_cast<hipStream_t>(stream)));
+                                         ldc, cus, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -113,7 +121,8 @@ int gemv_f32(int64_t M, int64_t K, const float *W, int64_t ldw, const float *x, 
     const Span ys = span(y, 1, M, M, 4);
     if (K > 0 && (overlaps(ys, span(W, M, K, ldw, 4)) || overlaps(ys, span(x, 1, K, K, 4))))
         return GG_ERR_ALIAS;
-    if (int st = check_device()) return st;
+    int cus = 0;
+    if (int st = check_device(&cus)) return st;
     (void)hipGetLastError();
     return launch_status(gg::launch_gemv_f32((int)M, (int)K, W, ldw, x, y,
                                              reinterpret_cast<hipStream_t>(stream)));
@@ -132,7 +141,8 @@ int gemv_q2(int64_t M, int64_t K, const uint8_t *Q, int64_t ldq, const uint16_t 
     if (K > 0 && (overlaps(ys, span(Q, M, qcols, ldq, 1)) ||
                   overlaps(ys, span(S, M, scols, lds, 2)) || overlaps(ys, span(x, 1, K, K, 4))))
         return GG_ERR_ALIAS;
-    if (int st = check_device()) return st;
+    int cus = 0;
+    if (int st = check_device(&cus)) return st;
     (void)hipGetLastError();
     return launch_status(gg::launch_gemv_q2((int)M, (int)K, Q, ldq, S, lds, x, y,
                                             reinterpret_cast<hipStream_t>(stream)));

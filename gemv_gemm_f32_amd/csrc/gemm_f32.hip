@@ -8,11 +8,12 @@
 // (16 x 16 workgroup tiles, 4 x 4 register blocks); here the tile is shaped
 // for CDNA4 instead:
 //
-//  * One workgroup of 256 lanes (4 wave64s) owns a 128 x 128 tile of C.  Each
-//    wave owns a 64 x 64 quarter as 2 x 2 blocks of v_mfma_f32_32x32x2_f32,
-//    whose 64 fp32 accumulators per lane stay in registers for the whole K
-//    walk.  The matrix core takes IEEE fp32 operands (no reduced-precision
-//    inputs) and accumulates in fp32.
+//  * One workgroup of 256 lanes (4 wave64s) owns a BM x BN tile of C (128 x 64
+//    or 64 x 64, picked per call from the grid size).  Each wave owns a
+//    quarter as 32 x 32 blocks of v_mfma_f32_32x32x2_f32, whose fp32
+//    accumulators stay in registers for the whole K walk.  The matrix core
+//    takes IEEE fp32 operands (no reduced-precision inputs) and accumulates
+//    in fp32.
 //  * Operands are staged global -> registers -> LDS in k-slabs of BK,
 //    double-buffered: slab k+1 is fetched from global memory while the
 //    MFMAs consume slab k from LDS, with one barrier per slab.
@@ -25,8 +26,8 @@
 //    column k = 8g + 4h + t.  An x-major operand then feeds 4 steps from one
 //    ds_read_b128 per lane (4 consecutive k); a k-major operand feeds each
 //    step from one ds_read_b32 (row 8g + 4h + t, 32 consecutive x per
-//    half-wave).  Row strides (BK + 4 words x-major, 136 words k-major) keep
-//    both reads free of LDS bank conflicts.  The next group's operands are
+//    half-wave).  Row strides (BK + 4 words x-major, tile width + 8 words
+//    k-major) keep both reads free of LDS bank conflicts.  The next group's operands are
 //    read before the current group's MFMAs are issued.
 //  * Edges: loads are clamped into the matrix; entries past the K edge are
 //    zeroed before they reach LDS, and stores outside C are skipped.  The
@@ -49,23 +50,24 @@ namespace {
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128;            // tile rows (M)
-constexpr int BN = 128;            // tile columns (N)
 constexpr int THREADS = 256;
 constexpr int GROUP_M = 4;         // tile rows per ordering group
-constexpr int KSTRIDE = 136;       // words per LDS row, k-major operand
 
-// LDS words per row of an x-major operand tile.
+// LDS words per row of an operand tile of TX values of x by BK values of k:
+// x-major rows hold BK words plus 4 of padding (16 consecutive rows then
+// cover all banks for a 16-byte read); k-major rows hold TX plus 8 (so rows
+// 4 apart, read by the two half-waves, fall 32 banks apart).
 template <int BK>
 constexpr int xstride() { return BK + 4; }
+template <int TX>
+constexpr int kstride() { return TX + 8; }
 
-// LDS words of one operand tile (128 x BK) in either orientation.
-template <int BK, bool XMAJOR>
-constexpr int tile_words() { return XMAJOR ? 128 * xstride<BK>() : BK * KSTRIDE; }
+template <int TX, int BK, bool XMAJOR>
+constexpr int tile_words() { return XMAJOR ? TX * xstride<BK>() : BK * kstride<TX>(); }
 
-// One operand tile of a k-slab: 128 values of x (m or n) by BK values of k.
-//   XMAJOR: element (x, k) at P[x*ld + k]; LDS [x][k], row stride BK + 4.
-//   else  : element (x, k) at P[k*ld + x]; LDS [k][x], row stride KSTRIDE.
+// One operand tile of a k-slab: TX values of x (m or n) by BK values of k.
+//   XMAJOR: element (x, k) at P[x*ld + k]; LDS [x][k].
+//   else  : element (x, k) at P[k*ld + x]; LDS [k][x].
 // Each thread moves NL groups of 4 consecutive elements per slab.
 //
 // Loads are unconditional, from indices clamped into the matrix, so they
@@ -73,9 +75,11 @@ constexpr int tile_words() { return XMAJOR ? 128 * xstride<BK>() : BK * KSTRIDE;
 // the matrix edge only ever meets rows or columns of C that are not stored;
 // values for k past K would enter real sums and are zeroed in store(), which
 // runs after the MFMAs of the current slab.
-template <int BK, bool XMAJOR, int VEC>
+template <int TX, int BK, bool XMAJOR, int VEC>
 struct Operand {
-    static constexpr int NL = BK / 8;
+    static constexpr int NL = TX * BK / 4 / THREADS;
+    static constexpr int KS = kstride<TX>();
+    static_assert(NL >= 1 && NL * 4 * THREADS == TX * BK, "tile must split evenly");
     v4f r[NL];
 
     __device__ __forceinline__ void load(const float *__restrict__ P, int64_t ld, int x0,
@@ -94,8 +98,8 @@ struct Operand {
                     for (int c = 0; c < 4; ++c) r[p][c] = row[min(k + c, K - 1)];
                 }
             } else {
-                const int k = min(k0 + idx / 32, K - 1);
-                const int x = x0 + (idx % 32) * 4;
+                const int k = min(k0 + idx / (TX / 4), K - 1);
+                const int x = x0 + (idx % (TX / 4)) * 4;
                 const float *row = P + (int64_t)k * ld;
                 if (VEC == 4) {
                     r[p] = *reinterpret_cast<const v4f *>(row + min(x, X - 4));
@@ -121,9 +125,9 @@ struct Operand {
                 }
                 *reinterpret_cast<v4f *>(lds + x * xstride<BK>() + k) = v;
             } else {
-                const int k = idx / 32, x = (idx % 32) * 4;
+                const int k = idx / (TX / 4), x = (idx % (TX / 4)) * 4;
                 if (tail && k0 + k >= K) v = v4f{0.f, 0.f, 0.f, 0.f};
-                *reinterpret_cast<v4f *>(lds + k * KSTRIDE + x) = v;
+                *reinterpret_cast<v4f *>(lds + k * KS + x) = v;
             }
         }
     }
@@ -134,8 +138,8 @@ struct Operand {
         if (XMAJOR) {
             return *reinterpret_cast<const v4f *>(lds + (xb + l32) * xstride<BK>() + 8 * g + 4 * h);
         } else {
-            const float *p = lds + (8 * g + 4 * h) * KSTRIDE + xb + l32;
-            return v4f{p[0], p[KSTRIDE], p[2 * KSTRIDE], p[3 * KSTRIDE]};
+            const float *p = lds + (8 * g + 4 * h) * KS + xb + l32;
+            return v4f{p[0], p[KS], p[2 * KS], p[3 * KS]};
         }
     }
 };
@@ -156,17 +160,21 @@ __device__ __forceinline__ void tile_of(int bid, int nwg, int tiles_m, int tiles
 
 // AX: A is stored M x K (x-major tiles); otherwise K x M.
 // BX: B is stored N x K (x-major tiles); otherwise K x N.
-template <int BK, bool AX, bool BX, int VA, int VB>
+// BM x BN tile per workgroup; 2 x 2 waves of (BM/2) x (BN/2), each as
+// (BM/64) x (BN/64) blocks of 32 x 32.
+template <int BM, int BN, int BK, bool AX, bool BX, int VA, int VB>
 __global__ __launch_bounds__(THREADS) void gemm_f32_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
     int tiles_m, int tiles_n) {
     static_assert(BK % 8 == 0, "k walks in groups of 8");
-    constexpr int AW = tile_words<BK, AX>(), BW = tile_words<BK, BX>();
+    constexpr int WM = BM / 2, WN = BN / 2;        // wave tile
+    constexpr int IB = WM / 32, JB = WN / 32;      // 32 x 32 blocks per wave
+    constexpr int AW = tile_words<BM, BK, AX>(), BW = tile_words<BN, BK, BX>();
     __shared__ __attribute__((aligned(16))) float As[2][AW];
     __shared__ __attribute__((aligned(16))) float Bs[2][BW];
-    using OpA = Operand<BK, AX, VA>;
-    using OpB = Operand<BK, BX, VB>;
+    using OpA = Operand<BM, BK, AX, VA>;
+    using OpB = Operand<BN, BK, BX, VB>;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -174,18 +182,18 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_kernel(
     int tm, tn;
     tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;   // wave quarter
+    const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;   // wave quarter
     const int h = lane >> 5;
     const int l32 = lane & 31;
 
     OpA la;
     OpB lb;
 
-    v16f acc[2][2];
+    v16f acc[IB][JB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < IB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < JB; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -206,25 +214,32 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_kernel(
         }
         const float *as = As[buf];
         const float *bs = Bs[buf];
-        v4f fa0 = OpA::frag(as, 0, wm, l32, h), fa1 = OpA::frag(as, 0, wm + 32, l32, h);
-        v4f fb0 = OpB::frag(bs, 0, wn, l32, h), fb1 = OpB::frag(bs, 0, wn + 32, l32, h);
+        v4f fa[IB], fb[JB];
+#pragma unroll
+        for (int i = 0; i < IB; ++i) fa[i] = OpA::frag(as, 0, wm + 32 * i, l32, h);
+#pragma unroll
+        for (int j = 0; j < JB; ++j) fb[j] = OpB::frag(bs, 0, wn + 32 * j, l32, h);
 #pragma unroll
         for (int g = 0; g < BK / 8; ++g) {
-            v4f na0 = fa0, na1 = fa1, nb0 = fb0, nb1 = fb1;
-            if (g + 1 < BK / 8) {
-                na0 = OpA::frag(as, g + 1, wm, l32, h);
-                na1 = OpA::frag(as, g + 1, wm + 32, l32, h);
-                nb0 = OpB::frag(bs, g + 1, wn, l32, h);
-                nb1 = OpB::frag(bs, g + 1, wn + 32, l32, h);
-            }
+            v4f na[IB], nb[JB];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa0[t], fb0[t], acc[0][0], 0, 0, 0);
-                acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa0[t], fb1[t], acc[0][1], 0, 0, 0);
-                acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa1[t], fb0[t], acc[1][0], 0, 0, 0);
-                acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa1[t], fb1[t], acc[1][1], 0, 0, 0);
-            }
-            fa0 = na0; fa1 = na1; fb0 = nb0; fb1 = nb1;
+            for (int i = 0; i < IB; ++i)
+                na[i] = g + 1 < BK / 8 ? OpA::frag(as, g + 1, wm + 32 * i, l32, h) : fa[i];
+#pragma unroll
+            for (int j = 0; j < JB; ++j)
+                nb[j] = g + 1 < BK / 8 ? OpB::frag(bs, g + 1, wn + 32 * j, l32, h) : fb[j];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < IB; ++i)
+#pragma unroll
+                    for (int j = 0; j < JB; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][t], fb[j][t],
+                                                                        acc[i][j], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < IB; ++i) fa[i] = na[i];
+#pragma unroll
+            for (int j = 0; j < JB; ++j) fb[j] = nb[j];
         }
         if (more) {
             la.store(As[buf ^ 1], tid, (kt + 1) * BK, K);
@@ -236,9 +251,9 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_kernel(
     // Accumulator layout of a 32 x 32 block: register r of lane l holds
     // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < IB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < JB; ++j) {
             const int col = n0 + wn + 32 * j + l32;
             if (col >= N) continue;
 #pragma unroll
@@ -251,13 +266,13 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_kernel(
 
 constexpr int PROD_BK = 32;
 
-template <bool AX, bool BX, int VA, int VB, int BK = PROD_BK>
+template <bool AX, bool BX, int VA, int VB, int BM = 128, int BN = 128, int BK = PROD_BK>
 hipError_t launch_t(int M, int N, int K, const float *A, int64_t lda, const float *B,
                     int64_t ldb, float *C, int64_t ldc, hipStream_t s) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const int nwg = tiles_m * tiles_n;
-    hipLaunchKernelGGL((gemm_f32_kernel<BK, AX, BX, VA, VB>), dim3(nwg), dim3(THREADS), 0, s,
-                       M, N, K, A, lda, B, ldb, C, ldc, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, BK, AX, BX, VA, VB>), dim3(nwg), dim3(THREADS),
+                       0, s, M, N, K, A, lda, B, ldb, C, ldc, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
@@ -266,7 +281,8 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 }  // namespace
 
 hipError_t launch_gemm(GemmLayout layout, int M, int N, int K, const float *A, int64_t lda,
-                       const float *B, int64_t ldb, float *C, int64_t ldc, hipStream_t s) {
+                       const float *B, int64_t ldb, float *C, int64_t ldc, int num_cus,
+                       hipStream_t s) {
     // 16-byte loads need the operand's contiguous extent, its leading
     // dimension and its base all to be multiples of 4 floats.
     const bool ax = layout != GemmLayout::TN;     // A stored M x K
@@ -275,17 +291,26 @@ hipError_t launch_gemm(GemmLayout layout, int M, int N, int K, const float *A, i
     const int b_contig = bx ? K : N;
     const bool va = aligned16(A) && (lda % 4 == 0) && (a_contig % 4 == 0);
     const bool vb = aligned16(B) && (ldb % 4 == 0) && (b_contig % 4 == 0);
-#define GG_GEMM_CASE(AX_, BX_)                                                          \
-    if (va && vb) return launch_t<AX_, BX_, 4, 4>(M, N, K, A, lda, B, ldb, C, ldc, s); \
-    if (va) return launch_t<AX_, BX_, 4, 1>(M, N, K, A, lda, B, ldb, C, ldc, s);       \
-    if (vb) return launch_t<AX_, BX_, 1, 4>(M, N, K, A, lda, B, ldb, C, ldc, s);       \
-    return launch_t<AX_, BX_, 1, 1>(M, N, K, A, lda, B, ldb, C, ldc, s);
+    // Tile shape: 128 x 64 when that grid still gives every CU two tiles to
+    // interleave; otherwise 64 x 64, four times the tiles of 128 x 128, which
+    // keeps small and K-heavy products (few output tiles) spread over the CUs.
+    const int64_t tiles_128x64 = (int64_t)((M + 127) / 128) * ((N + 63) / 64);
+    const bool big = tiles_128x64 >= 2 * (int64_t)num_cus;
+#define GG_GEMM_SHAPE(AX_, BX_, VA_, VB_)                                                   \
+    return big ? launch_t<AX_, BX_, VA_, VB_, 128, 64>(M, N, K, A, lda, B, ldb, C, ldc, s) \
+               : launch_t<AX_, BX_, VA_, VB_, 64, 64>(M, N, K, A, lda, B, ldb, C, ldc, s);
+#define GG_GEMM_CASE(AX_, BX_)                      \
+    if (va && vb) { GG_GEMM_SHAPE(AX_, BX_, 4, 4) } \
+    if (va) { GG_GEMM_SHAPE(AX_, BX_, 4, 1) }       \
+    if (vb) { GG_GEMM_SHAPE(AX_, BX_, 1, 4) }       \
+    GG_GEMM_SHAPE(AX_, BX_, 1, 1)
     switch (layout) {
         case GemmLayout::NN: { GG_GEMM_CASE(true, false) }
         case GemmLayout::TN: { GG_GEMM_CASE(false, false) }
         case GemmLayout::NT: { GG_GEMM_CASE(true, true) }
     }
 #undef GG_GEMM_CASE
+#undef GG_GEMM_SHAPE
     return hipErrorInvalidValue;
 }
 

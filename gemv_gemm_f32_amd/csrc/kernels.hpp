@@ -13,10 +13,11 @@ namespace gg {
 
 enum class GemmLayout { NN, TN, NT };
 
-// C = op(A).op(B) for the three layouts of gemvgemm.h.
+// C = op(A).op(B) for the three layouts of gemvgemm.h; num_cus is the
+// device's compute-unit count (it picks the tile shape).
 hipError_t launch_gemm(GemmLayout layout, int M, int N, int K,
                        const float *A, int64_t lda, const float *B, int64_t ldb,
-                       float *C, int64_t ldc, hipStream_t stream);
+                       float *C, int64_t ldc, int num_cus, hipStream_t stream);
 
 // y = W.x, fp32.
 hipError_t launch_gemv_f32(int M, int K, const float *W, int64_t ldw,
