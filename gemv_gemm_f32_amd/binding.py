@@ -27,7 +27,7 @@ GG_ERR_NO_DEVICE = -3
 GG_ERR_LAUNCH = -4
 
 ENTRY_POINTS = ("gemm_f32", "gemm_f32_tn", "gemm_f32_nt", "gemv_f32", "gemv_q2",
-                "gg_strerror")
+                "gemv_q2_batched", "gg_strerror")
 
 _lib = None
 
@@ -67,6 +67,9 @@ def load(path: str = LIB_PATH):
     lib.gemv_f32.restype = ctypes.c_int
     lib.gemv_q2.argtypes = [i64, i64, vp, i64, vp, i64, vp, vp, vp]
     lib.gemv_q2.restype = ctypes.c_int
+    pp = ctypes.POINTER(ctypes.c_void_p)
+    lib.gemv_q2_batched.argtypes = [i64, i64, i64, pp, i64, pp, i64, pp, pp, vp]
+    lib.gemv_q2_batched.restype = ctypes.c_int
     lib.gg_strerror.argtypes = [ctypes.c_int]
     lib.gg_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -204,3 +207,45 @@ def gemv_q2(Q, S, x, y=None, stream=None):
     _check(load().gemv_q2(M, K, pq, ldq, ps, lds, _vec(x, torch.float32, "x"),
                           _vec(y, torch.float32, "y"), _stream(stream)), "gemv_q2")
     return y
+
+
+def _ptr_array(ptrs):
+    arr = (ctypes.c_void_p * max(len(ptrs), 1))()
+    for i, p in enumerate(ptrs):
+        arr[i] = p
+    return arr
+
+
+def gemv_q2_batched(Qs, Ss, xs, ys=None, stream=None):
+    """y_b = W_b.x_b for every b: lists of Q (uint8 M x >= ceil(K/4)), S
+    (float16/int16 M x >= ceil(K/64)), x (K,) fp32; all Q share one shape and
+    leading dimension, as do all S.  Returns the list of outputs."""
+    torch = _torch()
+    n = len(Qs)
+    if len(Ss) != n or len(xs) != n:
+        raise ValueError("Qs, Ss and xs must have the same length")
+    if n == 0:
+        return []
+    M, K = Qs[0].shape[0], xs[0].shape[0]
+    if ys is None:
+        ys = [torch.empty(M, dtype=torch.float32, device=Qs[0].device) for _ in range(n)]
+    qp, sp, xp, yp, ldq, lds = [], [], [], [], None, None
+    for Q, S, x, y in zip(Qs, Ss, xs, ys):
+        if Q.shape[0] != M or S.shape[0] != M or x.shape != (K,) or y.shape != (M,):
+            raise ValueError("every product must have the same M and K")
+        if S.dtype not in (torch.float16, torch.int16):
+            raise TypeError("S must hold binary16 bit patterns (float16 or int16)")
+        pq, lq = _mat(Q, torch.uint8, "Q")
+        ps, ls = _mat(S.view(torch.float16), torch.float16, "S")
+        if ldq is None:
+            ldq, lds = lq, ls
+        elif (lq, ls) != (ldq, lds):
+            raise ValueError("every Q (and every S) must have the same leading dimension")
+        qp.append(pq)
+        sp.append(ps)
+        xp.append(_vec(x, torch.float32, "x"))
+        yp.append(_vec(y, torch.float32, "y"))
+    _check(load().gemv_q2_batched(n, M, K, _ptr_array(qp), ldq, _ptr_array(sp), lds,
+                                  _ptr_array(xp), _ptr_array(yp), _stream(stream)),
+           "gemv_q2_batched")
+    return ys

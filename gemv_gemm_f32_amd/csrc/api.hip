@@ -6,9 +6,11 @@
 // launch to a status.  No exception or abort leaves this file.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "../../include/gemvgemm.h"
 #include "kernels.hpp"
@@ -128,24 +130,59 @@ int gemv_f32(int64_t M, int64_t K, const float *W, int64_t ldw, const float *x, 
                                              reinterpret_cast<hipStream_t>(stream)));
 }
 
+int gemv_q2_batched(int64_t count, int64_t M, int64_t K, const uint8_t *const *Q, int64_t ldq,
+                    const uint16_t *const *S, int64_t lds, const float *const *x,
+                    float *const *y, gg_stream_t stream) {
+    if (count < 0 || count > kMaxDim || M < 0 || K < 0 || M > kMaxDim || K > kMaxDim)
+        return GG_ERR_INVALID_ARG;
+    if (count == 0 || M == 0) return GG_OK;
+    if (Q == nullptr || S == nullptr || x == nullptr || y == nullptr) return GG_ERR_INVALID_ARG;
+    const int64_t qcols = (K + 3) / 4, scols = (K + 63) / 64;
+    if (K > 0 && (ldq < qcols || lds < scols || ldq > kMaxDim || lds > kMaxDim))
+        return GG_ERR_INVALID_ARG;
+    for (int64_t b = 0; b < count; ++b) {
+        if (bad_ptr(y[b], 4)) return GG_ERR_INVALID_ARG;
+        if (K > 0 && (bad_ptr(Q[b], 1) || bad_ptr(S[b], 2) || bad_ptr(x[b], 4)))
+            return GG_ERR_INVALID_ARG;
+    }
+    // Every output must be disjoint from every input and from every other
+    // output, across the whole batch (inputs may overlap each other, e.g. a
+    // shared x).  Sorted sweep: an interval overlaps an earlier one exactly
+    // when its start lies below the largest end seen so far.
+    if (K > 0 || count > 1) {
+        struct Iv { Span s; bool out; };
+        std::vector<Iv> iv;
+        iv.reserve((size_t)count * 4);
+        for (int64_t b = 0; b < count; ++b) {
+            iv.push_back({span(y[b], 1, M, M, 4), true});
+            if (K > 0) {
+                iv.push_back({span(Q[b], M, qcols, ldq, 1), false});
+                iv.push_back({span(S[b], M, scols, lds, 2), false});
+                iv.push_back({span(x[b], 1, K, K, 4), false});
+            }
+        }
+        std::sort(iv.begin(), iv.end(), [](const Iv &a, const Iv &b) { return a.s.lo < b.s.lo; });
+        uintptr_t end_all = 0, end_out = 0;
+        for (const Iv &v : iv) {
+            if (v.s.lo >= v.s.hi) continue;
+            if (v.out ? end_all > v.s.lo : end_out > v.s.lo) return GG_ERR_ALIAS;
+            end_all = end_all > v.s.hi ? end_all : v.s.hi;
+            if (v.out) end_out = end_out > v.s.hi ? end_out : v.s.hi;
+        }
+    }
+    int cus = 0;
+    if (int st = check_device(&cus)) return st;
+    (void)hipGetLastError();
+    return launch_status(gg::launch_gemv_q2((int)count, (int)M, (int)K, Q, ldq, S, lds, x, y,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
 int gemv_q2(int64_t M, int64_t K, const uint8_t *Q, int64_t ldq, const uint16_t *S,
             int64_t lds, const float *x, float *y, gg_stream_t stream) {
     if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim) return GG_ERR_INVALID_ARG;
     if (M == 0) return GG_OK;
-    if (bad_ptr(y, 4)) return GG_ERR_INVALID_ARG;
-    const int64_t qcols = (K + 3) / 4, scols = (K + 63) / 64;
-    if (K > 0 && (bad_ptr(Q, 1) || bad_ptr(S, 2) || bad_ptr(x, 4))) return GG_ERR_INVALID_ARG;
-    if (K > 0 && (ldq < qcols || lds < scols || ldq > kMaxDim || lds > kMaxDim))
-        return GG_ERR_INVALID_ARG;
-    const Span ys = span(y, 1, M, M, 4);
-    if (K > 0 && (overlaps(ys, span(Q, M, qcols, ldq, 1)) ||
-                  overlaps(ys, span(S, M, scols, lds, 2)) || overlaps(ys, span(x, 1, K, K, 4))))
-        return GG_ERR_ALIAS;
-    int cus = 0;
-    if (int st = check_device(&cus)) return st;
-    (void)hipGetLastError();
-    return launch_status(gg::launch_gemv_q2((int)M, (int)K, Q, ldq, S, lds, x, y,
-                                            reinterpret_cast<hipStream_t>(stream)));
+    // one product of the batched entry point (same checks, same kernel)
+    return gemv_q2_batched(1, M, K, &Q, ldq, &S, lds, &x, &y, stream);
 }
 
 const char *gg_strerror(int status) {

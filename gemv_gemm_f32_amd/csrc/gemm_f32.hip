@@ -162,7 +162,7 @@ __device__ __forceinline__ void tile_of(int bid, int nwg, int tiles_m, int tiles
 // BX: B is stored N x K (x-major tiles); otherwise K x N.
 // BM x BN tile per workgroup; 2 x 2 waves of (BM/2) x (BN/2), each as
 // (BM/64) x (BN/64) blocks of 32 x 32.
-template <int BM, int BN, int BK, bool AX, bool BX, int VA, int VB>
+template <int BM, int BN, int BK, bool AX, bool BX, int VA, int VB, bool FENCE = true>
 __global__ __launch_bounds__(THREADS) void gemm_f32_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
@@ -228,6 +228,10 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_kernel(
 #pragma unroll
             for (int j = 0; j < JB; ++j)
                 nb[j] = g + 1 < BK / 8 ? OpB::frag(bs, g + 1, wn + 32 * j, l32, h) : fb[j];
+            // Keep the next group's LDS reads ahead of this group's MFMAs:
+            // left alone, the scheduler sinks each read to just before its
+            // use and the MFMA pipe waits on LDS latency.
+            if (FENCE) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -236,6 +240,7 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_kernel(
                     for (int j = 0; j < JB; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][t], fb[j][t],
                                                                         acc[i][j], 0, 0, 0);
+            if (FENCE) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < IB; ++i) fa[i] = na[i];
 #pragma unroll
@@ -266,12 +271,13 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_kernel(
 
 constexpr int PROD_BK = 32;
 
-template <bool AX, bool BX, int VA, int VB, int BM = 128, int BN = 128, int BK = PROD_BK>
+template <bool AX, bool BX, int VA, int VB, int BM = 128, int BN = 128, int BK = PROD_BK,
+          bool FENCE = true>
 hipError_t launch_t(int M, int N, int K, const float *A, int64_t lda, const float *B,
                     int64_t ldb, float *C, int64_t ldc, hipStream_t s) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const int nwg = tiles_m * tiles_n;
-    hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, BK, AX, BX, VA, VB>), dim3(nwg), dim3(THREADS),
+    hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, BK, AX, BX, VA, VB, FENCE>), dim3(nwg), dim3(THREADS),
                        0, s, M, N, K, A, lda, B, ldb, C, ldc, tiles_m, tiles_n);
     return hipGetLastError();
 }

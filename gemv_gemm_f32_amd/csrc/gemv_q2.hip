@@ -49,6 +49,16 @@ constexpr int WAVES = THREADS / 64;
 constexpr int WPL = 3;                 // code words per lane per pass
 constexpr int WORDS_PER_PASS = 32 * WPL;
 
+// Device pointers of up to NB products of one shape, passed by value in the
+// kernel arguments (blockIdx.y selects the product).
+template <int NB>
+struct Q2Ptrs {
+    const uint8_t *Q[NB];
+    const uint16_t *S[NB];
+    const float *x[NB];
+    float *y[NB];
+};
+
 // Words of 16 codes: fast specialisation loads them whole; the generic one
 // assembles them from bytes, zeroing columns at or beyond K.
 template <bool FAST>
@@ -68,11 +78,18 @@ __device__ __forceinline__ unsigned load_word(const uint8_t *__restrict__ Qrow, 
     return w;
 }
 
-template <int RPL, bool FAST>
-__global__ __launch_bounds__(THREADS) void gemv_q2_kernel(
-    int M, int K, const uint8_t *__restrict__ Q, int64_t ldq,
-    const uint16_t *__restrict__ S, int64_t lds, const float *__restrict__ x,
-    float *__restrict__ y) {
+// RPL rows per half-wave; FAST: word loads and 32-bit offsets; FULL (with
+// FAST): every wave's rows and every pass's words exist, so no index is
+// clamped; NB: number of matrices the pointer block holds (blockIdx.y picks
+// one).
+template <int RPL, bool FAST, bool FULL, int NB>
+__global__ __launch_bounds__(THREADS) void gemv_q2_kernel(int M, int K, int64_t ldq,
+                                                          int64_t lds, Q2Ptrs<NB> ptrs) {
+    const int b = NB == 1 ? 0 : (int)blockIdx.y;
+    const uint8_t *__restrict__ Q = ptrs.Q[b];
+    const uint16_t *__restrict__ S = ptrs.S[b];
+    const float *__restrict__ x = ptrs.x[b];
+    float *__restrict__ y = ptrs.y[b];
     const int lane = threadIdx.x & 63;
     const int j = lane & 31;
     const int wave = blockIdx.x * WAVES + (threadIdx.x >> 6);
@@ -103,6 +120,29 @@ __global__ __launch_bounds__(THREADS) void gemv_q2_kernel(
         v4f xraw[WPL][4];
         unsigned craw[RPL][WPL];
         unsigned sraw[RPL][WPL];          // binary16 bits, zero-extended
+        if (FULL) {
+            // Every row and word of this wave exists: one per-lane base and
+            // compile-time offsets (row m adds m*ldq, word q adds 32q words).
+            const char *xb = reinterpret_cast<const char *>(x) + (unsigned)(w0 + j) * 64u;
+            const unsigned qb = (unsigned)row0 * (unsigned)ldq + (unsigned)(w0 + j) * 4u;
+            const unsigned sb = ((unsigned)row0 * (unsigned)lds + (unsigned)((w0 + j) >> 2)) * 2u;
+#pragma unroll
+            for (int q = 0; q < WPL; ++q)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    xraw[q][c] = *reinterpret_cast<const v4f *>(xb + 2048 * q + 16 * c);
+#pragma unroll
+            for (int m = 0; m < RPL; ++m)
+#pragma unroll
+                for (int q = 0; q < WPL; ++q) {
+                    craw[m][q] = *reinterpret_cast<const unsigned *>(
+                        reinterpret_cast<const char *>(Q) + qb + (unsigned)m * (unsigned)ldq +
+                        128u * q);
+                    sraw[m][q] = *reinterpret_cast<const uint16_t *>(
+                        reinterpret_cast<const char *>(S) + sb + (unsigned)m * (unsigned)lds * 2u +
+                        16u * q);
+                }
+        } else {
 #pragma unroll
         for (int q = 0; q < WPL; ++q) {
             const int wd = w0 + j + 32 * q;
@@ -143,6 +183,7 @@ __global__ __launch_bounds__(THREADS) void gemv_q2_kernel(
                 }
             }
         }
+        }
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- Dead words (past the row's end, only in a last partial pass)
@@ -150,7 +191,7 @@ __global__ __launch_bounds__(THREADS) void gemv_q2_kernel(
         // computed on a clamped row and never stored.
         float xv[WPL][16];
         unsigned sbits[RPL][WPL];
-        if (w0 + WORDS_PER_PASS <= words && FAST) {      // uniform
+        if (FULL || (FAST && w0 + WORDS_PER_PASS <= words)) {
 #pragma unroll
             for (int q = 0; q < WPL; ++q) {
 #pragma unroll
@@ -215,26 +256,58 @@ __global__ __launch_bounds__(THREADS) void gemv_q2_kernel(
     }
 }
 
-}  // namespace
-
-hipError_t launch_gemv_q2(int M, int K, const uint8_t *Q, int64_t ldq, const uint16_t *S,
-                          int64_t lds, const float *x, float *y, hipStream_t s) {
-    constexpr int RPL = 6;
+// A single product needs every SIMD busy: 6 rows per half-wave gives one
+// wave per SIMD at 12,288 rows.  A batch has waves to spare, so each lane
+// takes more rows and reuses its x registers and word sums longer.
+template <int NB, int RPL = (NB == 1 ? 6 : 12)>
+hipError_t launch_chunk(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
+                        const uint16_t *const *S, int64_t lds, const float *const *x,
+                        float *const *y, hipStream_t s) {
     const int rows_per_wg = WAVES * 2 * RPL;
-    const int nwg = (M + rows_per_wg - 1) / rows_per_wg;
+    const dim3 grid((M + rows_per_wg - 1) / rows_per_wg, count);
+    Q2Ptrs<NB> p;
+    bool aligned = true;
+    for (int b = 0; b < NB; ++b) {
+        const int i = b < count ? b : 0;
+        p.Q[b] = Q[i];
+        p.S[b] = S[i];
+        p.x[b] = x[i];
+        p.y[b] = y[i];
+        aligned = aligned && reinterpret_cast<uintptr_t>(Q[i]) % 4 == 0 &&
+                  reinterpret_cast<uintptr_t>(x[i]) % 16 == 0;
+    }
     // word loads, 16-byte x loads, and 32-bit byte offsets into Q and S
-    const bool fast = (K % 16 == 0) && (ldq % 4 == 0) &&
-                      (reinterpret_cast<uintptr_t>(Q) % 4 == 0) &&
-                      (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+    const bool fast = aligned && (K % 16 == 0) && (ldq % 4 == 0) &&
                       (int64_t)M * ldq < (int64_t(1) << 32) &&
                       (int64_t)M * lds * 2 < (int64_t(1) << 32);
-    if (fast)
-        hipLaunchKernelGGL((gemv_q2_kernel<RPL, true>), dim3(nwg), dim3(THREADS), 0, s,
-                           M, K, Q, ldq, S, lds, x, y);
+    const bool full = fast && (K % (16 * WORDS_PER_PASS) == 0) && (M % (2 * RPL) == 0);
+    if (full)
+        hipLaunchKernelGGL((gemv_q2_kernel<RPL, true, true, NB>), grid, dim3(THREADS), 0, s,
+                           M, K, ldq, lds, p);
+    else if (fast)
+        hipLaunchKernelGGL((gemv_q2_kernel<RPL, true, false, NB>), grid, dim3(THREADS), 0, s,
+                           M, K, ldq, lds, p);
     else
-        hipLaunchKernelGGL((gemv_q2_kernel<RPL, false>), dim3(nwg), dim3(THREADS), 0, s,
-                           M, K, Q, ldq, S, lds, x, y);
+        hipLaunchKernelGGL((gemv_q2_kernel<RPL, false, false, NB>), grid, dim3(THREADS), 0, s,
+                           M, K, ldq, lds, p);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv_q2(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
+                          const uint16_t *const *S, int64_t lds, const float *const *x,
+                          float *const *y, hipStream_t s) {
+    if (count == 1) return launch_chunk<1>(1, M, K, Q, ldq, S, lds, x, y, s);
+    // Up to Q2_MAX_BATCH products per launch (their pointers travel in the
+    // kernel arguments); larger batches take several launches in order.
+    for (int b0 = 0; b0 < count; b0 += Q2_MAX_BATCH) {
+        const int n = count - b0 < Q2_MAX_BATCH ? count - b0 : Q2_MAX_BATCH;
+        const hipError_t e = launch_chunk<Q2_MAX_BATCH>(n, M, K, Q + b0, ldq, S + b0, lds,
+                                                        x + b0, y + b0, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace gg

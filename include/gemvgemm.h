@@ -125,6 +125,27 @@ int gemv_q2(int64_t M, int64_t K, const uint8_t *Q, int64_t ldq,
             const uint16_t *S, int64_t lds,
             const float *x, float *y, gg_stream_t stream);
 
+/*
+ * y_b = W_b . x_b for b = 0 .. count-1: count independent 2-bit products of
+ * one shape (M, K, ldq, lds), each exactly as gemv_q2 defines it, in as few
+ * launches as possible (up to 64 products per launch).  "Kernel 0112",
+ * section "What is being measured", runs this product 40 times per generated
+ * token; one launch per product pays a fixed dispatch cost each time, which
+ * at this size is as large as the product itself.
+ *   Q, S, x, y: HOST arrays of count DEVICE pointers (Q[b], S[b], x[b], y[b]
+ *   as in gemv_q2).  The arrays are read during the call and not kept.
+ *   Every y[b] must be disjoint from every input and from every other y[c]
+ *   (else GG_ERR_ALIAS); inputs may be shared (for example one x for all).
+ * A batch runs the same arithmetic per product as gemv_q2, with more rows
+ * per thread; results meet the same tolerance and are reproducible run to
+ * run, but a batch may sum in a different order from a gemv_q2 call and so
+ * need not match it bit for bit.
+ */
+int gemv_q2_batched(int64_t count, int64_t M, int64_t K,
+                    const uint8_t *const *Q, int64_t ldq,
+                    const uint16_t *const *S, int64_t lds,
+                    const float *const *x, float *const *y, gg_stream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *gg_strerror(int status);
 

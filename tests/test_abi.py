@@ -130,3 +130,32 @@ def test_single_hip_runtime_in_process():
     maps = open("/proc/self/maps").read()
     hip = set(re.findall(r"\S*libamdhip64\S*", maps))
     assert len(hip) == 1, hip
+
+
+def _parr(*ps):
+    arr = (ctypes.c_void_p * len(ps))()
+    for i, p in enumerate(ps):
+        arr[i] = p
+    return arr
+
+
+def test_gemv_q2_batched_validation():
+    f = lib.gemv_q2_batched
+    Q = _parr(PA, PA + 0x100000)
+    S = _parr(PB, PB + 0x100000)
+    x = _parr(PX, PX)                    # a shared x is allowed
+    y = _parr(PC, PC + 0x100000)
+    assert f(-1, 4, 64, Q, 16, S, 1, x, y, None) == bd.GG_ERR_INVALID_ARG
+    assert f(0, 4, 64, None, 16, None, 1, None, None, None) == bd.GG_OK
+    assert f(2, 0, 64, Q, 16, S, 1, x, y, None) == bd.GG_OK
+    assert f(2, 4, 64, None, 16, S, 1, x, y, None) == bd.GG_ERR_INVALID_ARG
+    assert f(2, 4, 64, Q, 15, S, 1, x, y, None) == bd.GG_ERR_INVALID_ARG
+    assert f(2, 4, 64, Q, 16, S, 1, x, _parr(PC, PC + 2), None) == bd.GG_ERR_INVALID_ARG
+    # y[1] overlaps y[0]
+    assert f(2, 4, 64, Q, 16, S, 1, x, _parr(PC, PC + 8), None) == bd.GG_ERR_ALIAS
+    # y[1] overlaps the codes of product 0
+    assert f(2, 4, 64, Q, 16, S, 1, x, _parr(PC, PA + 16), None) == bd.GG_ERR_ALIAS
+    # y[0] overlaps the shared x
+    assert f(2, 4, 64, Q, 16, S, 1, x, _parr(PX + 4, PC), None) == bd.GG_ERR_ALIAS
+    st = f(2, 4, 64, Q, 16, S, 1, x, y, None)
+    assert st not in (bd.GG_ERR_ALIAS, bd.GG_ERR_INVALID_ARG)

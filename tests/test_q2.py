@@ -133,3 +133,101 @@ def test_deterministic():
     a = host(bd.gemv_q2(dQ, dS, dx))
     b = host(bd.gemv_q2(dQ, dS, dx))
     assert np.array_equal(a, b)
+
+
+def _rotation(n, M=12288, K=1536, start=0):
+    out = []
+    for r in range(start, start + n):
+        Q, S = inputs.q2_weight(r, M, K)
+        out.append((Q, S))
+    return out
+
+
+def test_batched_equals_single_calls_bitwise():
+    mats = _rotation(5, 3000, 1536)
+    x = inputs.q2_x()
+    dQ = [dev(Q) for Q, _ in mats]
+    dS = [dev(S.view(np.int16)) for _, S in mats]
+    dx = dev(x)
+    ys = bd.gemv_q2_batched(dQ, dS, [dx] * 5)
+    for b, (Q, S) in enumerate(mats):
+        single = host(bd.gemv_q2(dQ[b], dS[b], dx))
+        assert np.array_equal(host(ys[b]), single), b
+        ref, bound = oracle.gemv_q2(Q, S, x)
+        assert_close(host(ys[b]), ref, bound, "batched %d" % b)
+
+
+def test_batched_more_than_one_launch_and_own_x():
+    # 70 products: two launches of the kernel (64 + 6); distinct x per product
+    M, K = 200, 320
+    n = 70
+    rng = np.random.default_rng(3)
+    Qs = [rng.integers(0, 256, (M, K // 4), dtype=np.uint8) for _ in range(n)]
+    Ss = [rng.uniform(0.01, 0.05, (M, K // 64)).astype(np.float16).view(np.uint16) for _ in range(n)]
+    xs = [inputs.normal(rng, (K,)) for _ in range(n)]
+    ys = bd.gemv_q2_batched([dev(q) for q in Qs], [dev(s.view(np.int16)) for s in Ss],
+                            [dev(x) for x in xs])
+    for b in range(n):
+        ref, bound = oracle.gemv_q2(Qs[b], Ss[b], xs[b])
+        assert_close(host(ys[b]), ref, bound, "product %d" % b)
+
+
+def test_batched_ragged_shape_generic_path():
+    M, K = 37, 70
+    rng = np.random.default_rng(4)
+    mats = []
+    for b in range(3):
+        codes = rng.integers(0, 4, (M, K))
+        mats.append((_pack(codes), _scales(M, K)))
+    x = inputs.normal(rng, (K,))
+    ys = bd.gemv_q2_batched([dev(Q) for Q, _ in mats], [dev(S.view(np.int16)) for _, S in mats],
+                            [dev(x)] * 3)
+    for b, (Q, S) in enumerate(mats):
+        ref, bound = oracle.gemv_q2(Q, S, x)
+        assert_close(host(ys[b]), ref, bound, "ragged %d" % b)
+
+
+def test_batched_large_full_size():
+    # 12 products of the full 12,288 x 1,536 shape in one launch
+    n = 12
+    mats = _rotation(n)
+    x = inputs.q2_x()
+    dQ = [dev(Q) for Q, _ in mats]
+    dS = [dev(S.view(np.int16)) for _, S in mats]
+    dx = dev(x)
+    ys = [host(y) for y in bd.gemv_q2_batched(dQ, dS, [dx] * n)]
+    again = [host(y) for y in bd.gemv_q2_batched(dQ, dS, [dx] * n)]
+    for b in (0, 5, 11):
+        ref, bound = oracle.gemv_q2(mats[b][0], mats[b][1], x)
+        assert_close(ys[b], ref, bound, "large batch %d" % b)
+    for b in range(n):
+        assert np.array_equal(ys[b], again[b]), "not reproducible"
+
+
+@pytest.mark.parametrize("M,K", [(12345, 3072), (20000, 640), (11000, 1600)])
+def test_batched_large_ragged(M, K):
+    # M not a multiple of any workgroup's rows; K of 48, 10 and 25 scale groups
+    n = max(2, -(-131072 // M))
+    rng = np.random.default_rng(M + K)
+    Qs = [rng.integers(0, 256, (M, K // 4), dtype=np.uint8) for _ in range(n)]
+    Ss = [rng.uniform(0.01, 0.05, (M, K // 64)).astype(np.float16).view(np.uint16) for _ in range(n)]
+    xs = [inputs.normal(rng, (K,)) for _ in range(n)]
+    ys = bd.gemv_q2_batched([dev(q) for q in Qs], [dev(s.view(np.int16)) for s in Ss],
+                            [dev(x) for x in xs])
+    for b in (0, n - 1):
+        ref, bound = oracle.gemv_q2(Qs[b], Ss[b], xs[b])
+        assert_close(host(ys[b]), ref, bound, "%dx%d product %d" % (M, K, b))
+
+
+def test_batched_large_integer_exact():
+    # scale 2 and integer x: every partial sum is an exact integer
+    M, K, n = 16384, 1536, 8
+    rng = np.random.default_rng(8)
+    codes = [rng.integers(0, 4, (M, K)) for _ in range(2)]
+    Qs = [_pack(c) for c in codes] * (n // 2)
+    S = np.full((M, K // 64), 0x4000, np.uint16)
+    x = inputs.integers(rng, (K,))
+    ys = bd.gemv_q2_batched([dev(q) for q in Qs], [dev(S.view(np.int16))] * n, [dev(x)] * n)
+    for b in range(2):
+        ref, _ = oracle.gemv_q2(Qs[b], S, x)
+        assert np.array_equal(host(ys[b]).astype(np.float64), ref)
