@@ -14,32 +14,42 @@
 //    accumulators stay in registers for the whole K walk.  The matrix core
 //    takes IEEE fp32 operands (no reduced-precision inputs) and accumulates
 //    in fp32.
-//  * Operands are staged global -> registers -> LDS in k-slabs of BK,
-//    double-buffered: slab k+1 is fetched from global memory while the
-//    MFMAs consume slab k from LDS, with one barrier per slab.
-//  * No operand is ever transposed.  Each operand tile is copied into LDS in
-//    the orientation it has in global memory, with 16-byte loads and writes:
-//      x-major  ([x][k], rows along k): an operand stored M x K or N x K;
-//      k-major  ([k][x], rows along x): an operand stored K x M or K x N.
-//    The sum over k may be taken in any order, so the MFMA steps walk k in
-//    groups of 8 with step t (0..3) of a group taking, in half-wave h, the
-//    column k = 8g + 4h + t.  An x-major operand then feeds 4 steps from one
-//    ds_read_b128 per lane (4 consecutive k); a k-major operand feeds each
-//    step from one ds_read_b32 (row 8g + 4h + t, 32 consecutive x per
-//    half-wave).  Row strides (BK + 4 words x-major, tile width + 8 words
-//    k-major) keep both reads free of LDS bank conflicts.  The next group's operands are
-//    read before the current group's MFMAs are issued.
-//  * Edges: loads are clamped into the matrix; entries past the K edge are
-//    zeroed before they reach LDS, and stores outside C are skipped.  The
-//    16-byte load path is a compile-time specialisation taken when pointers,
-//    leading dimensions and the contiguous extent are multiples of 4;
-//    otherwise the same kernel is instantiated with scalar loads.
+//  * Operand tiles are staged in LDS in k-slabs of BK = 32, double-buffered:
+//    slab k+1 is fetched while the MFMAs consume slab k, with one barrier per
+//    slab.  The sum over k may be taken in any order, so the MFMA steps walk k
+//    in groups of 8 with step t (0..3) of a group taking, in half-wave h, the
+//    column k = 8g + 4h + t.  An x-major operand ([x][k], stored M x K or
+//    N x K) then feeds 4 steps from one ds_read_b128 per lane (4 consecutive
+//    k); a k-major operand ([k][x], stored K x M or K x N) feeds each step
+//    from one ds_read_b32 (row 8g + 4h + t, 32 consecutive x per half-wave).
+//    No operand is ever transposed.  The next group's operands are read
+//    before the current group's MFMAs are issued.
+//  * Direct path (16-byte aligned operands whose byte extent fits 32-bit
+//    offsets): slabs move global -> LDS with buffer_load_dwordx4 ... lds, so
+//    the data never passes through registers and advancing a slab costs one
+//    scalar offset.  Each such instruction writes 1 KB of LDS in lane order;
+//    which global 16-byte chunk a lane fetches is chosen so that the chunks
+//    land XOR-swizzled (x-major rows: chunk c of row r at slot
+//    c ^ ((r ^ r/8) mod 8); k-major rows: c ^ 8 on every other group of 4
+//    rows), which keeps the fragment reads free of bank conflicts without
+//    padding.  Reads past the end of an operand return zero (range-checked
+//    buffer), and k past K is zeroed by the lane that fetched it once its
+//    load has landed, before the barrier that publishes the slab.
+//  * Staged path (any other operand): slabs move global -> registers -> LDS
+//    with loads clamped into the matrix, into padded rows (BK + 4 words
+//    x-major, tile width + 8 k-major) that are free of bank conflicts; k past
+//    K is zeroed on the way in.  16-byte loads are a compile-time
+//    specialisation taken when pointers, leading dimensions and the
+//    contiguous extent are multiples of 4 floats; otherwise scalar loads.
+//  * Edges: rows and columns past M or N are fetched clamped into the matrix
+//    and their results are never stored.
 //  * Tile order: workgroups are handed to the 8 XCDs round-robin, so the grid
 //    index is remapped to give each XCD a contiguous run of tiles, ordered in
 //    groups of 4 tile rows so that a run shares A row panels and B column
 //    panels in that XCD's L2.
 //  * Every output cell is one fixed sequence of MFMA accumulations over k,
-//    independent of timing, so results are reproducible bit for bit.
+//    independent of timing and of the path taken, so results are
+//    reproducible bit for bit.
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
@@ -52,6 +62,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int THREADS = 256;
 constexpr int GROUP_M = 4;         // tile rows per ordering group
+
+// ---------------------------------------------------------------------------
+// Staged path.
 
 // LDS words per row of an operand tile of TX values of x by BK values of k:
 // x-major rows hold BK words plus 4 of padding (16 consecutive rows then
@@ -269,6 +282,218 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_kernel(
         }
 }
 
+// ---------------------------------------------------------------------------
+// Direct path.
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// chunk slot of x-major row r (8 chunks of 16 B per row of BK = 32 floats)
+__device__ __forceinline__ int xswz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// One operand's k-slab (TX values of x by 32 of k) as NI buffer loads per
+// wave; instruction j of wave w fills the 1 KB block 4j + w of the stage.
+//   XMAJOR: element (x, k) at P[x*ld + k]; the stage holds TX rows of 128 B.
+//   else  : element (x, k) at P[k*ld + x]; the stage holds 32 rows of TX*4 B.
+template <int TX, bool XMAJOR>
+struct DirectOperand {
+    static constexpr int BK = 32;
+    static constexpr int STAGE = TX * BK * 4;     // bytes per stage
+    static constexpr int NI = STAGE / 1024 / 4;   // loads per wave per slab
+    static_assert(NI >= 1, "tile too small");
+    unsigned voff[NI];   // byte offset of this lane's chunk at k = 0
+    int kof[NI];         // k of this lane's chunk (x-major) or row (k-major) in the slab
+
+    __device__ __forceinline__ void init(int64_t ld, int x0, int X, int lane, int wave) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int blk = 4 * j + wave;
+            if (XMAJOR) {
+                const int row = 8 * blk + lane / 8;
+                const int c = (lane % 8) ^ xswz(row);
+                voff[j] = (unsigned)(((int64_t)min(x0 + row, X - 1) * ld + 4 * c) * 4);
+                kof[j] = 4 * c;
+            } else {
+                constexpr int CPR = TX / 4;       // chunks per row
+                constexpr int RPB = 64 / CPR;     // rows per 1 KB block
+                const int row = RPB * blk + lane / CPR;
+                const int c = (lane % CPR) ^ (8 * ((row >> 2) & 1));
+                voff[j] = (unsigned)(((int64_t)row * ld + min(x0 + 4 * c, X - 4)) * 4);
+                kof[j] = row;
+            }
+        }
+    }
+    // bytes from P to the end of the operand's last element
+    static __device__ __forceinline__ int extent(int64_t ld, int X, int K) {
+        return (int)(XMAJOR ? ((int64_t)(X - 1) * ld + K) * 4 : ((int64_t)(K - 1) * ld + X) * 4);
+    }
+    __device__ __forceinline__ void issue(char *stage, const float *P, int ext, int64_t ld, int k0,
+                                          int wave) const {
+        // The buffer builtins exist only in the device compilation.
+#if defined(__HIP_DEVICE_COMPILE__)
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void *)P, (short)0, ext, 0x00020000);
+        const unsigned so = (unsigned)((XMAJOR ? (int64_t)k0 : k0 * ld) * 4);
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (lds_void *)(stage + (4 * j + wave) * 1024), 16, voff[j], so, 0, 0);
+#endif
+    }
+    // after this wave's loads of the slab at k0 have landed: zero what lies at k >= K
+    __device__ __forceinline__ void zero_tail(char *stage, int k0, int K, int wave, int lane) const {
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            if (k0 + kof[j] >= K)
+                *reinterpret_cast<v4f *>(stage + (4 * j + wave) * 1024 + lane * 16) =
+                    v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    // byte offset, within a stage, of lane (l32, h)'s operand of k-group g
+    // for the 32-block at x = xb
+    static __device__ __forceinline__ int frag_offset(int xb, int l32, int h, int g) {
+        if (XMAJOR) {
+            const int r = xb + l32;
+            return r * 128 + (((2 * g + h) ^ xswz(r)) * 16);
+        }
+        const int x = xb + l32;
+        return (8 * g + 4 * h) * TX * 4 + (((x >> 2) ^ (8 * h)) * 16) + (x & 3) * 4;
+    }
+    static __device__ __forceinline__ v4f frag(const char *stage, int off) {
+        if (XMAJOR) return *reinterpret_cast<const v4f *>(stage + off);
+        const float *p = reinterpret_cast<const float *>(stage + off);
+        return v4f{p[0], p[TX], p[2 * TX], p[3 * TX]};
+    }
+};
+
+template <int BM, int BN, bool AX, bool BX>
+__global__ __launch_bounds__(THREADS) void gemm_f32_direct(
+    int M, int N, int K, const float *__restrict__ A, int64_t lda,
+    const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
+    int tiles_m, int tiles_n) {
+    constexpr int BK = 32;
+    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int IB = WM / 32, JB = WN / 32;
+    using OA = DirectOperand<BM, AX>;
+    using OB = DirectOperand<BN, BX>;
+    constexpr int STAGE = OA::STAGE + OB::STAGE;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, l32 = lane & 31;
+    int tm, tn;
+    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
+
+    OA oa;
+    OB ob;
+    oa.init(lda, m0, M, lane, wave);
+    ob.init(ldb, n0, N, lane, wave);
+    const int exta = OA::extent(lda, M, K), extb = OB::extent(ldb, N, K);
+    auto stage_a = [&](int b) { return smem + b * STAGE; };
+    auto stage_b = [&](int b) { return smem + b * STAGE + OA::STAGE; };
+    int aoff[IB][4], boff[JB][4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+        for (int i = 0; i < IB; ++i) aoff[i][g] = OA::frag_offset(wm + 32 * i, l32, h, g);
+#pragma unroll
+        for (int j = 0; j < JB; ++j) boff[j][g] = OB::frag_offset(wn + 32 * j, l32, h, g);
+    }
+
+    v16f acc[IB][JB];
+#pragma unroll
+    for (int i = 0; i < IB; ++i)
+#pragma unroll
+        for (int j = 0; j < JB; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int nk = (K + BK - 1) / BK;
+    if (nk > 0) {
+        oa.issue(stage_a(0), A, exta, lda, 0, wave);
+        ob.issue(stage_b(0), B, extb, ldb, 0, wave);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (BK > K) {
+            oa.zero_tail(stage_a(0), 0, K, wave, lane);
+            ob.zero_tail(stage_b(0), 0, K, wave, lane);
+        }
+        __syncthreads();
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        const int k1 = (kt + 1) * BK;
+        const bool more = kt + 1 < nk;
+        // slab kt+1 goes to the stage last read in slab kt-1, whose reads
+        // all finished before the previous barrier
+        if (more) {
+            oa.issue(stage_a(buf ^ 1), A, exta, lda, k1, wave);
+            ob.issue(stage_b(buf ^ 1), B, extb, ldb, k1, wave);
+        }
+        const char *as = stage_a(buf), *bs = stage_b(buf);
+        v4f fa[IB], fb[JB];
+#pragma unroll
+        for (int i = 0; i < IB; ++i) fa[i] = OA::frag(as, aoff[i][0]);
+#pragma unroll
+        for (int j = 0; j < JB; ++j) fb[j] = OB::frag(bs, boff[j][0]);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            v4f na[IB], nb[JB];
+#pragma unroll
+            for (int i = 0; i < IB; ++i) na[i] = g + 1 < 4 ? OA::frag(as, aoff[i][g + 1]) : fa[i];
+#pragma unroll
+            for (int j = 0; j < JB; ++j) nb[j] = g + 1 < 4 ? OB::frag(bs, boff[j][g + 1]) : fb[j];
+            // keep the next group's LDS reads ahead of this group's MFMAs
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < IB; ++i)
+#pragma unroll
+                    for (int j = 0; j < JB; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][t], fb[j][t],
+                                                                        acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < IB; ++i) fa[i] = na[i];
+#pragma unroll
+            for (int j = 0; j < JB; ++j) fb[j] = nb[j];
+        }
+        if (more) {
+            // the loads into LDS are tracked by vmcnt; the compiler does not
+            // wait for them, so wait here before publishing the slab
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (k1 + BK > K) {
+                oa.zero_tail(stage_a(buf ^ 1), k1, K, wave, lane);
+                ob.zero_tail(stage_b(buf ^ 1), k1, K, wave, lane);
+            }
+            __syncthreads();
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < IB; ++i)
+#pragma unroll
+        for (int j = 0; j < JB; ++j) {
+            const int col = n0 + wn + 32 * j + l32;
+            if (col >= N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (row < M) C[(int64_t)row * ldc + col] = acc[i][j][r];
+            }
+        }
+}
+
+template <bool AX, bool BX, int BM, int BN>
+hipError_t launch_direct(int M, int N, int K, const float *A, int64_t lda, const float *B,
+                         int64_t ldb, float *C, int64_t ldc, hipStream_t s) {
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    hipLaunchKernelGGL((gemm_f32_direct<BM, BN, AX, BX>), dim3(tiles_m * tiles_n),
+                       dim3(THREADS), 0, s, M, N, K, A, lda, B, ldb, C, ldc, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
 constexpr int PROD_BK = 32;
 
 template <bool AX, bool BX, int VA, int VB, int BM = 128, int BN = 128, int BK = PROD_BK,
@@ -297,15 +522,25 @@ hipError_t launch_gemm(GemmLayout layout, int M, int N, int K, const float *A, i
     const int b_contig = bx ? K : N;
     const bool va = aligned16(A) && (lda % 4 == 0) && (a_contig % 4 == 0);
     const bool vb = aligned16(B) && (ldb % 4 == 0) && (b_contig % 4 == 0);
+    // The direct path addresses each operand with 32-bit byte offsets.
+    auto extent = [](bool xmajor, int X, int64_t ld, int K) {
+        return xmajor ? ((int64_t)(X - 1) * ld + K) * 4 : ((int64_t)(K - 1) * ld + X) * 4;
+    };
+    const bool direct = va && vb && K > 0 && extent(ax, M, lda, K) < (int64_t(1) << 31) &&
+                        extent(bx, N, ldb, K) < (int64_t(1) << 31);
     // Tile shape: 128 x 64 when that grid still gives every CU two tiles to
-    // interleave; otherwise 64 x 64, four times the tiles of 128 x 128, which
-    // keeps small and K-heavy products (few output tiles) spread over the CUs.
+    // interleave; otherwise 64 x 64, which keeps small and K-heavy products
+    // (few output tiles) spread over the CUs.
     const int64_t tiles_128x64 = (int64_t)((M + 127) / 128) * ((N + 63) / 64);
     const bool big = tiles_128x64 >= 2 * (int64_t)num_cus;
+#define GG_GEMM_DIRECT(AX_, BX_)                                                         \
+    return big ? launch_direct<AX_, BX_, 128, 64>(M, N, K, A, lda, B, ldb, C, ldc, s) \
+               : launch_direct<AX_, BX_, 64, 64>(M, N, K, A, lda, B, ldb, C, ldc, s);
 #define GG_GEMM_SHAPE(AX_, BX_, VA_, VB_)                                                   \
     return big ? launch_t<AX_, BX_, VA_, VB_, 128, 64>(M, N, K, A, lda, B, ldb, C, ldc, s) \
                : launch_t<AX_, BX_, VA_, VB_, 64, 64>(M, N, K, A, lda, B, ldb, C, ldc, s);
 #define GG_GEMM_CASE(AX_, BX_)                      \
+    if (direct) { GG_GEMM_DIRECT(AX_, BX_) }        \
     if (va && vb) { GG_GEMM_SHAPE(AX_, BX_, 4, 4) } \
     if (va) { GG_GEMM_SHAPE(AX_, BX_, 4, 1) }       \
     if (vb) { GG_GEMM_SHAPE(AX_, BX_, 1, 4) }       \
@@ -317,6 +552,7 @@ hipError_t launch_gemm(GemmLayout layout, int M, int N, int K, const float *A, i
     }
 #undef GG_GEMM_CASE
 #undef GG_GEMM_SHAPE
+#undef GG_GEMM_DIRECT
     return hipErrorInvalidValue;
 }
 

@@ -82,6 +82,43 @@ def test_odd_shapes(layout, M, N, K):
     assert_close(C, ref, bound, "%s %dx%dx%d" % (layout, M, N, K))
 
 
+# Operands whose base, leading dimension and contiguous extent are multiples
+# of 4 floats take the global -> LDS direct path: K tails of 4..28 columns,
+# M and N edges, the 64 x 64 and the 128 x 64 grids (2048 x 2048 gives every
+# CU two 128 x 64 tiles).
+DIRECT_SHAPES = [(4, 4, 4), (132, 68, 36), (260, 196, 100), (68, 1028, 60), (1028, 132, 292),
+                 (8, 2052, 4), (2048, 2048, 100)]
+
+
+@pytest.mark.parametrize("layout", sorted(LAYOUTS))
+@pytest.mark.parametrize("M,N,K", DIRECT_SHAPES)
+def test_direct_path_integer_bitwise(layout, M, N, K):
+    A, B = _operands(layout, M, N, K, lambda s: inputs.integers(RNG, s))
+    C = _run(layout, A, B)
+    ref, _ = LAYOUTS[layout][1](A, B)
+    assert np.array_equal(C.astype(np.float64), ref), "%s %dx%dx%d" % (layout, M, N, K)
+
+
+@pytest.mark.parametrize("layout", sorted(LAYOUTS))
+def test_direct_path_padded_leading_dims(layout):
+    # aligned column slices of wider buffers: ld > row width, 16-byte aligned
+    M, N, K = 196, 132, 68
+    A, B = _operands(layout, M, N, K, lambda s: inputs.uniform(RNG, s))
+    Aw = np.full((A.shape[0], A.shape[1] + 12), np.float32(3e30))
+    Aw[:, 4:4 + A.shape[1]] = A
+    Bw = np.full((B.shape[0], B.shape[1] + 8), np.float32(-3e30))
+    Bw[:, 8:8 + B.shape[1]] = B
+    dA, dB = dev(Aw)[:, 4:4 + A.shape[1]], dev(Bw)[:, 8:8 + B.shape[1]]
+    buf, _ = guarded(M, N + 4)
+    Cw = buf[64:64 + M * (N + 4)].view(M, N + 4)
+    C = Cw[:, :N]
+    LAYOUTS[layout][0](dA, dB, C=C)
+    ref, bound = LAYOUTS[layout][1](A, B)
+    assert_close(host(C), ref, bound, layout + " aligned padded")
+    assert np.all(host(Cw)[:, N:] == np.float32(1.2345e9)), "wrote outside C's columns"
+    assert canaries_intact(buf), "wrote outside C"
+
+
 def test_small_square_config():
     # 256^3, A then B uniform [-1, 1) from seed 0
     A, B = inputs.small_square(0)
