@@ -23,9 +23,10 @@ average launch duration, runs of back-to-back launches of that kernel alone
 Output: one JSON line.  `value` is the GEMM's TFLOP/s (2 * 2048^3 flops per
 launch over its average launch duration); the 2-bit GEMV's weight GB/s
 (codes + scales per call over its average duration) is in `q2_gemv`.  Both
-carry a roofline object.  Before any number is printed the outputs are
-checked against the CPU oracle on sampled cells; a failing kernel reports no
-speed.  `cpu_baseline` times the oracle itself on a bounded sample.
+carry a roofline object.  `q2_gemv_batched` times the same tokens with each
+token's 40 products in one gemv_q2_batched launch.  Before any number is
+printed the outputs are checked against the CPU oracle on sampled cells; a
+failing kernel reports no speed.  `cpu_baseline` times the oracle itself on a bounded sample.
 """
 from __future__ import annotations
 
@@ -180,12 +181,16 @@ def write_traffic(fetch_db, write_db):
     f_scale = nbytes / (fetch[ck] * 1024.0)
     w_scale = nbytes / (write[ck] * 1024.0)
     out = []
-    for key, fname, srcs, alg in (
-            ("gemm_f32_kernel", "traffic_gemm_f32_2048.json", ("gemm_f32.hip",),
-             3 * 4 * GEMM_N * GEMM_N),
-            ("gemv_q2_kernel", "traffic_gemv_q2_12288x1536.json", ("gemv_q2.hip", "wave.hpp"),
-             Q2_ALG_BYTES)):
-        k = [n for n in fetch if n.startswith(key)]
+    q2_srcs = ("gemv_q2.hip", "wave.hpp")
+    for match, fname, srcs, alg in (
+            (lambda n: n.startswith("gemm_f32_direct<128, 64, true, false>"),
+             "traffic_gemm_f32_2048.json", ("gemm_f32.hip",), 3 * 4 * GEMM_N * GEMM_N),
+            (lambda n: n.startswith("gemv_q2_kernel") and n.endswith(", 1>"),
+             "traffic_gemv_q2_12288x1536.json", q2_srcs, Q2_ALG_BYTES),
+            (lambda n: n.startswith("gemv_q2_kernel") and n.endswith(", 64>"),
+             "traffic_gemv_q2_batched_12288x1536.json", q2_srcs,
+             CALLS_PER_TOKEN * Q2_ALG_BYTES)):
+        k = [n for n in fetch if match(n)]
         if not k:
             continue
         k = k[0]
@@ -283,8 +288,17 @@ def main():
     gemm_ok, gemm_worst, _ = oracle.check(C[rows, cols], ref, bound)
     yref, ybound = oracle.gemv_q2(Q0, S0, x)
     q2_ok, q2_worst, _ = oracle.check(y, yref, ybound)
-    log("parity: gemm worst %.3g, q2 worst %.3g (x 1e-4 bound)" %
-        (gemm_worst / 1e-4, q2_worst / 1e-4))
+    # the batched entry point on token 0's 40 products, checked on 3 of them
+    dys = [torch.empty(Q2_M, dtype=torch.float32, device=dev) for _ in range(CALLS_PER_TOKEN)]
+    bd.gemv_q2_batched(Qd[:CALLS_PER_TOKEN], Sd[:CALLS_PER_TOKEN], [dx] * CALLS_PER_TOKEN, ys=dys)
+    qb_ok, qb_worst = True, 0.0
+    for b in (0, 17, CALLS_PER_TOKEN - 1):
+        Qb, Sb = inputs.q2_weight(b)
+        rb, bb = oracle.gemv_q2(Qb, Sb, x)
+        ok, worst, _ = oracle.check(dys[b].cpu().numpy(), rb, bb)
+        qb_ok, qb_worst = qb_ok and ok, max(qb_worst, worst)
+    log("parity: gemm worst %.3g, q2 worst %.3g, q2 batched worst %.3g (x 1e-4 bound)" %
+        (gemm_worst / 1e-4, q2_worst / 1e-4, qb_worst / 1e-4))
 
     if args.copy_calibration > 0:
         n = args.copy_calibration // 4
@@ -323,8 +337,14 @@ def main():
             fn()
         return g
 
+    def token_batched(t):
+        idx = [(t * CALLS_PER_TOKEN + c) % Q2_ROTATION for c in range(CALLS_PER_TOKEN)]
+        bd.gemv_q2_batched([Qd[i] for i in idx], [Sd[i] for i in idx],
+                           [dx] * CALLS_PER_TOKEN, ys=dys)
+
     step_graphs = [capture(lambda t=t: (bd.gemm_f32(dA, dB, C=dC), token(t)))
                    for t in range(n_tok)]
+    btok_graphs = [capture(lambda t=t: token_batched(t)) for t in range(n_tok)]
     tok_graphs = [capture(lambda t=t: token(t)) for t in range(n_tok)]
     gemm_graph = capture(lambda: [bd.gemm_f32(dA, dB, C=dC)
                                   for _ in range(gemms_per_replay)])
@@ -372,9 +392,20 @@ def main():
             tok_graphs[s % n_tok].replay()
         return args.steps * CALLS_PER_TOKEN
 
+    def run_btokens(i):
+        if i is not None:
+            btok_graphs[i % n_tok].replay()
+            return 1
+        for s in range(args.steps):
+            btok_graphs[s % n_tok].replay()
+        return args.steps * CALLS_PER_TOKEN
+
     total_ms, _, t_wall = timed(run_steps, args.warmup)
     gemm_ms, n_gemm, _ = timed(run_gemms, max(1, args.warmup // gemms_per_replay))
     tok_ms, n_q2, _ = timed(run_tokens, args.warmup)
+    btok_ms, n_qb, _ = timed(run_btokens, args.warmup)
+    qb_us = 1e3 * btok_ms / n_qb
+    qb_alg_gbs = Q2_ALG_BYTES / qb_us / 1e3
     gemm_us = 1e3 * gemm_ms / n_gemm
     q2_us = 1e3 * tok_ms / n_q2
 
@@ -385,6 +416,8 @@ def main():
     gemm_traffic = traffic_from_profile("traffic_gemm_f32_2048.json",
                                         src_sha("gemm_f32.hip"))
     q2_traffic = traffic_from_profile("traffic_gemv_q2_12288x1536.json",
+                                      src_sha("gemv_q2.hip", "wave.hpp"))
+    qb_traffic = traffic_from_profile("traffic_gemv_q2_batched_12288x1536.json",
                                       src_sha("gemv_q2.hip", "wave.hpp"))
 
     cpu = None
@@ -445,8 +478,28 @@ def main():
                 "traffic": q2_traffic,
             },
         },
+        "q2_gemv_batched": {
+            "metric": ("2-bit GEMV effective weight-streaming GB/s at 12288x1536, one "
+                       "token's 40 products in one gemv_q2_batched launch (cold rotation)"),
+            "value": Q2_WEIGHT_BYTES / qb_us / 1e3 if qb_ok else None,
+            "unit": "GB/s",
+            "us_per_gemv": qb_us,
+            "us_per_token": qb_us * CALLS_PER_TOKEN,
+            "roofline": {
+                "kernel": "gemv_q2_batched (40 x 12288x1536 per launch)",
+                "bound": "hbm",
+                "achieved": qb_alg_gbs,
+                "peak": PEAK_HBM_GBS,
+                "unit": "GB/s",
+                "frac": qb_alg_gbs / PEAK_HBM_GBS,
+                "traffic": (qb_traffic / CALLS_PER_TOKEN) if qb_traffic else None,
+                "traffic_note": "HBM bytes per product (launch total / 40)",
+            },
+        },
         "parity": {"gemm_f32_2048": "pass" if gemm_ok else "FAIL",
                    "gemv_q2": "pass" if q2_ok else "FAIL",
+                   "gemv_q2_batched": "pass" if qb_ok else "FAIL",
+                   "q2_batched_worst_err_over_bound": qb_worst,
                    "gemm_worst_err_over_bound": gemm_worst,
                    "q2_worst_err_over_bound": q2_worst},
         "cpu_baseline": cpu,
@@ -456,7 +509,7 @@ def main():
         "wall_s_timed": t_wall,
     }
     print(json.dumps(out), flush=True)
-    return 0 if (gemm_ok and q2_ok) else 1
+    return 0 if (gemm_ok and q2_ok and qb_ok) else 1
 
 
 if __name__ == "__main__":
