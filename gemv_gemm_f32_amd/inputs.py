@@ -156,5 +156,20 @@ def q2_weight(r: int, M: int = GEMV_M, K: int = GEMV_K):
     return Q, S
 
 
+def q4_weight(r: int, M: int = GEMV_M, K: int = GEMV_K):
+    """Rotation matrix r of the 4-bit set: (Q, S), drawn like the 2-bit set.
+
+    Q: uint8 M x ceil(K/2), i.i.d. uniform random bytes (every 4-bit code
+       equally likely).
+    S: uint16 M x ceil(K/64), binary16 bit patterns of scales drawn uniform
+       in [0.01, 0.05) and rounded to binary16.
+    """
+    rng = np.random.default_rng(6000 + r)
+    Q = rng.integers(0, 256, size=(M, (K + 1) // 2), dtype=np.uint8)
+    S = rng.uniform(0.01, 0.05, size=(M, (K + Q2_GROUP - 1) // Q2_GROUP))
+    S = S.astype(np.float16).view(np.uint16)
+    return Q, S
+
+
 def q2_x(K: int = GEMV_K) -> np.ndarray:
     return normal(np.random.default_rng(5999), (K,))

@@ -1,4 +1,5 @@
-"""CPU oracle for the dense fp32 product, the fp32 GEMV and the 2-bit GEMV.
+"""CPU oracle for the dense fp32 product, the fp32 GEMV and the 2-bit and
+4-bit GEMVs.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  The product path
@@ -22,6 +23,11 @@ Definitions followed (the pages):
     12,288 x 1,536 matrix of 2-bit weights times a vector of 1,536 inputs, the
     2-bit fields unpacked to floating point; bit order, code map and scale
     layout are readings (see ``oracle.c``).
+  * The 4-bit matrices of the same page's patch set (kernels 0099 and 0105)
+    and the packed NF4 path of "More Stumbling, This Time in the Browser":
+    4-bit weights with no format given; the reading (nibbles least
+    significant first, w = (code - 7.5) * s, one binary16 scale per 64
+    columns) is in ``oracle.c``.
 """
 from __future__ import annotations
 
@@ -79,6 +85,10 @@ def bind(lib):
     lib.oracle_q2_unpack_row.restype = None
     lib.oracle_gemv_q2.argtypes = [i64, i64, vp, i64, vp, i64, vp, vp, vp, vp]
     lib.oracle_gemv_q2.restype = None
+    lib.oracle_q4_unpack_row.argtypes = [i64, i64, vp, i64, vp, i64, vp]
+    lib.oracle_q4_unpack_row.restype = None
+    lib.oracle_gemv_q4.argtypes = [i64, i64, vp, i64, vp, i64, vp, vp, vp, vp]
+    lib.oracle_gemv_q4.restype = None
     return lib
 
 
@@ -219,6 +229,48 @@ def gemv_q2(Q, S, x, K=None):
     b = np.zeros(M, np.float64)
     w = np.zeros(max(K, 1), np.float64)
     lib.oracle_gemv_q2(M, K, _ptr(Q), ldq, _ptr(S), lds, _ptr(x),
+                       _ptr(y), _ptr(b), _ptr(w))
+    return y, b
+
+
+def _q4_args(Q, S, K):
+    Q, ldq = _as2d(Q, np.uint8)
+    S, lds = _as2d(S, np.uint16)
+    M = Q.shape[0]
+    if S.shape[0] != M:
+        raise ValueError("Q and S must have the same number of rows")
+    if ldq < (K + 1) // 2 or Q.shape[1] < (K + 1) // 2:
+        raise ValueError("Q rows hold fewer than ceil(K/2) bytes")
+    if lds < (K + 63) // 64 or S.shape[1] < (K + 63) // 64:
+        raise ValueError("S rows hold fewer than ceil(K/64) scales")
+    return Q, ldq, S, lds, M
+
+
+def q4_unpack(Q, S, K):
+    """The dequantised 4-bit matrix (M x K, fp64): w = (code - 7.5) * s."""
+    lib = _load()
+    Q, ldq, S, lds, M = _q4_args(Q, S, K)
+    W = np.zeros((M, K), np.float64)
+    for i in range(M):
+        lib.oracle_q4_unpack_row(i, K, _ptr(Q), ldq, _ptr(S), lds,
+                                 _ptr(W[i]))
+    return W
+
+
+def gemv_q4(Q, S, x, K=None):
+    """y = W.x for the 4-bit matrix (Q codes uint8 M x ceil(K/2),
+    S binary16 bit patterns uint16 M x ceil(K/64), x fp32 (K,))."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if K is None:
+        K = x.shape[0]
+    if x.shape != (K,):
+        raise ValueError("x must have K entries")
+    Q, ldq, S, lds, M = _q4_args(Q, S, K)
+    y = np.zeros(M, np.float64)
+    b = np.zeros(M, np.float64)
+    w = np.zeros(max(K, 1), np.float64)
+    lib.oracle_gemv_q4(M, K, _ptr(Q), ldq, _ptr(S), lds, _ptr(x),
                        _ptr(y), _ptr(b), _ptr(w))
     return y, b
 

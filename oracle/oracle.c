@@ -1,6 +1,7 @@
 /*
  * oracle.c -- plain CPU oracle for the dense fp32 matrix product, its
- * one-row case, and the 2-bit packed-weight matrix-vector product.
+ * one-row case, and the 2-bit and 4-bit packed-weight matrix-vector
+ * products.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
  * load this file: only the tests, the smoke check and the benchmark's CPU
@@ -32,6 +33,14 @@
  *    in bits 2t..2t+1 of byte q (least significant first), the weight is
  *    (code - 1.5) * s, and s is the IEEE binary16 scale of columns
  *    [64g, 64g+64) stored at S[i*lds + g].
+ *  - "Kernel 0112", sections "What is being measured" (two of the kernels
+ *    patched beside it, 0099 and 0105, are 4-bit) and "More Stumbling, This
+ *    Time in the Browser" (a packed NF4 path): 4-bit weight matrices also sit
+ *    on this path, with no format given.  The reading taken for them follows
+ *    the 2-bit one: column 2q+t of a row sits in bits 4t..4t+3 of byte q
+ *    (least significant first), the weight is (code - 7.5) * s (16 levels
+ *    symmetric about zero), and s is the binary16 scale of columns
+ *    [64g, 64g+64) at S[i*lds + g].
  *
  * Pins: every function here is checked against something other than itself in
  * tests/test_oracle.py (hand-worked cases, numpy's float64 product, exact
@@ -192,6 +201,43 @@ void oracle_gemv_q2(int64_t M, int64_t K, const uint8_t *Q, int64_t ldq,
 {
     for (int64_t i = 0; i < M; ++i) {
         oracle_q2_unpack_row(i, K, Q, ldq, S, lds, w);
+        double s = 0.0, t = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double p = w[k] * (double)x[k];
+            s += p;
+            t += fabs(p);
+        }
+        y[i] = s;
+        bound[i] = t;
+    }
+}
+
+/* --------------------------------------------------------- 4-bit gemv -- */
+
+/* Unpack row i of a 4-bit matrix into fp64 weights w[0..K).
+ *   byte  = Q[i*ldq + k/2]
+ *   code  = (byte >> 4*(k%2)) & 15
+ *   s     = binary16 S[i*lds + k/64]
+ *   w[k]  = (code - 7.5) * s                                             */
+void oracle_q4_unpack_row(int64_t i, int64_t K, const uint8_t *Q, int64_t ldq,
+                          const uint16_t *S, int64_t lds, double *w)
+{
+    for (int64_t k = 0; k < K; ++k) {
+        unsigned byte = Q[i * ldq + k / 2];
+        unsigned code = (byte >> (4 * (k % 2))) & 15u;
+        double s = oracle_half_to_double(S[i * lds + k / 64]);
+        w[k] = ((double)code - 7.5) * s;
+    }
+}
+
+/* y = W.x for the 4-bit matrix: unpack each row whole into the caller's
+ * scratch w (K doubles), then the plain dot product. */
+void oracle_gemv_q4(int64_t M, int64_t K, const uint8_t *Q, int64_t ldq,
+                    const uint16_t *S, int64_t lds, const float *x,
+                    double *y, double *bound, double *w)
+{
+    for (int64_t i = 0; i < M; ++i) {
+        oracle_q4_unpack_row(i, K, Q, ldq, S, lds, w);
         double s = 0.0, t = 0.0;
         for (int64_t k = 0; k < K; ++k) {
             double p = w[k] * (double)x[k];

@@ -72,6 +72,18 @@ def test_q2_tiny_golden():
     assert np.array_equal(b, np.abs(W) @ np.abs(x.astype(np.float64)))
 
 
+def test_q4_tiny_golden():
+    g = load("q4_tiny_2x4.txt")
+    Q = np.array(g["Q"], dtype=np.uint8)
+    S = np.array(g["S"], dtype=np.uint16)
+    x = _f32(g["x"])[0]
+    y, b = oracle.gemv_q4(Q, S, x)
+    assert np.array_equal(y, np.asarray(g["y"], np.float64)[0])
+    W = oracle.q4_unpack(Q, S, 4)
+    assert np.array_equal(W, [[-3.75, -3.25, -0.25, 3.75], [15, 1, 9, -9]])
+    assert np.array_equal(b, np.abs(W) @ np.abs(x.astype(np.float64)))
+
+
 # ------------------------------------------------------- library routine --
 
 SHAPES = [(1, 1, 1), (1, 7, 3), (5, 1, 9), (3, 4, 2), (17, 33, 31),
@@ -285,6 +297,88 @@ def test_q2_scale_doubling():
     S2 = (S.view(np.float16) * np.float16(2)).view(np.uint16)
     y2, _ = oracle.gemv_q2(Q, S2, x)
     assert np.array_equal(y2, 2 * y)
+
+
+def _pack_nibbles(codes):
+    """Independent packer: column 2q+t in bits 4t..4t+3 of byte q."""
+    M, K = codes.shape
+    nb = (K + 1) // 2
+    padded = np.zeros((M, nb * 2), np.uint16)
+    padded[:, :K] = codes
+    q = padded.reshape(M, nb, 2)
+    return (q[..., 0] | (q[..., 1] << 4)).astype(np.uint8)
+
+
+def _dequant4_numpy(codes, S):
+    M, K = codes.shape
+    s = S.view(np.float16).astype(np.float64)
+    s_full = np.repeat(s, 64, axis=1)[:, :K]
+    return (codes.astype(np.float64) - 7.5) * s_full
+
+
+def test_q4_integer_exact():
+    # scale 2.0 and integer x: every weight is an odd integer in [-15, 15]
+    M, K = 9, 256
+    codes = RNG.integers(0, 16, (M, K))
+    Q = _pack_nibbles(codes)
+    S = np.full((M, K // 64), 0x4000, np.uint16)
+    x = inputs.integers(RNG, (K,))
+    y, _ = oracle.gemv_q4(Q, S, x)
+    ref = (2 * codes - 15) @ x.astype(np.int64)
+    assert np.array_equal(y, ref.astype(np.float64))
+
+
+@pytest.mark.parametrize("M,K", [(1, 64), (5, 1536), (7, 100), (3, 5), (4, 1)])
+def test_q4_matches_independent_packer(M, K):
+    codes = RNG.integers(0, 16, (M, K))
+    Q = _pack_nibbles(codes)
+    S = RNG.uniform(0.01, 0.05, (M, (K + 63) // 64)).astype(np.float16).view(np.uint16)
+    x = inputs.normal(RNG, (K,))
+    W = _dequant4_numpy(codes, S)
+    assert np.array_equal(oracle.q4_unpack(Q, S, K), W)
+    y, b = oracle.gemv_q4(Q, S, x)
+    np.testing.assert_allclose(y, W @ x.astype(np.float64), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(b, np.abs(W) @ np.abs(x.astype(np.float64)), rtol=1e-13)
+
+
+def test_q4_padding_is_ignored():
+    # K = 71: the last byte holds 1 live column and 1 dead one; the second
+    # scale group is partial; the row strides carry extra garbage
+    M, K = 6, 71
+    codes = RNG.integers(0, 16, (M, K))
+    Q = _pack_nibbles(codes)
+    S = RNG.uniform(0.01, 0.05, (M, 2)).astype(np.float16).view(np.uint16)
+    x = inputs.normal(RNG, (K,))
+    y, _ = oracle.gemv_q4(Q, S, x)
+    Qg = RNG.integers(0, 256, (M, Q.shape[1] + 5)).astype(np.uint8)
+    Qg[:, :Q.shape[1]] = Q
+    Qg[:, Q.shape[1] - 1] |= np.uint8(0xF0)          # dead column 71
+    Sg = RNG.integers(0, 65536, (M, 4)).astype(np.uint16)
+    Sg[:, :2] = S
+    y2, _ = oracle.gemv_q4(Qg[:, :Q.shape[1] + 5], Sg, x, K=K)
+    assert np.array_equal(y, y2)
+
+
+def test_q4_scale_doubling():
+    M, K = 4, 192
+    Q, S = inputs.q4_weight(0, M, K)
+    x = inputs.normal(RNG, (K,))
+    y, _ = oracle.gemv_q4(Q, S, x)
+    S2 = (S.view(np.float16) * np.float16(2)).view(np.uint16)
+    y2, _ = oracle.gemv_q4(Q, S2, x)
+    assert np.array_equal(y2, 2 * y)
+
+
+def test_q4_agrees_with_q2_on_shared_levels():
+    # codes 6..9 of the 4-bit format are the levels -1.5..1.5 of the 2-bit
+    # one: (c4 - 7.5) = (c2 - 1.5) with c4 = c2 + 6
+    M, K = 5, 130
+    c2 = RNG.integers(0, 4, (M, K))
+    S = RNG.uniform(0.01, 0.05, (M, 3)).astype(np.float16).view(np.uint16)
+    x = inputs.normal(RNG, (K,))
+    y2, b2 = oracle.gemv_q2(_pack_codes(c2), S, x)
+    y4, b4 = oracle.gemv_q4(_pack_nibbles(c2 + 6), S, x)
+    assert np.array_equal(y2, y4) and np.array_equal(b2, b4)
 
 
 # ------------------------------------------------------- acceptance test --

@@ -42,6 +42,15 @@ MUTANTS = {
     "half_subnormal": ("ldexp((double)f, -24)", "ldexp((double)f, -25)"),
     "q2_dot_drops_first": ("for (int64_t k = 0; k < K; ++k) {\n            double p = w[k]",
                            "for (int64_t k = 1; k < K; ++k) {\n            double p = w[k]"),
+    "q4_sign_flipped": ("w[k] = ((double)code - 7.5) * s;", "w[k] = (7.5 - (double)code) * s;"),
+    "q4_offset_wrong": ("w[k] = ((double)code - 7.5) * s;", "w[k] = ((double)code - 8.0) * s;"),
+    "q4_nibble_order_msb_first": ("(byte >> (4 * (k % 2))) & 15u", "(byte >> (4 - 4 * (k % 2))) & 15u"),
+    "q4_mask_three_bits": ("(byte >> (4 * (k % 2))) & 15u", "(byte >> (4 * (k % 2))) & 7u"),
+    "q4_byte_index": ("Q[i * ldq + k / 2]", "Q[i * ldq + k / 4]"),
+    "q4_scale_index": ("& 15u;\n        double s = oracle_half_to_double(S[i * lds + k / 64]);",
+                       "& 15u;\n        double s = oracle_half_to_double(S[i * lds + k / 32]);"),
+    "q4_dot_drops_last": ("oracle_q4_unpack_row(i, K, Q, ldq, S, lds, w);\n        double s = 0.0, t = 0.0;\n        for (int64_t k = 0; k < K; ++k)",
+                          "oracle_q4_unpack_row(i, K, Q, ldq, S, lds, w);\n        double s = 0.0, t = 0.0;\n        for (int64_t k = 0; k + 1 < K; ++k)"),
     "cells_trans_b_ignored": ("double b = trans_b ? (double)B[j * ldb + k] : (double)B[k * ldb + j];",
                               "double b = (double)B[k * ldb + j];"),
 }
@@ -106,6 +115,20 @@ def _battery():
     Wd = (codes - 1.5) * np.repeat(S.view(np.float16).astype(np.float64), 64, 1)[:, :K]
     y, _ = oracle.gemv_q2(_pack(codes), S, x)
     expect("q2_np", np.allclose(y, Wd @ x.astype(np.float64), rtol=0, atol=1e-12))
+
+    g = load("q4_tiny_2x4.txt")
+    y, _ = oracle.gemv_q4(np.array(g["Q"], np.uint8), np.array(g["S"], np.uint16),
+                          np.asarray(g["x"], np.float64).astype(np.float32)[0])
+    expect("q4_tiny", np.array_equal(y, np.asarray(g["y"], np.float64)[0]))
+
+    M, K = 5, 200
+    codes = rng.integers(0, 16, (M, K))
+    S = rng.uniform(0.01, 0.05, (M, 4)).astype(np.float16).view(np.uint16)
+    x = inputs.normal(rng, (K,))
+    Wd = (codes - 7.5) * np.repeat(S.view(np.float16).astype(np.float64), 64, 1)[:, :K]
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    y, _ = oracle.gemv_q4(packed, S, x)
+    expect("q4_np", np.allclose(y, Wd @ x.astype(np.float64), rtol=0, atol=1e-12))
 
     pats = np.arange(0, 65536, 97, dtype=np.uint32).astype(np.uint16)
     got = np.array([oracle.half_to_double(int(h)) for h in pats])
