@@ -27,7 +27,7 @@ GG_ERR_NO_DEVICE = -3
 GG_ERR_LAUNCH = -4
 
 ENTRY_POINTS = ("gemm_f32", "gemm_f32_tn", "gemm_f32_nt", "gemv_f32", "gemv_q2",
-                "gemv_q2_batched", "gg_strerror")
+                "gemv_q2_batched", "gemv_q4", "gemv_q4_batched", "gg_strerror")
 
 _lib = None
 
@@ -65,11 +65,14 @@ def load(path: str = LIB_PATH):
         f.restype = ctypes.c_int
     lib.gemv_f32.argtypes = [i64, i64, vp, i64, vp, vp, vp]
     lib.gemv_f32.restype = ctypes.c_int
-    lib.gemv_q2.argtypes = [i64, i64, vp, i64, vp, i64, vp, vp, vp]
-    lib.gemv_q2.restype = ctypes.c_int
     pp = ctypes.POINTER(ctypes.c_void_p)
-    lib.gemv_q2_batched.argtypes = [i64, i64, i64, pp, i64, pp, i64, pp, pp, vp]
-    lib.gemv_q2_batched.restype = ctypes.c_int
+    for name in ("gemv_q2", "gemv_q4"):
+        f = getattr(lib, name)
+        f.argtypes = [i64, i64, vp, i64, vp, i64, vp, vp, vp]
+        f.restype = ctypes.c_int
+        f = getattr(lib, name + "_batched")
+        f.argtypes = [i64, i64, i64, pp, i64, pp, i64, pp, pp, vp]
+        f.restype = ctypes.c_int
     lib.gg_strerror.argtypes = [ctypes.c_int]
     lib.gg_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -186,9 +189,7 @@ def gemv_f32(W, x, y=None, stream=None):
     return y
 
 
-def gemv_q2(Q, S, x, y=None, stream=None):
-    """y = W.x with W as 2-bit codes Q (uint8, M x >= ceil(K/4)) and binary16
-    scales S (float16 or int16 bit patterns, M x >= ceil(K/64)); x (K,) fp32."""
+def _packed(name, Q, S, x, y, stream):
     torch = _torch()
     M = Q.shape[0]
     K = x.shape[0]
@@ -204,9 +205,21 @@ def gemv_q2(Q, S, x, y=None, stream=None):
         raise ValueError("y must have M entries")
     pq, ldq = _mat(Q, torch.uint8, "Q")
     ps, lds = _mat(S, torch.float16, "S")
-    _check(load().gemv_q2(M, K, pq, ldq, ps, lds, _vec(x, torch.float32, "x"),
-                          _vec(y, torch.float32, "y"), _stream(stream)), "gemv_q2")
+    _check(getattr(load(), name)(M, K, pq, ldq, ps, lds, _vec(x, torch.float32, "x"),
+                                 _vec(y, torch.float32, "y"), _stream(stream)), name)
     return y
+
+
+def gemv_q2(Q, S, x, y=None, stream=None):
+    """y = W.x with W as 2-bit codes Q (uint8, M x >= ceil(K/4)) and binary16
+    scales S (float16 or int16 bit patterns, M x >= ceil(K/64)); x (K,) fp32."""
+    return _packed("gemv_q2", Q, S, x, y, stream)
+
+
+def gemv_q4(Q, S, x, y=None, stream=None):
+    """y = W.x with W as 4-bit codes Q (uint8, M x >= ceil(K/2)) and binary16
+    scales S (float16 or int16 bit patterns, M x >= ceil(K/64)); x (K,) fp32."""
+    return _packed("gemv_q4", Q, S, x, y, stream)
 
 
 def _ptr_array(ptrs):
@@ -216,10 +229,7 @@ def _ptr_array(ptrs):
     return arr
 
 
-def gemv_q2_batched(Qs, Ss, xs, ys=None, stream=None):
-    """y_b = W_b.x_b for every b: lists of Q (uint8 M x >= ceil(K/4)), S
-    (float16/int16 M x >= ceil(K/64)), x (K,) fp32; all Q share one shape and
-    leading dimension, as do all S.  Returns the list of outputs."""
+def _packed_batched(name, Qs, Ss, xs, ys, stream):
     torch = _torch()
     n = len(Qs)
     if len(Ss) != n or len(xs) != n:
@@ -245,7 +255,18 @@ def gemv_q2_batched(Qs, Ss, xs, ys=None, stream=None):
         sp.append(ps)
         xp.append(_vec(x, torch.float32, "x"))
         yp.append(_vec(y, torch.float32, "y"))
-    _check(load().gemv_q2_batched(n, M, K, _ptr_array(qp), ldq, _ptr_array(sp), lds,
-                                  _ptr_array(xp), _ptr_array(yp), _stream(stream)),
-           "gemv_q2_batched")
+    _check(getattr(load(), name)(n, M, K, _ptr_array(qp), ldq, _ptr_array(sp), lds,
+                                 _ptr_array(xp), _ptr_array(yp), _stream(stream)), name)
     return ys
+
+
+def gemv_q2_batched(Qs, Ss, xs, ys=None, stream=None):
+    """y_b = W_b.x_b for every b: lists of Q (uint8 M x >= ceil(K/4)), S
+    (float16/int16 M x >= ceil(K/64)), x (K,) fp32; all Q share one shape and
+    leading dimension, as do all S.  Returns the list of outputs."""
+    return _packed_batched("gemv_q2_batched", Qs, Ss, xs, ys, stream)
+
+
+def gemv_q4_batched(Qs, Ss, xs, ys=None, stream=None):
+    """As gemv_q2_batched for 4-bit codes (Q uint8 M x >= ceil(K/2))."""
+    return _packed_batched("gemv_q4_batched", Qs, Ss, xs, ys, stream)

@@ -130,14 +130,20 @@ int gemv_f32(int64_t M, int64_t K, const float *W, int64_t ldw, const float *x, 
                                              reinterpret_cast<hipStream_t>(stream)));
 }
 
-int gemv_q2_batched(int64_t count, int64_t M, int64_t K, const uint8_t *const *Q, int64_t ldq,
-                    const uint16_t *const *S, int64_t lds, const float *const *x,
-                    float *const *y, gg_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The checks and launch shared by the 2-bit and 4-bit entry points.
+int packed_batched(int bits, int64_t count, int64_t M, int64_t K, const uint8_t *const *Q,
+                   int64_t ldq, const uint16_t *const *S, int64_t lds, const float *const *x,
+                   float *const *y, gg_stream_t stream) {
     if (count < 0 || count > kMaxDim || M < 0 || K < 0 || M > kMaxDim || K > kMaxDim)
         return GG_ERR_INVALID_ARG;
     if (count == 0 || M == 0) return GG_OK;
     if (Q == nullptr || S == nullptr || x == nullptr || y == nullptr) return GG_ERR_INVALID_ARG;
-    const int64_t qcols = (K + 3) / 4, scols = (K + 63) / 64;
+    const int64_t per_byte = 8 / bits;
+    const int64_t qcols = (K + per_byte - 1) / per_byte, scols = (K + 63) / 64;
     if (K > 0 && (ldq < qcols || lds < scols || ldq > kMaxDim || lds > kMaxDim))
         return GG_ERR_INVALID_ARG;
     for (int64_t b = 0; b < count; ++b) {
@@ -173,8 +179,21 @@ int gemv_q2_batched(int64_t count, int64_t M, int64_t K, const uint8_t *const *Q
     int cus = 0;
     if (int st = check_device(&cus)) return st;
     (void)hipGetLastError();
-    return launch_status(gg::launch_gemv_q2((int)count, (int)M, (int)K, Q, ldq, S, lds, x, y,
-                                            reinterpret_cast<hipStream_t>(stream)));
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    return launch_status(bits == 2 ? gg::launch_gemv_q2((int)count, (int)M, (int)K, Q, ldq, S,
+                                                        lds, x, y, hs)
+                                   : gg::launch_gemv_q4((int)count, (int)M, (int)K, Q, ldq, S,
+                                                        lds, x, y, hs));
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemv_q2_batched(int64_t count, int64_t M, int64_t K, const uint8_t *const *Q, int64_t ldq,
+                    const uint16_t *const *S, int64_t lds, const float *const *x,
+                    float *const *y, gg_stream_t stream) {
+    return packed_batched(2, count, M, K, Q, ldq, S, lds, x, y, stream);
 }
 
 int gemv_q2(int64_t M, int64_t K, const uint8_t *Q, int64_t ldq, const uint16_t *S,
@@ -182,7 +201,20 @@ int gemv_q2(int64_t M, int64_t K, const uint8_t *Q, int64_t ldq, const uint16_t 
     if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim) return GG_ERR_INVALID_ARG;
     if (M == 0) return GG_OK;
     // one product of the batched entry point (same checks, same kernel)
-    return gemv_q2_batched(1, M, K, &Q, ldq, &S, lds, &x, &y, stream);
+    return packed_batched(2, 1, M, K, &Q, ldq, &S, lds, &x, &y, stream);
+}
+
+int gemv_q4_batched(int64_t count, int64_t M, int64_t K, const uint8_t *const *Q, int64_t ldq,
+                    const uint16_t *const *S, int64_t lds, const float *const *x,
+                    float *const *y, gg_stream_t stream) {
+    return packed_batched(4, count, M, K, Q, ldq, S, lds, x, y, stream);
+}
+
+int gemv_q4(int64_t M, int64_t K, const uint8_t *Q, int64_t ldq, const uint16_t *S,
+            int64_t lds, const float *x, float *y, gg_stream_t stream) {
+    if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim) return GG_ERR_INVALID_ARG;
+    if (M == 0) return GG_OK;
+    return packed_batched(4, 1, M, K, &Q, ldq, &S, lds, &x, &y, stream);
 }
 
 const char *gg_strerror(int status) {

@@ -1,0 +1,383 @@
+// gemv_packed.hip -- y = W.x with W as 2-bit or 4-bit codes and binary16
+// group scales.
+//
+// The 12,288 x 1,536 2-bit matrix-vector product of "Kernel 0112" (section
+// "What is being measured"): the work is dominated by streaming the packed
+// weights, the original kernel kept too few reads in flight, and splitting a
+// row's dot product over 32 threads was the change that paid (sections "What
+// is being measured" and "The four variants").  The same page patches two
+// 4-bit kernels beside it, and "More Stumbling, This Time in the Browser" has
+// a packed 4-bit path; the 4-bit product here uses the same kernel with
+// wider codes.  That page's kernel unpacked the fields with floating-point
+// floor arithmetic and reduced through shared memory with barriers (section
+// "The kernel"); this one is shaped for CDNA4:
+//
+//  * Units: a row is read in units of 16 codes -- 4 bytes of 2-bit codes or
+//    8 bytes of 4-bit codes -- and 4 units make one 64-column scale group.
+//  * Split: a row belongs to 32 lanes (half a wave64).  Lane j takes units j,
+//    j+32, j+64, ..., so each load instruction covers 128 (2-bit) or 256
+//    (4-bit) contiguous bytes of a row.  Each half-wave owns RPL consecutive
+//    rows and issues every code and scale load of a pass before consuming
+//    any, so all bytes of a call are requested up front.
+//  * x: lane j keeps the 16 x values of each of its units in registers and
+//    reuses them for all RPL rows; x is 6 KiB and read from L2/L1.
+//  * Unpack: a shift and one and-or place two codes of a 32-bit word in the
+//    top fraction bits of a binary16 pair of 1.0 (bits 8-9 for 2-bit codes,
+//    6-9 for 4-bit), i.e. h = 1 + c / 2^b exactly for b-bit codes.  The
+//    multiply-add then reads h directly as a binary16 operand of
+//    v_fma_mix_f32, with x and the accumulator in fp32, so the product h*x is
+//    formed from exact operands.  With the zero point z = (2^b - 1) / 2 of
+//    the code-to-weight map w = (c - z) * s, per unit:
+//        a = -(1 + z / 2^b) X + sum h x = sum (c - z) x / 2^b,
+//    with X = sum x over the unit's columns, precomputed once per lane.  The
+//    row sum is y = 2^b * sum over units of s * a: about two instructions per
+//    weight, and one scale multiply per 16 weights.
+//  * Rounding: |c - z| >= 1/2, so sum |w x| >= s sum|x| / 2 over a unit.  A
+//    2-bit unit's chain starts at -(1 + z/4) X and its partial sums stay
+//    within 3.2 sum|x|: the fp32 error is below 2.5e-5 sum |w x|.  A 4-bit
+//    chain starts at zero and adds -(1 + z/16) X last, which keeps its
+//    partial sums within 1.94 sum|x| (started at -(1 + z/16) X they could
+//    reach 3.4 sum|x|, and the worst case would touch the 1e-4 bound): its
+//    error is below 6.5e-5 sum |w x|.  Both hold for any inputs.
+//  * Reduction: the 32 partial sums of a row are added with DPP and
+//    ds_swizzle (wave.hpp), no LDS storage, barriers or atomics; lane 0 of the
+//    half-wave writes y.  The tree is fixed, so results repeat bit for bit.
+//  * A byte-load specialisation of the same kernel serves K not a multiple of
+//    16, or Q rows not aligned to a unit; it masks columns k >= K.
+//  * Batches: blockIdx.y picks one of up to 64 products of one shape whose
+//    pointers travel in the kernel arguments, so a token's worth of products
+//    costs one launch.
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+#include "wave.hpp"
+
+namespace gg {
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef unsigned u2 __attribute__((ext_vector_type(2)));
+
+constexpr int THREADS = 256;
+constexpr int WAVES = THREADS / 64;
+constexpr int UPL = 3;                  // units of 16 codes per lane per pass
+constexpr int UNITS_PER_PASS = 32 * UPL;
+
+// Device pointers of up to NB products of one shape, passed by value in the
+// kernel arguments (blockIdx.y selects the product).
+template <int NB>
+struct PackedPtrs {
+    const uint8_t *Q[NB];
+    const uint16_t *S[NB];
+    const float *x[NB];
+    float *y[NB];
+};
+
+// Per-width constants of the unpack.
+template <int BITS>
+struct Codes {
+    static constexpr int UW = BITS / 2;              // 32-bit words per unit
+    static constexpr int CPD = 32 / BITS;            // codes per word
+    static constexpr int HALF = CPD / 2;             // code pairs per word
+    static constexpr int TOP = 10 - BITS;            // fraction bit of the low code
+    static constexpr unsigned FIELD = (1u << BITS) - 1u;
+    static constexpr unsigned MASK = (FIELD << TOP) | (FIELD << (TOP + 16));
+    static constexpr float INIT = -(1.f + (float)FIELD / 2.f / (float)(1 << BITS));
+    static constexpr float OUT = (float)(1 << BITS);
+};
+
+// The unit of 16 codes at unit index u of a row, as UW words: the fast
+// specialisation loads it whole; the generic one assembles it from bytes,
+// zeroing columns at or beyond K.
+template <int BITS, bool FAST>
+__device__ __forceinline__ void load_unit(const uint8_t *__restrict__ Qrow, int u, int K,
+                                          unsigned (&w)[Codes<BITS>::UW]) {
+    constexpr int UW = Codes<BITS>::UW, CPB = 8 / BITS;   // codes per byte
+    if (FAST) {
+        if (UW == 1) {
+            w[0] = reinterpret_cast<const unsigned *>(Qrow)[u];
+        } else {
+            const u2 v = reinterpret_cast<const u2 *>(Qrow)[u];
+            w[0] = v.x;
+            w[UW - 1] = v.y;
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < UW; ++i) {
+        unsigned word = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int k = u * 16 + (4 * i + b) * CPB;   // first column of this byte
+            if (k < K) {
+                unsigned byte = Qrow[k / CPB];
+                const int live = K - k;                  // columns of this byte below K
+                if (live < CPB) byte &= (1u << (BITS * live)) - 1u;
+                word |= byte << (8 * b);
+            }
+        }
+        w[i] = word;
+    }
+}
+
+// RPL rows per half-wave; FAST: unit loads and 32-bit offsets; FULL (with
+// FAST): every wave's rows and every pass's units exist, so no index is
+// clamped; NB: number of products the pointer block holds (blockIdx.y picks
+// one).
+template <int BITS, int RPL, bool FAST, bool FULL, int NB>
+__global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int64_t ldq,
+                                                              int64_t lds, PackedPtrs<NB> ptrs) {
+    using C = Codes<BITS>;
+    constexpr int UW = C::UW, UB = 4 * UW;         // words, bytes per unit
+    const int b = NB == 1 ? 0 : (int)blockIdx.y;
+    const uint8_t *__restrict__ Q = ptrs.Q[b];
+    const uint16_t *__restrict__ S = ptrs.S[b];
+    const float *__restrict__ x = ptrs.x[b];
+    float *__restrict__ y = ptrs.y[b];
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 31;
+    const int wave = blockIdx.x * WAVES + (threadIdx.x >> 6);
+    const int row0 = wave * (2 * RPL) + (lane >> 5) * RPL;
+    if (wave * (2 * RPL) >= M) return;    // uniform per wave
+
+    const int units = (K + 15) >> 4;      // units of 16 codes per row
+    const int row_last = M - 1;
+    float acc[RPL];
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) acc[m] = 0.f;
+
+    // Mask of the two code slots, and the binary16 pair (1.0, 1.0).  The
+    // empty asm pins both in VGPRs, so (sh & mask) | one is selected as one
+    // v_and_or_b32: gfx9 VOP3 forms take no literal operand, and with the
+    // constants left visible the compiler splits it into an AND and an OR.
+    unsigned mask = C::MASK, one = 0x3C003C00u;
+    asm volatile("" : "+v"(mask));
+    asm volatile("" : "+v"(one));
+
+    for (int u0 = 0; u0 < units; u0 += UNITS_PER_PASS) {
+        // ---- Loads.  Every load of a pass is issued first, unconditionally,
+        // from clamped (always in-bounds) addresses: x, then codes and scales
+        // row by row, so that the rows can be consumed in the order their
+        // data arrives.  Predicated loads, or selects right after each load,
+        // make the compiler wait for each load before issuing the next.  The
+        // fast path addresses with 32-bit byte offsets from the base pointer.
+        v4f xraw[UPL][4];
+        unsigned craw[RPL][UPL][UW];
+        unsigned sraw[RPL][UPL];          // binary16 bits, zero-extended
+        if (FULL) {
+            // Every row and unit of this wave exists: one per-lane base and
+            // compile-time offsets (row m adds m*ldq, unit q adds 32q units).
+            const char *xb = reinterpret_cast<const char *>(x) + (unsigned)(u0 + j) * 64u;
+            const unsigned qb = (unsigned)row0 * (unsigned)ldq + (unsigned)(u0 + j) * UB;
+            const unsigned sb = ((unsigned)row0 * (unsigned)lds + (unsigned)((u0 + j) >> 2)) * 2u;
+#pragma unroll
+            for (int q = 0; q < UPL; ++q)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    xraw[q][c] = *reinterpret_cast<const v4f *>(xb + 2048 * q + 16 * c);
+#pragma unroll
+            for (int m = 0; m < RPL; ++m)
+#pragma unroll
+                for (int q = 0; q < UPL; ++q) {
+                    const char *qp = reinterpret_cast<const char *>(Q) + qb +
+                                     (unsigned)m * (unsigned)ldq + 32u * UB * q;
+                    if (UW == 1) {
+                        craw[m][q][0] = *reinterpret_cast<const unsigned *>(qp);
+                    } else {
+                        const u2 v = *reinterpret_cast<const u2 *>(qp);
+                        craw[m][q][0] = v.x;
+                        craw[m][q][UW - 1] = v.y;
+                    }
+                    sraw[m][q] = *reinterpret_cast<const uint16_t *>(
+                        reinterpret_cast<const char *>(S) + sb + (unsigned)m * (unsigned)lds * 2u +
+                        16u * q);
+                }
+        } else {
+#pragma unroll
+        for (int q = 0; q < UPL; ++q) {
+            const int ud = u0 + j + 32 * q;
+            const int udc = ud < units ? ud : units - 1;
+            if (FAST) {
+                const char *xb = reinterpret_cast<const char *>(x) + (unsigned)udc * 64u;
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    xraw[q][c] = *reinterpret_cast<const v4f *>(xb + 16 * c);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int k = udc * 16 + 4 * c + e;
+                        xraw[q][c][e] = x[k < K ? k : K - 1];
+                    }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < RPL; ++m) {
+            const int row = row0 + m;
+            const int rowc = row < M ? row : row_last;
+#pragma unroll
+            for (int q = 0; q < UPL; ++q) {
+                const int ud = u0 + j + 32 * q;
+                const int udc = ud < units ? ud : units - 1;
+                if (FAST) {
+                    const unsigned qo = (unsigned)rowc * (unsigned)ldq;
+                    const unsigned so = ((unsigned)rowc * (unsigned)lds + (unsigned)(udc >> 2)) * 2u;
+                    load_unit<BITS, true>(reinterpret_cast<const uint8_t *>(Q) + qo, udc, K,
+                                          craw[m][q]);
+                    sraw[m][q] = *reinterpret_cast<const uint16_t *>(
+                        reinterpret_cast<const char *>(S) + so);
+                } else {
+                    load_unit<BITS, false>(Q + (int64_t)rowc * ldq, udc, K, craw[m][q]);
+                    sraw[m][q] = S[(int64_t)rowc * lds + (udc >> 2)];
+                }
+            }
+        }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- Dead units (past the row's end, only in a last partial pass)
+        // contribute nothing: their x and scale are zeroed.  Rows past M are
+        // computed on a clamped row and never stored.
+        float xv[UPL][16];
+        unsigned sbits[RPL][UPL];
+        if (FULL || (FAST && u0 + UNITS_PER_PASS <= units)) {
+#pragma unroll
+            for (int q = 0; q < UPL; ++q) {
+#pragma unroll
+                for (int p = 0; p < 16; ++p) xv[q][p] = xraw[q][p >> 2][p & 3];
+#pragma unroll
+                for (int m = 0; m < RPL; ++m) sbits[m][q] = sraw[m][q];
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < UPL; ++q) {
+                const int ud = u0 + j + 32 * q;
+                const bool live = ud < units;
+#pragma unroll
+                for (int p = 0; p < 16; ++p)
+                    xv[q][p] = (live && (FAST || ud * 16 + p < K)) ? xraw[q][p >> 2][p & 3] : 0.f;
+#pragma unroll
+                for (int m = 0; m < RPL; ++m) sbits[m][q] = live ? sraw[m][q] : 0u;
+            }
+        }
+
+        float init[UPL];
+#pragma unroll
+        for (int q = 0; q < UPL; ++q) {
+            float X = 0.f;
+#pragma unroll
+            for (int p = 0; p < 16; ++p) X += xv[q][p];
+            init[q] = C::INIT * X;
+        }
+
+        // ---- Row by row; the UPL units of a row are independent
+        // multiply-add chains, interleaved step by step.
+#pragma unroll
+        for (int m = 0; m < RPL; ++m) {
+            float a[UPL];
+#pragma unroll
+            for (int q = 0; q < UPL; ++q) a[q] = BITS == 2 ? init[q] : 0.f;
+#pragma unroll
+            for (int i = 0; i < UW; ++i)
+#pragma unroll
+                for (int t = 0; t < C::HALF; ++t) {
+#pragma unroll
+                    for (int q = 0; q < UPL; ++q) {
+                        const unsigned d = craw[m][q][i];
+                        // codes t and t+HALF of the word moved to the top
+                        // fraction bits of the low and high halves
+                        const unsigned sh = BITS * t <= C::TOP ? (d << (C::TOP - BITS * t))
+                                                               : (d >> (BITS * t - C::TOP));
+                        const unsigned hb = (sh & mask) | one;
+                        const h2 hv = __builtin_bit_cast(h2, hb);
+                        a[q] = __builtin_fmaf((float)hv.x, xv[q][i * C::CPD + t], a[q]);
+                        a[q] = __builtin_fmaf((float)hv.y, xv[q][i * C::CPD + t + C::HALF], a[q]);
+                    }
+                }
+#pragma unroll
+            for (int q = 0; q < UPL; ++q) {
+                if (BITS != 2) a[q] += init[q];
+                const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits[m][q]);
+                acc[m] = __builtin_fmaf(s, a[q], acc[m]);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+        const float t = half32_sum(acc[m]);
+        if (j == 0 && row0 + m < M) y[row0 + m] = C::OUT * t;
+    }
+}
+
+// A single product needs every SIMD busy: 6 rows per half-wave gives one
+// wave per SIMD at 12,288 rows.  A batch has waves to spare, so each lane
+// takes more rows and reuses its x registers and unit sums longer.
+template <int BITS, int NB, int RPL = (NB == 1 ? 6 : 12)>
+hipError_t launch_chunk(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
+                        const uint16_t *const *S, int64_t lds, const float *const *x,
+                        float *const *y, hipStream_t s) {
+    constexpr int UB = 2 * BITS;                   // bytes per unit of 16 codes
+    const int rows_per_wg = WAVES * 2 * RPL;
+    const dim3 grid((M + rows_per_wg - 1) / rows_per_wg, count);
+    PackedPtrs<NB> p;
+    bool aligned = true;
+    for (int b = 0; b < NB; ++b) {
+        const int i = b < count ? b : 0;
+        p.Q[b] = Q[i];
+        p.S[b] = S[i];
+        p.x[b] = x[i];
+        p.y[b] = y[i];
+        aligned = aligned && reinterpret_cast<uintptr_t>(Q[i]) % UB == 0 &&
+                  reinterpret_cast<uintptr_t>(x[i]) % 16 == 0;
+    }
+    // unit loads, 16-byte x loads, and 32-bit byte offsets into Q and S
+    const bool fast = aligned && (K % 16 == 0) && (ldq % UB == 0) &&
+                      (int64_t)M * ldq < (int64_t(1) << 32) &&
+                      (int64_t)M * lds * 2 < (int64_t(1) << 32);
+    const bool full = fast && (K % (16 * UNITS_PER_PASS) == 0) && (M % (2 * RPL) == 0);
+    if (full)
+        hipLaunchKernelGGL((gemv_packed_kernel<BITS, RPL, true, true, NB>), grid, dim3(THREADS),
+                           0, s, M, K, ldq, lds, p);
+    else if (fast)
+        hipLaunchKernelGGL((gemv_packed_kernel<BITS, RPL, true, false, NB>), grid, dim3(THREADS),
+                           0, s, M, K, ldq, lds, p);
+    else
+        hipLaunchKernelGGL((gemv_packed_kernel<BITS, RPL, false, false, NB>), grid, dim3(THREADS),
+                           0, s, M, K, ldq, lds, p);
+    return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_batch(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
+                        const uint16_t *const *S, int64_t lds, const float *const *x,
+                        float *const *y, hipStream_t s) {
+    if (count == 1) return launch_chunk<BITS, 1>(1, M, K, Q, ldq, S, lds, x, y, s);
+    // Up to PACKED_MAX_BATCH products per launch (their pointers travel in
+    // the kernel arguments); larger batches take several launches in order.
+    for (int b0 = 0; b0 < count; b0 += PACKED_MAX_BATCH) {
+        const int n = count - b0 < PACKED_MAX_BATCH ? count - b0 : PACKED_MAX_BATCH;
+        const hipError_t e = launch_chunk<BITS, PACKED_MAX_BATCH>(n, M, K, Q + b0, ldq, S + b0,
+                                                                  lds, x + b0, y + b0, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_gemv_q2(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
+                          const uint16_t *const *S, int64_t lds, const float *const *x,
+                          float *const *y, hipStream_t s) {
+    return launch_batch<2>(count, M, K, Q, ldq, S, lds, x, y, s);
+}
+
+hipError_t launch_gemv_q4(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
+                          const uint16_t *const *S, int64_t lds, const float *const *x,
+                          float *const *y, hipStream_t s) {
+    return launch_batch<4>(count, M, K, Q, ldq, S, lds, x, y, s);
+}
+
+}  // namespace gg

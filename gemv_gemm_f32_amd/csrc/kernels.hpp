@@ -23,10 +23,14 @@ hipError_t launch_gemm(GemmLayout layout, int M, int N, int K,
 hipError_t launch_gemv_f32(int M, int K, const float *W, int64_t ldw,
                            const float *x, float *y, hipStream_t stream);
 
-// y_b = W_b.x_b for b < count, W_b as 2-bit codes with one binary16 scale
-// per 64 columns; the pointer arrays are host arrays of device pointers.
-constexpr int Q2_MAX_BATCH = 64;
+// y_b = W_b.x_b for b < count, W_b as 2-bit (q2) or 4-bit (q4) codes with
+// one binary16 scale per 64 columns; the pointer arrays are host arrays of
+// device pointers.
+constexpr int PACKED_MAX_BATCH = 64;
 hipError_t launch_gemv_q2(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
+                          const uint16_t *const *S, int64_t lds, const float *const *x,
+                          float *const *y, hipStream_t stream);
+hipError_t launch_gemv_q4(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
                           const uint16_t *const *S, int64_t lds, const float *const *x,
                           float *const *y, hipStream_t stream);
 

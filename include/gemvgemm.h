@@ -1,7 +1,7 @@
 /*
  * gemvgemm.h -- C interface of libgemvgemm.so: fp32 matrix products, the fp32
- * matrix-vector product, and the 2-bit packed-weight matrix-vector product,
- * as hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ * matrix-vector product, and the 2-bit and 4-bit packed-weight matrix-vector
+ * products, as hand-written HIP kernels for AMD Instinct MI355X (gfx950).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -142,6 +142,38 @@ int gemv_q2(int64_t M, int64_t K, const uint8_t *Q, int64_t ldq,
  * need not match it bit for bit.
  */
 int gemv_q2_batched(int64_t count, int64_t M, int64_t K,
+                    const uint8_t *const *Q, int64_t ldq,
+                    const uint16_t *const *S, int64_t lds,
+                    const float *const *x, float *const *y, gg_stream_t stream);
+
+/*
+ * y[M] = W[M x K] . x[K] with W held as 4-bit codes and binary16 scales.
+ *
+ * 4-bit weight matrices sit beside the 2-bit one on the same path: two of the
+ * kernels patched with "Kernel 0112" are 4-bit (section "What is being
+ * measured"), and "More Stumbling, This Time in the Browser" has a packed
+ * 4-bit (NF4) path.  No page fixes the format; this library reads it like the
+ * 2-bit one:
+ *   code(i,k) = (Q[i*ldq + k/2] >> (4*(k%2))) & 15   (least significant first)
+ *   s(i,k)    = binary16 S[i*lds + k/64]             (one scale per 64 columns)
+ *   w(i,k)    = (code(i,k) - 7.5) * s(i,k)
+ *   y[i]      = sum_k w(i,k) * x[k]
+ *   Q: ldq >= ceil(K/2) bytes per row;  S: lds >= ceil(K/64) halves per row;
+ *   x (fp32) and y (fp32) contiguous.
+ * Bits of Q for columns k >= K and scales past ceil(K/64) are never used.
+ * A non-uniform codebook such as NF4 is not this format.
+ */
+int gemv_q4(int64_t M, int64_t K, const uint8_t *Q, int64_t ldq,
+            const uint16_t *S, int64_t lds,
+            const float *x, float *y, gg_stream_t stream);
+
+/*
+ * y_b = W_b . x_b for b = 0 .. count-1: count independent 4-bit products of
+ * one shape, each exactly as gemv_q4 defines it, in as few launches as
+ * possible (up to 64 products per launch).  Arguments, aliasing rules and
+ * result guarantees are those of gemv_q2_batched.
+ */
+int gemv_q4_batched(int64_t count, int64_t M, int64_t K,
                     const uint8_t *const *Q, int64_t ldq,
                     const uint16_t *const *S, int64_t lds,
                     const float *const *x, float *const *y, gg_stream_t stream);

@@ -116,11 +116,41 @@ def test_gemv_q2_validation():
     assert f(4, 100, PA, 25, PB, 2, PX, PB + 4, None) == bd.GG_ERR_ALIAS
 
 
+def test_gemv_q4_validation():
+    f = lib.gemv_q4
+    # K = 101: rows need ceil(101/2) = 51 bytes and ceil(101/64) = 2 scales
+    assert f(4, 101, PA, 50, PB, 2, PX, PC, None) == bd.GG_ERR_INVALID_ARG
+    assert f(4, 101, PA, 51, PB, 1, PX, PC, None) == bd.GG_ERR_INVALID_ARG
+    assert f(4, 101, PA, 51, PB + 1, 2, PX, PC, None) == bd.GG_ERR_INVALID_ARG
+    assert f(4, 101, PA, 51, PB, 2, PX + 2, PC, None) == bd.GG_ERR_INVALID_ARG
+    assert f(-1, 101, PA, 51, PB, 2, PX, PC, None) == bd.GG_ERR_INVALID_ARG
+    assert f(0, 101, None, 0, None, 0, None, None, None) == bd.GG_OK
+    # the codes of 4 rows of 51 bytes end at PA + 204: y starting there is fine,
+    # y starting at PA + 200 overlaps
+    assert f(4, 101, PA, 51, PB, 2, PX, PA + 200, None) == bd.GG_ERR_ALIAS
+    assert f(4, 101, PA, 51, PB, 2, PX, PB + 4, None) == bd.GG_ERR_ALIAS
+    st = f(4, 101, PA, 51, PB, 2, PX, PA + 204, None)
+    assert st not in (bd.GG_ERR_ALIAS, bd.GG_ERR_INVALID_ARG)
+
+
+def test_gemv_q4_batched_validation():
+    f = lib.gemv_q4_batched
+    Q = _parr(PA, PA + 0x100000)
+    S = _parr(PB, PB + 0x100000)
+    x = _parr(PX, PX)
+    y = _parr(PC, PC + 0x100000)
+    assert f(2, 4, 64, Q, 31, S, 1, x, y, None) == bd.GG_ERR_INVALID_ARG   # needs 32 bytes
+    assert f(2, 4, 64, Q, 32, S, 1, x, _parr(PC, PA + 96), None) == bd.GG_ERR_ALIAS
+    st = f(2, 4, 64, Q, 32, S, 1, x, y, None)
+    assert st not in (bd.GG_ERR_ALIAS, bd.GG_ERR_INVALID_ARG)
+
+
 @pytest.mark.skipif(_gpu_present(), reason="checks the no-device path")
 def test_no_device_is_reported():
     assert lib.gemm_f32(4, 4, 4, PA, 4, PB, 4, PC, 4, None) == bd.GG_ERR_NO_DEVICE
     assert lib.gemv_f32(4, 4, PA, 4, PX, PC, None) == bd.GG_ERR_NO_DEVICE
     assert lib.gemv_q2(4, 64, PA, 16, PB, 1, PX, PC, None) == bd.GG_ERR_NO_DEVICE
+    assert lib.gemv_q4(4, 64, PA, 32, PB, 1, PX, PC, None) == bd.GG_ERR_NO_DEVICE
 
 
 def test_single_hip_runtime_in_process():
