@@ -24,7 +24,8 @@ Output: one JSON line.  `value` is the GEMM's TFLOP/s (2 * 2048^3 flops per
 launch over its average launch duration); the 2-bit GEMV's weight GB/s
 (codes + scales per call over its average duration) is in `q2_gemv`.  Both
 carry a roofline object.  `q2_gemv_batched` times the same tokens with each
-token's 40 products in one gemv_q2_batched launch.  Before any number is
+token's 40 products in one gemv_q2_batched launch; `q4_gemv` times the 4-bit
+product the same two ways.  Before any number is
 printed the outputs are checked against the CPU oracle on sampled cells; a
 failing kernel reports no speed.  `cpu_baseline` times the oracle itself on a bounded sample.
 """
@@ -52,6 +53,10 @@ Q2_WEIGHT_BYTES = Q2_CODE_BYTES + Q2_SCALE_BYTES   # 5,308,416
 Q2_ALG_BYTES = Q2_WEIGHT_BYTES + Q2_K * 4 + Q2_M * 4   # + x + y = 5,363,712
 Q2_ROTATION = 128
 CALLS_PER_TOKEN = 40
+Q4_CODE_BYTES = Q2_M * Q2_K // 2                   # 9,437,184
+Q4_WEIGHT_BYTES = Q4_CODE_BYTES + Q2_SCALE_BYTES   # 10,027,008
+Q4_ALG_BYTES = Q4_WEIGHT_BYTES + Q2_K * 4 + Q2_M * 4   # + x + y = 10,082,304
+Q4_ROTATION = 64                                   # 642 MB of codes+scales
 
 PEAK_FP32_MFMA_TFLOPS = 157.3      # MI355X dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
@@ -181,15 +186,20 @@ def write_traffic(fetch_db, write_db):
     f_scale = nbytes / (fetch[ck] * 1024.0)
     w_scale = nbytes / (write[ck] * 1024.0)
     out = []
-    q2_srcs = ("gemv_q2.hip", "wave.hpp")
+    q2_srcs = ("gemv_packed.hip", "wave.hpp")
     for match, fname, srcs, alg in (
             (lambda n: n.startswith("gemm_f32_direct<128, 64, true, false>"),
              "traffic_gemm_f32_2048.json", ("gemm_f32.hip",), 3 * 4 * GEMM_N * GEMM_N),
-            (lambda n: n.startswith("gemv_q2_kernel") and n.endswith(", 1>"),
+            (lambda n: n.startswith("gemv_packed_kernel<2,") and n.endswith(", 1>"),
              "traffic_gemv_q2_12288x1536.json", q2_srcs, Q2_ALG_BYTES),
-            (lambda n: n.startswith("gemv_q2_kernel") and n.endswith(", 64>"),
+            (lambda n: n.startswith("gemv_packed_kernel<2,") and n.endswith(", 64>"),
              "traffic_gemv_q2_batched_12288x1536.json", q2_srcs,
-             CALLS_PER_TOKEN * Q2_ALG_BYTES)):
+             CALLS_PER_TOKEN * Q2_ALG_BYTES),
+            (lambda n: n.startswith("gemv_packed_kernel<4,") and n.endswith(", 1>"),
+             "traffic_gemv_q4_12288x1536.json", q2_srcs, Q4_ALG_BYTES),
+            (lambda n: n.startswith("gemv_packed_kernel<4,") and n.endswith(", 64>"),
+             "traffic_gemv_q4_batched_12288x1536.json", q2_srcs,
+             CALLS_PER_TOKEN * Q4_ALG_BYTES)):
         k = [n for n in fetch if match(n)]
         if not k:
             continue
@@ -271,9 +281,19 @@ def main():
         Qd.append(torch.from_numpy(Q).to(dev))
         Sd.append(torch.from_numpy(S.view(np.int16)).to(dev))
     dy = torch.empty(Q2_M, dtype=torch.float32, device=dev)
+    Q4d, S4d, h4 = [], [], hashlib.sha256()
+    Q40 = S40 = None
+    for r in range(Q4_ROTATION):
+        Q, S = inputs.q4_weight(r)
+        if r == 0:
+            Q40, S40 = Q, S
+        h4.update(Q.tobytes())
+        h4.update(S.tobytes())
+        Q4d.append(torch.from_numpy(Q).to(dev))
+        S4d.append(torch.from_numpy(S.view(np.int16)).to(dev))
     torch.cuda.synchronize()
     hashes = {"gemm_A_B": inputs.sha256(A, B)[:16], "q2_x": inputs.sha256(x)[:16],
-              "q2_set": hq.hexdigest()[:16]}
+              "q2_set": hq.hexdigest()[:16], "q4_set": h4.hexdigest()[:16]}
     log("inputs ready in %.1f s" % (time.perf_counter() - t0))
 
     # ---- parity first: a wrong kernel reports no speed
@@ -297,8 +317,21 @@ def main():
         rb, bb = oracle.gemv_q2(Qb, Sb, x)
         ok, worst, _ = oracle.check(dys[b].cpu().numpy(), rb, bb)
         qb_ok, qb_worst = qb_ok and ok, max(qb_worst, worst)
-    log("parity: gemm worst %.3g, q2 worst %.3g, q2 batched worst %.3g (x 1e-4 bound)" %
-        (gemm_worst / 1e-4, q2_worst / 1e-4, qb_worst / 1e-4))
+    bd.gemv_q4(Q4d[0], S4d[0], dx, y=dy)
+    y4ref, y4bound = oracle.gemv_q4(Q40, S40, x)
+    q4_ok, q4_worst, _ = oracle.check(dy.cpu().numpy(), y4ref, y4bound)
+    bd.gemv_q4_batched(Q4d[:CALLS_PER_TOKEN], S4d[:CALLS_PER_TOKEN], [dx] * CALLS_PER_TOKEN,
+                       ys=dys)
+    q4b_ok, q4b_worst = True, 0.0
+    for b in (0, CALLS_PER_TOKEN - 1):
+        Qb, Sb = inputs.q4_weight(b)
+        rb, bb = oracle.gemv_q4(Qb, Sb, x)
+        ok, worst, _ = oracle.check(dys[b].cpu().numpy(), rb, bb)
+        q4b_ok, q4b_worst = q4b_ok and ok, max(q4b_worst, worst)
+    log("parity: gemm worst %.3g, q2 worst %.3g, q2 batched worst %.3g, q4 worst %.3g, "
+        "q4 batched worst %.3g (x 1e-4 bound)" %
+        (gemm_worst / 1e-4, q2_worst / 1e-4, qb_worst / 1e-4, q4_worst / 1e-4,
+         q4b_worst / 1e-4))
 
     if args.copy_calibration > 0:
         n = args.copy_calibration // 4
@@ -345,6 +378,19 @@ def main():
     step_graphs = [capture(lambda t=t: (bd.gemm_f32(dA, dB, C=dC), token(t)))
                    for t in range(n_tok)]
     btok_graphs = [capture(lambda t=t: token_batched(t)) for t in range(n_tok)]
+
+    def token4(t):
+        for c in range(CALLS_PER_TOKEN):
+            n = (t * CALLS_PER_TOKEN + c) % Q4_ROTATION
+            bd.gemv_q4(Q4d[n], S4d[n], dx, y=dy)
+
+    def token4_batched(t):
+        idx = [(t * CALLS_PER_TOKEN + c) % Q4_ROTATION for c in range(CALLS_PER_TOKEN)]
+        bd.gemv_q4_batched([Q4d[i] for i in idx], [S4d[i] for i in idx],
+                           [dx] * CALLS_PER_TOKEN, ys=dys)
+
+    tok4_graphs = [capture(lambda t=t: token4(t)) for t in range(n_tok)]
+    btok4_graphs = [capture(lambda t=t: token4_batched(t)) for t in range(n_tok)]
     tok_graphs = [capture(lambda t=t: token(t)) for t in range(n_tok)]
     gemm_graph = capture(lambda: [bd.gemm_f32(dA, dB, C=dC)
                                   for _ in range(gemms_per_replay)])
@@ -392,13 +438,17 @@ def main():
             tok_graphs[s % n_tok].replay()
         return args.steps * CALLS_PER_TOKEN
 
-    def run_btokens(i):
-        if i is not None:
-            btok_graphs[i % n_tok].replay()
-            return 1
-        for s in range(args.steps):
-            btok_graphs[s % n_tok].replay()
-        return args.steps * CALLS_PER_TOKEN
+    def token_runner(graphs):
+        def run(i):
+            if i is not None:
+                graphs[i % n_tok].replay()
+                return 1
+            for s in range(args.steps):
+                graphs[s % n_tok].replay()
+            return args.steps * CALLS_PER_TOKEN
+        return run
+
+    run_btokens = token_runner(btok_graphs)
 
     total_ms, _, t_wall = timed(run_steps, args.warmup)
     gemm_ms, n_gemm, _ = timed(run_gemms, max(1, args.warmup // gemms_per_replay))
@@ -406,6 +456,10 @@ def main():
     btok_ms, n_qb, _ = timed(run_btokens, args.warmup)
     qb_us = 1e3 * btok_ms / n_qb
     qb_alg_gbs = Q2_ALG_BYTES / qb_us / 1e3
+    tok4_ms, n_q4, _ = timed(token_runner(tok4_graphs), args.warmup)
+    btok4_ms, n_q4b, _ = timed(token_runner(btok4_graphs), args.warmup)
+    q4_us = 1e3 * tok4_ms / n_q4
+    q4b_us = 1e3 * btok4_ms / n_q4b
     gemm_us = 1e3 * gemm_ms / n_gemm
     q2_us = 1e3 * tok_ms / n_q2
 
@@ -415,10 +469,11 @@ def main():
 
     gemm_traffic = traffic_from_profile("traffic_gemm_f32_2048.json",
                                         src_sha("gemm_f32.hip"))
-    q2_traffic = traffic_from_profile("traffic_gemv_q2_12288x1536.json",
-                                      src_sha("gemv_q2.hip", "wave.hpp"))
-    qb_traffic = traffic_from_profile("traffic_gemv_q2_batched_12288x1536.json",
-                                      src_sha("gemv_q2.hip", "wave.hpp"))
+    psha = src_sha("gemv_packed.hip", "wave.hpp")
+    q2_traffic = traffic_from_profile("traffic_gemv_q2_12288x1536.json", psha)
+    qb_traffic = traffic_from_profile("traffic_gemv_q2_batched_12288x1536.json", psha)
+    q4_traffic = traffic_from_profile("traffic_gemv_q4_12288x1536.json", psha)
+    q4b_traffic = traffic_from_profile("traffic_gemv_q4_batched_12288x1536.json", psha)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -496,7 +551,42 @@ def main():
                 "traffic_note": "HBM bytes per product (launch total / 40)",
             },
         },
+        "q4_gemv": {
+            "metric": ("4-bit GEMV effective weight-streaming GB/s at 12288x1536 "
+                       "(cold rotation over 64 matrices)"),
+            "value": Q4_WEIGHT_BYTES / q4_us / 1e3 if q4_ok else None,
+            "unit": "GB/s",
+            "avg_launch_us": q4_us,
+            "roofline": {
+                "kernel": "gemv_q4 (12288x1536)",
+                "bound": "hbm",
+                "achieved": Q4_ALG_BYTES / q4_us / 1e3,
+                "peak": PEAK_HBM_GBS,
+                "unit": "GB/s",
+                "frac": Q4_ALG_BYTES / q4_us / 1e3 / PEAK_HBM_GBS,
+                "traffic": q4_traffic,
+            },
+            "batched": {
+                "value": Q4_WEIGHT_BYTES / q4b_us / 1e3 if q4b_ok else None,
+                "unit": "GB/s",
+                "us_per_gemv": q4b_us,
+                "roofline": {
+                    "kernel": "gemv_q4_batched (40 x 12288x1536 per launch)",
+                    "bound": "hbm",
+                    "achieved": Q4_ALG_BYTES / q4b_us / 1e3,
+                    "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s",
+                    "frac": Q4_ALG_BYTES / q4b_us / 1e3 / PEAK_HBM_GBS,
+                    "traffic": (q4b_traffic / CALLS_PER_TOKEN) if q4b_traffic else None,
+                    "traffic_note": "HBM bytes per product (launch total / 40)",
+                },
+            },
+        },
         "parity": {"gemm_f32_2048": "pass" if gemm_ok else "FAIL",
+                   "gemv_q4": "pass" if q4_ok else "FAIL",
+                   "gemv_q4_batched": "pass" if q4b_ok else "FAIL",
+                   "q4_worst_err_over_bound": q4_worst,
+                   "q4_batched_worst_err_over_bound": q4b_worst,
                    "gemv_q2": "pass" if q2_ok else "FAIL",
                    "gemv_q2_batched": "pass" if qb_ok else "FAIL",
                    "q2_batched_worst_err_over_bound": qb_worst,
@@ -509,7 +599,7 @@ def main():
         "wall_s_timed": t_wall,
     }
     print(json.dumps(out), flush=True)
-    return 0 if (gemm_ok and q2_ok and qb_ok) else 1
+    return 0 if (gemm_ok and q2_ok and qb_ok and q4_ok and q4b_ok) else 1
 
 
 if __name__ == "__main__":
