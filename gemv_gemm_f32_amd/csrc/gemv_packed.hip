@@ -14,11 +14,17 @@
 //
 //  * Units: a row is read in units of 16 codes -- 4 bytes of 2-bit codes or
 //    8 bytes of 4-bit codes -- and 4 units make one 64-column scale group.
-//  * Split: a row belongs to 32 lanes (half a wave64).  Lane j takes units j,
-//    j+32, j+64, ..., so each load instruction covers 128 (2-bit) or 256
-//    (4-bit) contiguous bytes of a row.  Each half-wave owns RPL consecutive
-//    rows and issues every code and scale load of a pass before consuming
-//    any, so all bytes of a call are requested up front.
+//  * Split: a row belongs to SPLIT lanes.  Lane j of those takes units j,
+//    j+SPLIT, j+2*SPLIT, ..., so each load instruction covers 128 (2-bit) or
+//    256 (4-bit) contiguous bytes of a row per 32 lanes.  With SPLIT = 32 (half
+//    a wave64) each half-wave owns RPL consecutive rows; with SPLIT = 256 the
+//    workgroup's four waves share RPL rows, the deeper split that long rows
+//    with few outputs need: the transposed 12,288 -> 1,536 shape, whose
+//    kernel 0113 was patched from 2 x 32 to 1 x 256 threads per row in the
+//    running model ("Kernel 0112", section "What the kernel costs in a whole
+//    token").  Either way each group of lanes issues every code and scale
+//    load of a pass before consuming any, so all bytes of a call are
+//    requested up front.
 //  * x: lane j keeps the 16 x values of each of its units in registers and
 //    reuses them for all RPL rows; x is 6 KiB and read from L2/L1.
 //  * Unpack: a shift and one and-or place two codes of a 32-bit word in the
@@ -39,9 +45,10 @@
 //    partial sums within 1.94 sum|x| (started at -(1 + z/16) X they could
 //    reach 3.4 sum|x|, and the worst case would touch the 1e-4 bound): its
 //    error is below 6.5e-5 sum |w x|.  Both hold for any inputs.
-//  * Reduction: the 32 partial sums of a row are added with DPP and
-//    ds_swizzle (wave.hpp), no LDS storage, barriers or atomics; lane 0 of the
-//    half-wave writes y.  The tree is fixed, so results repeat bit for bit.
+//  * Reduction: the partial sums of a row are added within each wave with DPP
+//    and ds_swizzle (wave.hpp), without LDS or atomics; with SPLIT = 256 the
+//    four wave sums then meet in LDS and one lane adds them in wave order.
+//    The tree is fixed, so results repeat bit for bit.
 //  * A byte-load specialisation of the same kernel serves K not a multiple of
 //    16, or Q rows not aligned to a unit; it masks columns k >= K.
 //  * Batches: blockIdx.y picks one of up to 64 products of one shape whose
@@ -62,7 +69,6 @@ typedef unsigned u2 __attribute__((ext_vector_type(2)));
 constexpr int THREADS = 256;
 constexpr int WAVES = THREADS / 64;
 constexpr int UPL = 3;                  // units of 16 codes per lane per pass
-constexpr int UNITS_PER_PASS = 32 * UPL;
 
 // Device pointers of up to NB products of one shape, passed by value in the
 // kernel arguments (blockIdx.y selects the product).
@@ -121,25 +127,33 @@ __device__ __forceinline__ void load_unit(const uint8_t *__restrict__ Qrow, int 
     }
 }
 
-// RPL rows per half-wave; FAST: unit loads and 32-bit offsets; FULL (with
-// FAST): every wave's rows and every pass's units exist, so no index is
-// clamped; NB: number of products the pointer block holds (blockIdx.y picks
-// one).
-template <int BITS, int RPL, bool FAST, bool FULL, int NB>
+// SPLIT lanes per row (32 or 256); RPL rows per group of SPLIT lanes; FAST:
+// unit loads and 32-bit offsets; FULL (with FAST): every group's rows and
+// every pass's units exist, so no index is clamped; NB: number of products
+// the pointer block holds (blockIdx.y picks one).
+template <int BITS, int SPLIT, int RPL, bool FAST, bool FULL, int NB>
 __global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int64_t ldq,
                                                               int64_t lds, PackedPtrs<NB> ptrs) {
+    static_assert(SPLIT == 32 || SPLIT == THREADS, "a row is split over 32 or 256 lanes");
     using C = Codes<BITS>;
     constexpr int UW = C::UW, UB = 4 * UW;         // words, bytes per unit
+    constexpr int UNITS_PER_PASS = SPLIT * UPL;
     const int b = NB == 1 ? 0 : (int)blockIdx.y;
     const uint8_t *__restrict__ Q = ptrs.Q[b];
     const uint16_t *__restrict__ S = ptrs.S[b];
     const float *__restrict__ x = ptrs.x[b];
     float *__restrict__ y = ptrs.y[b];
     const int lane = threadIdx.x & 63;
-    const int j = lane & 31;
-    const int wave = blockIdx.x * WAVES + (threadIdx.x >> 6);
-    const int row0 = wave * (2 * RPL) + (lane >> 5) * RPL;
-    if (wave * (2 * RPL) >= M) return;    // uniform per wave
+    const int j = SPLIT == 32 ? lane & 31 : (int)threadIdx.x;   // lane within the row's group
+    int row0;
+    if (SPLIT == 32) {
+        const int wave = blockIdx.x * WAVES + (threadIdx.x >> 6);
+        row0 = wave * (2 * RPL) + (lane >> 5) * RPL;
+        if (wave * (2 * RPL) >= M) return;    // uniform per wave
+    } else {
+        row0 = blockIdx.x * RPL;
+        if (row0 >= M) return;                // uniform per workgroup
+    }
 
     const int units = (K + 15) >> 4;      // units of 16 codes per row
     const int row_last = M - 1;
@@ -175,13 +189,13 @@ __global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int6
             for (int q = 0; q < UPL; ++q)
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    xraw[q][c] = *reinterpret_cast<const v4f *>(xb + 2048 * q + 16 * c);
+                    xraw[q][c] = *reinterpret_cast<const v4f *>(xb + 64 * SPLIT * q + 16 * c);
 #pragma unroll
             for (int m = 0; m < RPL; ++m)
 #pragma unroll
                 for (int q = 0; q < UPL; ++q) {
                     const char *qp = reinterpret_cast<const char *>(Q) + qb +
-                                     (unsigned)m * (unsigned)ldq + 32u * UB * q;
+                                     (unsigned)m * (unsigned)ldq + (unsigned)(SPLIT * UB * q);
                     if (UW == 1) {
                         craw[m][q][0] = *reinterpret_cast<const unsigned *>(qp);
                     } else {
@@ -191,12 +205,12 @@ __global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int6
                     }
                     sraw[m][q] = *reinterpret_cast<const uint16_t *>(
                         reinterpret_cast<const char *>(S) + sb + (unsigned)m * (unsigned)lds * 2u +
-                        16u * q);
+                        (unsigned)(SPLIT / 2 * q));
                 }
         } else {
 #pragma unroll
         for (int q = 0; q < UPL; ++q) {
-            const int ud = u0 + j + 32 * q;
+            const int ud = u0 + j + SPLIT * q;
             const int udc = ud < units ? ud : units - 1;
             if (FAST) {
                 const char *xb = reinterpret_cast<const char *>(x) + (unsigned)udc * 64u;
@@ -219,7 +233,7 @@ __global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int6
             const int rowc = row < M ? row : row_last;
 #pragma unroll
             for (int q = 0; q < UPL; ++q) {
-                const int ud = u0 + j + 32 * q;
+                const int ud = u0 + j + SPLIT * q;
                 const int udc = ud < units ? ud : units - 1;
                 if (FAST) {
                     const unsigned qo = (unsigned)rowc * (unsigned)ldq;
@@ -253,7 +267,7 @@ __global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int6
         } else {
 #pragma unroll
             for (int q = 0; q < UPL; ++q) {
-                const int ud = u0 + j + 32 * q;
+                const int ud = u0 + j + SPLIT * q;
                 const bool live = ud < units;
 #pragma unroll
                 for (int p = 0; p < 16; ++p)
@@ -305,22 +319,41 @@ __global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int6
         }
     }
 
+    if (SPLIT == 32) {
 #pragma unroll
-    for (int m = 0; m < RPL; ++m) {
-        const float t = half32_sum(acc[m]);
-        if (j == 0 && row0 + m < M) y[row0 + m] = C::OUT * t;
+        for (int m = 0; m < RPL; ++m) {
+            const float t = half32_sum(acc[m]);
+            if (j == 0 && row0 + m < M) y[row0 + m] = C::OUT * t;
+        }
+    } else {
+        __shared__ float part[WAVES][RPL];
+        const int wave = threadIdx.x >> 6;
+#pragma unroll
+        for (int m = 0; m < RPL; ++m) {
+            const float t = wave64_sum(acc[m]);
+            if (lane == 0) part[wave][m] = t;
+        }
+        __syncthreads();
+        if (threadIdx.x < RPL && row0 + (int)threadIdx.x < M) {
+            float t = part[0][threadIdx.x];
+#pragma unroll
+            for (int w = 1; w < WAVES; ++w) t += part[w][threadIdx.x];
+            y[row0 + threadIdx.x] = C::OUT * t;
+        }
     }
 }
 
-// A single product needs every SIMD busy: 6 rows per half-wave gives one
-// wave per SIMD at 12,288 rows.  A batch has waves to spare, so each lane
-// takes more rows and reuses its x registers and unit sums longer.
-template <int BITS, int NB, int RPL = (NB == 1 ? 6 : 12)>
+// A single product needs every SIMD busy: 6 rows per group of lanes gives
+// one wave per SIMD at 12,288 rows split 32 ways, or at 1,536 rows split 256
+// ways.  A batch has waves to spare, so each lane takes more rows and reuses
+// its x registers and unit sums longer.
+template <int BITS, int SPLIT, int NB, int RPL = (NB == 1 ? 6 : 12)>
 hipError_t launch_chunk(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
                         const uint16_t *const *S, int64_t lds, const float *const *x,
                         float *const *y, hipStream_t s) {
     constexpr int UB = 2 * BITS;                   // bytes per unit of 16 codes
-    const int rows_per_wg = WAVES * 2 * RPL;
+    constexpr int GROUPS = THREADS / SPLIT;        // row groups per workgroup
+    const int rows_per_wg = GROUPS * RPL;
     const dim3 grid((M + rows_per_wg - 1) / rows_per_wg, count);
     PackedPtrs<NB> p;
     bool aligned = true;
@@ -337,29 +370,45 @@ hipError_t launch_chunk(int count, int M, int K, const uint8_t *const *Q, int64_
     const bool fast = aligned && (K % 16 == 0) && (ldq % UB == 0) &&
                       (int64_t)M * ldq < (int64_t(1) << 32) &&
                       (int64_t)M * lds * 2 < (int64_t(1) << 32);
-    const bool full = fast && (K % (16 * UNITS_PER_PASS) == 0) && (M % (2 * RPL) == 0);
+    const bool full = fast && (K % (16 * SPLIT * UPL) == 0) &&
+                      (M % (SPLIT == 32 ? 2 * RPL : RPL) == 0);
     if (full)
-        hipLaunchKernelGGL((gemv_packed_kernel<BITS, RPL, true, true, NB>), grid, dim3(THREADS),
-                           0, s, M, K, ldq, lds, p);
+        hipLaunchKernelGGL((gemv_packed_kernel<BITS, SPLIT, RPL, true, true, NB>), grid,
+                           dim3(THREADS), 0, s, M, K, ldq, lds, p);
     else if (fast)
-        hipLaunchKernelGGL((gemv_packed_kernel<BITS, RPL, true, false, NB>), grid, dim3(THREADS),
-                           0, s, M, K, ldq, lds, p);
+        hipLaunchKernelGGL((gemv_packed_kernel<BITS, SPLIT, RPL, true, false, NB>), grid,
+                           dim3(THREADS), 0, s, M, K, ldq, lds, p);
     else
-        hipLaunchKernelGGL((gemv_packed_kernel<BITS, RPL, false, false, NB>), grid, dim3(THREADS),
-                           0, s, M, K, ldq, lds, p);
+        hipLaunchKernelGGL((gemv_packed_kernel<BITS, SPLIT, RPL, false, false, NB>), grid,
+                           dim3(THREADS), 0, s, M, K, ldq, lds, p);
     return hipGetLastError();
+}
+
+// Rows split 32 ways unless the rows are long and few: at K >= 6,144 (each
+// of 256 lanes then holds at least one live unit per pass in two of its
+// three slots) with fewer rows than 32-way groups of one product would need
+// to fill the chip, the row is split over the whole workgroup.
+inline bool deep_split(int M, int K) { return K >= 6144 && M < 12288; }
+
+template <int BITS, int NB>
+hipError_t launch_split(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
+                        const uint16_t *const *S, int64_t lds, const float *const *x,
+                        float *const *y, hipStream_t s) {
+    return deep_split(M, K)
+               ? launch_chunk<BITS, THREADS, NB>(count, M, K, Q, ldq, S, lds, x, y, s)
+               : launch_chunk<BITS, 32, NB>(count, M, K, Q, ldq, S, lds, x, y, s);
 }
 
 template <int BITS>
 hipError_t launch_batch(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
                         const uint16_t *const *S, int64_t lds, const float *const *x,
                         float *const *y, hipStream_t s) {
-    if (count == 1) return launch_chunk<BITS, 1>(1, M, K, Q, ldq, S, lds, x, y, s);
+    if (count == 1) return launch_split<BITS, 1>(1, M, K, Q, ldq, S, lds, x, y, s);
     // Up to PACKED_MAX_BATCH products per launch (their pointers travel in
     // the kernel arguments); larger batches take several launches in order.
     for (int b0 = 0; b0 < count; b0 += PACKED_MAX_BATCH) {
         const int n = count - b0 < PACKED_MAX_BATCH ? count - b0 : PACKED_MAX_BATCH;
-        const hipError_t e = launch_chunk<BITS, PACKED_MAX_BATCH>(n, M, K, Q + b0, ldq, S + b0,
+        const hipError_t e = launch_split<BITS, PACKED_MAX_BATCH>(n, M, K, Q + b0, ldq, S + b0,
                                                                   lds, x + b0, y + b0, s);
         if (e != hipSuccess) return e;
     }

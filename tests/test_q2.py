@@ -231,3 +231,34 @@ def test_batched_large_integer_exact():
     for b in range(2):
         ref, _ = oracle.gemv_q2(Qs[b], S, x)
         assert np.array_equal(host(ys[b]).astype(np.float64), ref)
+
+
+# ---- the transposed shape: 1,536 rows of 12,288 columns, split 256 ways
+
+@pytest.mark.parametrize("r", [0, 3])
+def test_transposed_shape_full_size(r):
+    Q, S = inputs.q2_weight(r, 1536, 12288)
+    x = inputs.q2_x(12288)
+    ref, bound = oracle.gemv_q2(Q, S, x)
+    assert_close(_run(Q, S, x), ref, bound, "1536x12288 #%d" % r)
+
+
+@pytest.mark.parametrize("M,K", [(1536, 12288), (100, 6500), (7, 24576), (13, 6160)])
+def test_transposed_shape_integer_exact(M, K):
+    codes = RNG.integers(0, 4, (M, K))
+    Q = _pack(codes)
+    S = np.full((M, (K + 63) // 64), 0x4000, np.uint16)
+    x = inputs.integers(RNG, (K,), -4, 4)
+    ref, _ = oracle.gemv_q2(Q, S, x)
+    assert np.array_equal(_run(Q, S, x).astype(np.float64), ref)
+
+
+def test_transposed_shape_batched():
+    mats = [inputs.q2_weight(r, 1536, 12288) for r in range(3)]
+    x = inputs.q2_x(12288)
+    dx = dev(x)
+    ys = bd.gemv_q2_batched([dev(Q) for Q, _ in mats], [dev(S.view(np.int16)) for _, S in mats],
+                            [dx] * 3)
+    for b, (Q, S) in enumerate(mats):
+        ref, bound = oracle.gemv_q2(Q, S, x)
+        assert_close(host(ys[b]), ref, bound, "batched transposed %d" % b)

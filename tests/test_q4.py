@@ -190,3 +190,33 @@ def test_batched_more_than_one_launch_and_ragged():
     for b in range(n):
         ref, bound = oracle.gemv_q4(Qs[b], Ss[b], xs[b])
         assert_close(host(ys[b]), ref, bound, "product %d" % b)
+
+
+# ---- the transposed shape: 1,536 rows of 12,288 columns, split 256 ways
+
+def test_transposed_shape_full_size():
+    Q, S = inputs.q4_weight(0, 1536, 12288)
+    x = inputs.q2_x(12288)
+    ref, bound = oracle.gemv_q4(Q, S, x)
+    assert_close(_run(Q, S, x), ref, bound, "4-bit 1536x12288")
+
+
+@pytest.mark.parametrize("M,K", [(1536, 12288), (100, 6500), (13, 6161)])
+def test_transposed_shape_integer_exact(M, K):
+    codes = RNG.integers(0, 16, (M, K))
+    Q = _pack(codes)
+    S = np.full((M, (K + 63) // 64), 0x4000, np.uint16)
+    x = inputs.integers(RNG, (K,), -2, 2)
+    ref, _ = oracle.gemv_q4(Q, S, x)
+    assert np.array_equal(_run(Q, S, x).astype(np.float64), ref)
+
+
+def test_transposed_shape_batched():
+    mats = [inputs.q4_weight(r, 1536, 12288) for r in range(3)]
+    x = inputs.q2_x(12288)
+    dx = dev(x)
+    ys = bd.gemv_q4_batched([dev(Q) for Q, _ in mats], [dev(S.view(np.int16)) for _, S in mats],
+                            [dx] * 3)
+    for b, (Q, S) in enumerate(mats):
+        ref, bound = oracle.gemv_q4(Q, S, x)
+        assert_close(host(ys[b]), ref, bound, "4-bit batched transposed %d" % b)
