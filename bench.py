@@ -25,7 +25,8 @@ launch over its average launch duration); the 2-bit GEMV's weight GB/s
 (codes + scales per call over its average duration) is in `q2_gemv`.  Both
 carry a roofline object.  `q2_gemv_batched` times the same tokens with each
 token's 40 products in one gemv_q2_batched launch; `q4_gemv` times the 4-bit
-product the same two ways.  Before any number is
+product the same two ways, and `q2_gemv_transposed` the 2-bit product at the
+transposed 1,536 x 12,288 shape.  Before any number is
 printed the outputs are checked against the CPU oracle on sampled cells; a
 failing kernel reports no speed.  `cpu_baseline` times the oracle itself on a bounded sample.
 """
@@ -57,6 +58,8 @@ Q4_CODE_BYTES = Q2_M * Q2_K // 2                   # 9,437,184
 Q4_WEIGHT_BYTES = Q4_CODE_BYTES + Q2_SCALE_BYTES   # 10,027,008
 Q4_ALG_BYTES = Q4_WEIGHT_BYTES + Q2_K * 4 + Q2_M * 4   # + x + y = 10,082,304
 Q4_ROTATION = 64                                   # 642 MB of codes+scales
+QT_M, QT_K = 1536, 12288                           # the transposed 2-bit shape
+QT_ALG_BYTES = Q2_WEIGHT_BYTES + QT_K * 4 + QT_M * 4   # 5,363,712
 
 PEAK_FP32_MFMA_TFLOPS = 157.3      # MI355X dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
@@ -190,16 +193,18 @@ def write_traffic(fetch_db, write_db):
     for match, fname, srcs, alg in (
             (lambda n: n.startswith("gemm_f32_direct<128, 64, true, false>"),
              "traffic_gemm_f32_2048.json", ("gemm_f32.hip",), 3 * 4 * GEMM_N * GEMM_N),
-            (lambda n: n.startswith("gemv_packed_kernel<2,") and n.endswith(", 1>"),
+            (lambda n: n.startswith("gemv_packed_kernel<2, 32, 6,") and n.endswith(", 1>"),
              "traffic_gemv_q2_12288x1536.json", q2_srcs, Q2_ALG_BYTES),
-            (lambda n: n.startswith("gemv_packed_kernel<2,") and n.endswith(", 64>"),
+            (lambda n: n.startswith("gemv_packed_kernel<2, 32, 12,") and n.endswith(", 64>"),
              "traffic_gemv_q2_batched_12288x1536.json", q2_srcs,
              CALLS_PER_TOKEN * Q2_ALG_BYTES),
-            (lambda n: n.startswith("gemv_packed_kernel<4,") and n.endswith(", 1>"),
+            (lambda n: n.startswith("gemv_packed_kernel<4, 32, 6,") and n.endswith(", 1>"),
              "traffic_gemv_q4_12288x1536.json", q2_srcs, Q4_ALG_BYTES),
-            (lambda n: n.startswith("gemv_packed_kernel<4,") and n.endswith(", 64>"),
+            (lambda n: n.startswith("gemv_packed_kernel<4, 32, 12,") and n.endswith(", 64>"),
              "traffic_gemv_q4_batched_12288x1536.json", q2_srcs,
-             CALLS_PER_TOKEN * Q4_ALG_BYTES)):
+             CALLS_PER_TOKEN * Q4_ALG_BYTES),
+            (lambda n: n.startswith("gemv_packed_kernel<2, 256, 6,") and n.endswith(", 1>"),
+             "traffic_gemv_q2_1536x12288.json", q2_srcs, QT_ALG_BYTES)):
         k = [n for n in fetch if match(n)]
         if not k:
             continue
@@ -291,9 +296,25 @@ def main():
         h4.update(S.tobytes())
         Q4d.append(torch.from_numpy(Q).to(dev))
         S4d.append(torch.from_numpy(S.view(np.int16)).to(dev))
+    # the transposed shape: 1,536 rows of 12,288 columns, same bytes per matrix
+    xt = inputs.q2_x(QT_K)
+    dxt = torch.from_numpy(xt).to(dev)
+    QTd, STd, ht = [], [], hashlib.sha256()
+    QT0 = ST0 = None
+    for r in range(Q2_ROTATION):
+        Q, S = inputs.q2_weight(r, QT_M, QT_K)
+        if r == 0:
+            QT0, ST0 = Q, S
+        ht.update(Q.tobytes())
+        ht.update(S.tobytes())
+        QTd.append(torch.from_numpy(Q).to(dev))
+        STd.append(torch.from_numpy(S.view(np.int16)).to(dev))
+    dyt = torch.empty(QT_M, dtype=torch.float32, device=dev)
+    dyts = [torch.empty(QT_M, dtype=torch.float32, device=dev) for _ in range(CALLS_PER_TOKEN)]
     torch.cuda.synchronize()
     hashes = {"gemm_A_B": inputs.sha256(A, B)[:16], "q2_x": inputs.sha256(x)[:16],
-              "q2_set": hq.hexdigest()[:16], "q4_set": h4.hexdigest()[:16]}
+              "q2_set": hq.hexdigest()[:16], "q4_set": h4.hexdigest()[:16],
+              "q2_transposed_set": ht.hexdigest()[:16], "q2_transposed_x": inputs.sha256(xt)[:16]}
     log("inputs ready in %.1f s" % (time.perf_counter() - t0))
 
     # ---- parity first: a wrong kernel reports no speed
@@ -328,10 +349,13 @@ def main():
         rb, bb = oracle.gemv_q4(Qb, Sb, x)
         ok, worst, _ = oracle.check(dys[b].cpu().numpy(), rb, bb)
         q4b_ok, q4b_worst = q4b_ok and ok, max(q4b_worst, worst)
+    bd.gemv_q2(QTd[0], STd[0], dxt, y=dyt)
+    ytref, ytbound = oracle.gemv_q2(QT0, ST0, xt)
+    qt_ok, qt_worst, _ = oracle.check(dyt.cpu().numpy(), ytref, ytbound)
     log("parity: gemm worst %.3g, q2 worst %.3g, q2 batched worst %.3g, q4 worst %.3g, "
-        "q4 batched worst %.3g (x 1e-4 bound)" %
+        "q4 batched worst %.3g, q2 transposed worst %.3g (x 1e-4 bound)" %
         (gemm_worst / 1e-4, q2_worst / 1e-4, qb_worst / 1e-4, q4_worst / 1e-4,
-         q4b_worst / 1e-4))
+         q4b_worst / 1e-4, qt_worst / 1e-4))
 
     if args.copy_calibration > 0:
         n = args.copy_calibration // 4
@@ -389,6 +413,18 @@ def main():
         bd.gemv_q4_batched([Q4d[i] for i in idx], [S4d[i] for i in idx],
                            [dx] * CALLS_PER_TOKEN, ys=dys)
 
+    def tokent(t):
+        for c in range(CALLS_PER_TOKEN):
+            n = (t * CALLS_PER_TOKEN + c) % Q2_ROTATION
+            bd.gemv_q2(QTd[n], STd[n], dxt, y=dyt)
+
+    def tokent_batched(t):
+        idx = [(t * CALLS_PER_TOKEN + c) % Q2_ROTATION for c in range(CALLS_PER_TOKEN)]
+        bd.gemv_q2_batched([QTd[i] for i in idx], [STd[i] for i in idx],
+                           [dxt] * CALLS_PER_TOKEN, ys=dyts)
+
+    tokt_graphs = [capture(lambda t=t: tokent(t)) for t in range(n_tok)]
+    btokt_graphs = [capture(lambda t=t: tokent_batched(t)) for t in range(n_tok)]
     tok4_graphs = [capture(lambda t=t: token4(t)) for t in range(n_tok)]
     btok4_graphs = [capture(lambda t=t: token4_batched(t)) for t in range(n_tok)]
     tok_graphs = [capture(lambda t=t: token(t)) for t in range(n_tok)]
@@ -460,6 +496,10 @@ def main():
     btok4_ms, n_q4b, _ = timed(token_runner(btok4_graphs), args.warmup)
     q4_us = 1e3 * tok4_ms / n_q4
     q4b_us = 1e3 * btok4_ms / n_q4b
+    tokt_ms, n_qt, _ = timed(token_runner(tokt_graphs), args.warmup)
+    btokt_ms, n_qtb, _ = timed(token_runner(btokt_graphs), args.warmup)
+    qt_us = 1e3 * tokt_ms / n_qt
+    qtb_us = 1e3 * btokt_ms / n_qtb
     gemm_us = 1e3 * gemm_ms / n_gemm
     q2_us = 1e3 * tok_ms / n_q2
 
@@ -474,6 +514,7 @@ def main():
     qb_traffic = traffic_from_profile("traffic_gemv_q2_batched_12288x1536.json", psha)
     q4_traffic = traffic_from_profile("traffic_gemv_q4_12288x1536.json", psha)
     q4b_traffic = traffic_from_profile("traffic_gemv_q4_batched_12288x1536.json", psha)
+    qt_traffic = traffic_from_profile("traffic_gemv_q2_1536x12288.json", psha)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -582,7 +623,32 @@ def main():
                 },
             },
         },
+        "q2_gemv_transposed": {
+            "metric": ("2-bit GEMV effective weight-streaming GB/s at the transposed shape "
+                       "1536x12288 (12,288 inputs -> 1,536 outputs), cold rotation over 128 "
+                       "matrices; rows split over 256 lanes"),
+            "value": Q2_WEIGHT_BYTES / qt_us / 1e3 if qt_ok else None,
+            "unit": "GB/s",
+            "avg_launch_us": qt_us,
+            "roofline": {
+                "kernel": "gemv_q2 (1536x12288)",
+                "bound": "hbm",
+                "achieved": QT_ALG_BYTES / qt_us / 1e3,
+                "peak": PEAK_HBM_GBS,
+                "unit": "GB/s",
+                "frac": QT_ALG_BYTES / qt_us / 1e3 / PEAK_HBM_GBS,
+                "traffic": qt_traffic,
+            },
+            "batched": {
+                "value": Q2_WEIGHT_BYTES / qtb_us / 1e3 if qt_ok else None,
+                "unit": "GB/s",
+                "us_per_gemv": qtb_us,
+                "frac": QT_ALG_BYTES / qtb_us / 1e3 / PEAK_HBM_GBS,
+            },
+        },
         "parity": {"gemm_f32_2048": "pass" if gemm_ok else "FAIL",
+                   "gemv_q2_transposed": "pass" if qt_ok else "FAIL",
+                   "q2_transposed_worst_err_over_bound": qt_worst,
                    "gemv_q4": "pass" if q4_ok else "FAIL",
                    "gemv_q4_batched": "pass" if q4b_ok else "FAIL",
                    "q4_worst_err_over_bound": q4_worst,
@@ -599,7 +665,7 @@ def main():
         "wall_s_timed": t_wall,
     }
     print(json.dumps(out), flush=True)
-    return 0 if (gemm_ok and q2_ok and qb_ok and q4_ok and q4b_ok) else 1
+    return 0 if (gemm_ok and q2_ok and qb_ok and q4_ok and q4b_ok and qt_ok) else 1
 
 
 if __name__ == "__main__":
