@@ -85,6 +85,10 @@ def bind(lib):
     lib.oracle_q2_unpack_row.restype = None
     lib.oracle_gemv_q2.argtypes = [i64, i64, vp, i64, vp, i64, vp, vp, vp, vp]
     lib.oracle_gemv_q2.restype = None
+    dbl = ctypes.c_double
+    lib.oracle_gemm_ex.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, dbl, vp, i64,
+                                   vp, i64, dbl, vp, i64, vp, vp]
+    lib.oracle_gemm_ex.restype = None
     lib.oracle_q4_unpack_row.argtypes = [i64, i64, vp, i64, vp, i64, vp]
     lib.oracle_q4_unpack_row.restype = None
     lib.oracle_gemv_q4.argtypes = [i64, i64, vp, i64, vp, i64, vp, vp, vp, vp]
@@ -170,6 +174,35 @@ def gemm_cells(A, B, rows, cols, trans_a=False, trans_b=False):
                           _ptr(B), ldb, rows.size, _ptr(rows), _ptr(cols),
                           _ptr(c), _ptr(b))
     return c, b
+
+
+def gemm_ex(A, B, C=None, alpha=1.0, beta=0.0, trans_a=False, trans_b=False):
+    """alpha * op(A).op(B) + beta * C (C is not read when beta == 0), with
+    op(A) = A^T if trans_a and op(B) = B^T if trans_b; alpha and beta are
+    taken as fp32 values.  Returns (values, bounds) as M x N fp64 arrays."""
+    lib = _load()
+    A, lda = _as2d(A, np.float32)
+    B, ldb = _as2d(B, np.float32)
+    M = A.shape[1] if trans_a else A.shape[0]
+    K = A.shape[0] if trans_a else A.shape[1]
+    Kb = B.shape[1] if trans_b else B.shape[0]
+    N = B.shape[0] if trans_b else B.shape[1]
+    if K != Kb:
+        raise ValueError("inner dimensions differ")
+    alpha = float(np.float32(alpha))
+    beta = float(np.float32(beta))
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs C")
+        C = np.full((M, N), np.nan, np.float32)     # never read when beta == 0
+    C, ldc = _as2d(C, np.float32)
+    if C.shape != (M, N):
+        raise ValueError("C must be M x N")
+    out = np.zeros((M, N), np.float64)
+    bnd = np.zeros((M, N), np.float64)
+    lib.oracle_gemm_ex(int(trans_a), int(trans_b), M, N, K, alpha, _ptr(A), lda,
+                       _ptr(B), ldb, beta, _ptr(C), ldc, _ptr(out), _ptr(bnd))
+    return out, bnd
 
 
 def gemv(W, x):

@@ -24,7 +24,10 @@
  *  - "I built a GPT-2 in the browser, then made it 2.6x-12.1x faster",
  *    sections "The architecture in 60 seconds" and "The kernel sweep": matmul
  *    with hand-derived backward passes, which for Y = X.W need dX = dY.W^T and
- *    dW = X^T.dY (the transposed products below).
+ *    dW = X^T.dY (the transposed products below).  The same training loop
+ *    (forward, backward, AdamW) accumulates gradients; the scaled and
+ *    accumulating form C = alpha * op(A).op(B) + beta * C is read from that
+ *    (the pages give no formula for it; beta = 0 means C is not read).
  *  - "Kernel 0112", section "What is being measured": a 12,288 x 1,536 matrix
  *    of 2-bit weights times a vector of 1,536 inputs, 12,288 outputs; section
  *    "The kernel": the 2-bit fields are unpacked to floating point before the
@@ -137,6 +140,39 @@ void oracle_gemm_cells(int trans_a, int trans_b, int64_t K,
 }
 
 /* ----------------------------------------------------------------- gemv -- */
+
+/* C_out = alpha * op(A).op(B) + beta * C_in, one cell at a time:
+ *   s  = sum_k opA(i,k) * opB(k,j), k = 0, 1, ..., K-1 (fp64)
+ *   c  = alpha * s + beta * C_in[i*ldc + j]   (the C_in term only if beta != 0,
+ *        so C_in is not read when beta == 0 and may hold anything)
+ * with opA(i,k) = A[k*lda + i] if trans_a else A[i*lda + k] and
+ *      opB(k,j) = B[j*ldb + k] if trans_b else B[k*ldb + j].
+ * bound = |alpha| * sum_k |opA * opB| + |beta * C_in|.  C_out and bound are
+ * M x N doubles with stride N. */
+void oracle_gemm_ex(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                    double alpha, const float *A, int64_t lda,
+                    const float *B, int64_t ldb, double beta,
+                    const float *C_in, int64_t ldc, double *C_out, double *bound)
+{
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) {
+            double s = 0.0, t = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double a = trans_a ? (double)A[k * lda + i] : (double)A[i * lda + k];
+                double b = trans_b ? (double)B[j * ldb + k] : (double)B[k * ldb + j];
+                s += a * b;
+                t += fabs(a * b);
+            }
+            double c = alpha * s, u = fabs(alpha) * t;
+            if (beta != 0.0) {
+                double cin = beta * (double)C_in[i * ldc + j];
+                c += cin;
+                u += fabs(cin);
+            }
+            C_out[i * N + j] = c;
+            bound[i * N + j] = u;
+        }
+}
 
 /* y = W.x with W row-major M x K (W[i*ldw+k]). */
 void oracle_gemv(int64_t M, int64_t K, const float *W, int64_t ldw,

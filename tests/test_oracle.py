@@ -393,3 +393,59 @@ def test_check_semantics():
     assert not oracle.check([1e-30], [0.0], [0.0])[0]
     assert not oracle.check([np.nan], [0.0], [1.0])[0]
     assert not oracle.check([np.inf], [1e38], [1e38])[0]
+
+
+# ------------------------------------------------------ scaled, accumulating --
+
+def test_gemm_ex_tiny_golden():
+    g = load("gemm_ex_tiny_2x3x2.txt")
+    A, B, C = _f32(g["A"]), _f32(g["B"]), _f32(g["C"])
+    alpha, beta = np.asarray(g["alpha_beta"], np.float64)[0]
+    out, bound = oracle.gemm_ex(A, B, C, alpha, beta)
+    assert np.array_equal(out, np.asarray(g["out"], np.float64))
+    assert np.array_equal(bound, np.asarray(g["bound"], np.float64))
+
+
+@pytest.mark.parametrize("ta,tb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+@pytest.mark.parametrize("alpha,beta", [(1.0, 0.0), (2.5, -0.5), (-1.0, 1.0), (0.75, 3.0)])
+def test_gemm_ex_matches_numpy(ta, tb, alpha, beta):
+    M, N, K = 13, 9, 21
+    A = inputs.uniform(RNG, (K, M) if ta else (M, K))
+    B = inputs.uniform(RNG, (N, K) if tb else (K, N))
+    C = inputs.uniform(RNG, (M, N))
+    a64 = A.astype(np.float64).T if ta else A.astype(np.float64)
+    b64 = B.astype(np.float64).T if tb else B.astype(np.float64)
+    ref = alpha * (a64 @ b64) + beta * C.astype(np.float64)
+    out, bound = oracle.gemm_ex(A, B, C, alpha, beta, trans_a=bool(ta), trans_b=bool(tb))
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(bound, abs(alpha) * (np.abs(a64) @ np.abs(b64)) +
+                               np.abs(beta * C.astype(np.float64)), rtol=1e-13)
+
+
+def test_gemm_ex_beta_zero_ignores_c():
+    A = inputs.uniform(RNG, (6, 5))
+    B = inputs.uniform(RNG, (5, 4))
+    C = np.full((6, 4), np.nan, np.float32)
+    out, _ = oracle.gemm_ex(A, B, C, 1.5, 0.0)
+    assert np.all(np.isfinite(out))
+    np.testing.assert_allclose(out, 1.5 * (A.astype(np.float64) @ B.astype(np.float64)),
+                               rtol=0, atol=1e-13)
+
+
+def test_gemm_ex_alpha_zero_scales_c_exactly():
+    A = inputs.uniform(RNG, (6, 5))
+    B = inputs.uniform(RNG, (5, 4))
+    C = inputs.uniform(RNG, (6, 4))
+    out, _ = oracle.gemm_ex(A, B, C, 0.0, -2.0)
+    assert np.array_equal(out, -2.0 * C.astype(np.float64))
+
+
+def test_gemm_ex_integer_exact():
+    M, N, K = 17, 11, 40
+    A = inputs.integers(RNG, (K, M))
+    B = inputs.integers(RNG, (N, K))
+    C = inputs.integers(RNG, (M, N))
+    out, _ = oracle.gemm_ex(A, B, C, 3.0, -2.0, trans_a=True, trans_b=True)
+    ref = 3 * (A.T.astype(np.int64) @ B.T.astype(np.int64)) - 2 * C.astype(np.int64)
+    assert np.array_equal(out, ref.astype(np.float64))
+

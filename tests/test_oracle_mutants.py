@@ -51,6 +51,12 @@ MUTANTS = {
                        "& 15u;\n        double s = oracle_half_to_double(S[i * lds + k / 32]);"),
     "q4_dot_drops_last": ("oracle_q4_unpack_row(i, K, Q, ldq, S, lds, w);\n        double s = 0.0, t = 0.0;\n        for (int64_t k = 0; k < K; ++k)",
                           "oracle_q4_unpack_row(i, K, Q, ldq, S, lds, w);\n        double s = 0.0, t = 0.0;\n        for (int64_t k = 0; k + 1 < K; ++k)"),
+    "ex_bound_drops_beta": ("u += fabs(cin);", "u += 0.0;"),
+    "ex_beta_scales_product": ("double c = alpha * s, u = fabs(alpha) * t;",
+                               "double c = beta * s, u = fabs(alpha) * t;"),
+    "ex_reads_c_when_beta_zero": ("if (beta != 0.0) {\n                double cin", "if (1) {\n                double cin"),
+    "ex_trans_a_ignored": ("double a = trans_a ? (double)A[k * lda + i] : (double)A[i * lda + k];\n                double b = trans_b ? (double)B[j * ldb + k] : (double)B[k * ldb + j];\n                s += a * b;",
+                           "double a = (double)A[i * lda + k];\n                double b = trans_b ? (double)B[j * ldb + k] : (double)B[k * ldb + j];\n                s += a * b;"),
     "cells_trans_b_ignored": ("double b = trans_b ? (double)B[j * ldb + k] : (double)B[k * ldb + j];",
                               "double b = (double)B[k * ldb + j];"),
 }
@@ -115,6 +121,20 @@ def _battery():
     Wd = (codes - 1.5) * np.repeat(S.view(np.float16).astype(np.float64), 64, 1)[:, :K]
     y, _ = oracle.gemv_q2(_pack(codes), S, x)
     expect("q2_np", np.allclose(y, Wd @ x.astype(np.float64), rtol=0, atol=1e-12))
+
+    g = load("gemm_ex_tiny_2x3x2.txt")
+    ab = np.asarray(g["alpha_beta"], np.float64)[0]
+    out, bnd = oracle.gemm_ex(np.asarray(g["A"], np.float64).astype(np.float32),
+                              np.asarray(g["B"], np.float64).astype(np.float32),
+                              np.asarray(g["C"], np.float64).astype(np.float32), ab[0], ab[1])
+    expect("ex_tiny", np.array_equal(out, np.asarray(g["out"], np.float64)) and
+           np.array_equal(bnd, np.asarray(g["bound"], np.float64)))
+    At = inputs.uniform(rng, (9, 7))
+    Bt = inputs.uniform(rng, (9, 5))
+    Cn = np.full((7, 5), np.nan, np.float32)
+    out, _ = oracle.gemm_ex(At, Bt, Cn, 1.0, 0.0, trans_a=True)
+    expect("ex_ta_beta0", np.allclose(out, At.T.astype(np.float64) @ Bt.astype(np.float64),
+                                      rtol=0, atol=1e-12))
 
     g = load("q4_tiny_2x4.txt")
     y, _ = oracle.gemv_q4(np.array(g["Q"], np.uint8), np.array(g["S"], np.uint16),
