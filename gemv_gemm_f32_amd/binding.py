@@ -26,7 +26,7 @@ GG_ERR_ALIAS = -2
 GG_ERR_NO_DEVICE = -3
 GG_ERR_LAUNCH = -4
 
-ENTRY_POINTS = ("gemm_f32", "gemm_f32_tn", "gemm_f32_nt", "gemv_f32", "gemv_q2",
+ENTRY_POINTS = ("gemm_f32", "gemm_f32_tn", "gemm_f32_nt", "gemm_f32_ex", "gemv_f32", "gemv_q2",
                 "gemv_q2_batched", "gemv_q4", "gemv_q4_batched", "gg_strerror")
 
 _lib = None
@@ -63,6 +63,10 @@ def load(path: str = LIB_PATH):
         f = getattr(lib, name)
         f.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
         f.restype = ctypes.c_int
+    f32 = ctypes.c_float
+    lib.gemm_f32_ex.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, f32, vp, i64,
+                                vp, i64, f32, vp, i64, vp]
+    lib.gemm_f32_ex.restype = ctypes.c_int
     lib.gemv_f32.argtypes = [i64, i64, vp, i64, vp, vp, vp]
     lib.gemv_f32.restype = ctypes.c_int
     pp = ctypes.POINTER(ctypes.c_void_p)
@@ -171,6 +175,33 @@ def gemm_f32_nt(A, B, C=None, stream=None):
     if B.shape[1] != K:
         raise ValueError("inner dimensions differ")
     return _gemm("gemm_f32_nt", A, B, C, M, B.shape[0], K, stream)
+
+
+def gemm_f32_ex(A, B, C=None, alpha=1.0, beta=0.0, trans_a=False, trans_b=False,
+                stream=None):
+    """C = alpha * op(A).op(B) + beta * C in place (C is not read when beta
+    == 0; a new C is allocated when None, which needs beta == 0).  op(A) =
+    A^T when trans_a (A stored K x M), op(B) = B^T when trans_b."""
+    torch = _torch()
+    M = A.shape[1] if trans_a else A.shape[0]
+    K = A.shape[0] if trans_a else A.shape[1]
+    Kb = B.shape[1] if trans_b else B.shape[0]
+    N = B.shape[0] if trans_b else B.shape[1]
+    if K != Kb:
+        raise ValueError("inner dimensions differ")
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs C")
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if tuple(C.shape) != (M, N):
+        raise ValueError("C must be M x N")
+    pa, lda = _mat(A, torch.float32, "A")
+    pb, ldb = _mat(B, torch.float32, "B")
+    pc, ldc = _mat(C, torch.float32, "C")
+    _check(load().gemm_f32_ex(int(bool(trans_a)), int(bool(trans_b)), M, N, K, float(alpha),
+                              pa, lda, pb, ldb, float(beta), pc, ldc, _stream(stream)),
+           "gemm_f32_ex")
+    return C
 
 
 def gemv_f32(W, x, y=None, stream=None):

@@ -67,31 +67,32 @@ bool bad_ptr(const void *p, int64_t align) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? GG_OK : GG_ERR_LAUNCH; }
 
-int gemm_common(gg::GemmLayout layout, int64_t M, int64_t N, int64_t K, const float *A,
-                int64_t lda, const float *B, int64_t ldb, float *C, int64_t ldc,
+// op(A) = A^T when ta (A stored K x M), op(B) = B^T when tb (B stored N x K).
+int gemm_common(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha, const float *A,
+                int64_t lda, const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
                 gg_stream_t stream) {
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return GG_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return GG_OK;
-    // Stored shapes: A is M x K (NN, NT) or K x M (TN); B is K x N (NN, TN)
-    // or N x K (NT).
-    const bool ta = layout == gg::GemmLayout::TN, tb = layout == gg::GemmLayout::NT;
+    // A and B are read only when the product term is present.
+    const bool use_ab = K > 0 && alpha != 0.f;
     const int64_t a_rows = ta ? K : M, a_cols = ta ? M : K;
     const int64_t b_rows = tb ? N : K, b_cols = tb ? K : N;
     if (bad_ptr(C, 4)) return GG_ERR_INVALID_ARG;
-    if (K > 0 && (bad_ptr(A, 4) || bad_ptr(B, 4))) return GG_ERR_INVALID_ARG;
+    if (use_ab && (bad_ptr(A, 4) || bad_ptr(B, 4))) return GG_ERR_INVALID_ARG;
     if (ldc < N || ldc > kMaxDim) return GG_ERR_INVALID_ARG;
-    if (K > 0 && (lda < a_cols || ldb < b_cols || lda > kMaxDim || ldb > kMaxDim))
+    if (use_ab && (lda < a_cols || ldb < b_cols || lda > kMaxDim || ldb > kMaxDim))
         return GG_ERR_INVALID_ARG;
     const Span c = span(C, M, N, ldc, 4);
-    if (K > 0 && (overlaps(c, span(A, a_rows, a_cols, lda, 4)) ||
-                  overlaps(c, span(B, b_rows, b_cols, ldb, 4))))
+    if (use_ab && (overlaps(c, span(A, a_rows, a_cols, lda, 4)) ||
+                   overlaps(c, span(B, b_rows, b_cols, ldb, 4))))
         return GG_ERR_ALIAS;
     int cus = 0;
     if (int st = check_device(&cus)) return st;
     (void)hipGetLastError();   // clear a stale error so the check below is ours
-    return launch_status(gg::launch_gemm(layout, (int)M, (int)N, (int)K, A, lda, B, ldb, C,
-                                         ldc, cus, reinterpret_cast<hipStream_t>(stream)));
+    return launch_status(gg::launch_gemm(!ta, tb, (int)M, (int)N, use_ab ? (int)K : 0, alpha,
+                                         A, lda, B, ldb, beta, C, ldc, cus,
+                                         reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -100,17 +101,26 @@ extern "C" {
 
 int gemm_f32(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
              int64_t ldb, float *C, int64_t ldc, gg_stream_t stream) {
-    return gemm_common(gg::GemmLayout::NN, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return gemm_common(false, false, M, N, K, 1.f, A, lda, B, ldb, 0.f, C, ldc, stream);
 }
 
 int gemm_f32_tn(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
                 int64_t ldb, float *C, int64_t ldc, gg_stream_t stream) {
-    return gemm_common(gg::GemmLayout::TN, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return gemm_common(true, false, M, N, K, 1.f, A, lda, B, ldb, 0.f, C, ldc, stream);
 }
 
 int gemm_f32_nt(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
                 int64_t ldb, float *C, int64_t ldc, gg_stream_t stream) {
-    return gemm_common(gg::GemmLayout::NT, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return gemm_common(false, true, M, N, K, 1.f, A, lda, B, ldb, 0.f, C, ldc, stream);
+}
+
+int gemm_f32_ex(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, float alpha,
+                const float *A, int64_t lda, const float *B, int64_t ldb, float beta, float *C,
+                int64_t ldc, gg_stream_t stream) {
+    if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
+        return GG_ERR_INVALID_ARG;
+    return gemm_common(trans_a == 1, trans_b == 1, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                       stream);
 }
 
 int gemv_f32(int64_t M, int64_t K, const float *W, int64_t ldw, const float *x, float *y,

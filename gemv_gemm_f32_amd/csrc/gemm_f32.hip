@@ -43,6 +43,9 @@
 //    contiguous extent are multiples of 4 floats; otherwise scalar loads.
 //  * Edges: rows and columns past M or N are fetched clamped into the matrix
 //    and their results are never stored.
+//  * Epilogue: C = alpha * acc, plus beta * C when beta != 0 (C is not read
+//    otherwise).  With alpha = 1 and beta = 0 the stored value is the
+//    accumulator itself.
 //  * Tile order: workgroups are handed to the 8 XCDs round-robin, so the grid
 //    index is remapped to give each XCD a contiguous run of tiles, ordered in
 //    groups of 4 tile rows so that a run shares A row panels and B column
@@ -157,6 +160,13 @@ struct Operand {
     }
 };
 
+// One output cell: alpha * acc, plus beta * C when beta != 0.
+__device__ __forceinline__ void store_c(float *c, float acc, float alpha, float beta) {
+    float v = alpha * acc;
+    if (beta != 0.f) v = __builtin_fmaf(beta, *c, v);
+    *c = v;
+}
+
 // Grid index -> (tile row, tile column).
 __device__ __forceinline__ void tile_of(int bid, int nwg, int tiles_m, int tiles_n,
                                         int &tm, int &tn) {
@@ -177,8 +187,8 @@ __device__ __forceinline__ void tile_of(int bid, int nwg, int tiles_m, int tiles
 // (BM/64) x (BN/64) blocks of 32 x 32.
 template <int BM, int BN, int BK, bool AX, bool BX, int VA, int VB, bool FENCE = true>
 __global__ __launch_bounds__(THREADS) void gemm_f32_kernel(
-    int M, int N, int K, const float *__restrict__ A, int64_t lda,
-    const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
+    int M, int N, int K, float alpha, const float *__restrict__ A, int64_t lda,
+    const float *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
     int tiles_m, int tiles_n) {
     static_assert(BK % 8 == 0, "k walks in groups of 8");
     constexpr int WM = BM / 2, WN = BN / 2;        // wave tile
@@ -277,7 +287,7 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (row < M) C[(int64_t)row * ldc + col] = acc[i][j][r];
+                if (row < M) store_c(C + (int64_t)row * ldc + col, acc[i][j][r], alpha, beta);
             }
         }
 }
@@ -366,8 +376,8 @@ struct DirectOperand {
 
 template <int BM, int BN, bool AX, bool BX>
 __global__ __launch_bounds__(THREADS) void gemm_f32_direct(
-    int M, int N, int K, const float *__restrict__ A, int64_t lda,
-    const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
+    int M, int N, int K, float alpha, const float *__restrict__ A, int64_t lda,
+    const float *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
     int tiles_m, int tiles_n) {
     constexpr int BK = 32;
     constexpr int WM = BM / 2, WN = BN / 2;
@@ -480,17 +490,19 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_direct(
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (row < M) C[(int64_t)row * ldc + col] = acc[i][j][r];
+                if (row < M) store_c(C + (int64_t)row * ldc + col, acc[i][j][r], alpha, beta);
             }
         }
 }
 
 template <bool AX, bool BX, int BM, int BN>
-hipError_t launch_direct(int M, int N, int K, const float *A, int64_t lda, const float *B,
-                         int64_t ldb, float *C, int64_t ldc, hipStream_t s) {
+hipError_t launch_direct(int M, int N, int K, float alpha, const float *A, int64_t lda,
+                         const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
+                         hipStream_t s) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     hipLaunchKernelGGL((gemm_f32_direct<BM, BN, AX, BX>), dim3(tiles_m * tiles_n),
-                       dim3(THREADS), 0, s, M, N, K, A, lda, B, ldb, C, ldc, tiles_m, tiles_n);
+                       dim3(THREADS), 0, s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                       tiles_m, tiles_n);
     return hipGetLastError();
 }
 
@@ -498,12 +510,14 @@ constexpr int PROD_BK = 32;
 
 template <bool AX, bool BX, int VA, int VB, int BM = 128, int BN = 128, int BK = PROD_BK,
           bool FENCE = true>
-hipError_t launch_t(int M, int N, int K, const float *A, int64_t lda, const float *B,
-                    int64_t ldb, float *C, int64_t ldc, hipStream_t s) {
+hipError_t launch_t(int M, int N, int K, float alpha, const float *A, int64_t lda,
+                    const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
+                    hipStream_t s) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const int nwg = tiles_m * tiles_n;
-    hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, BK, AX, BX, VA, VB, FENCE>), dim3(nwg), dim3(THREADS),
-                       0, s, M, N, K, A, lda, B, ldb, C, ldc, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, BK, AX, BX, VA, VB, FENCE>), dim3(nwg),
+                       dim3(THREADS), 0, s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                       tiles_m, tiles_n);
     return hipGetLastError();
 }
 
@@ -511,13 +525,11 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 }  // namespace
 
-hipError_t launch_gemm(GemmLayout layout, int M, int N, int K, const float *A, int64_t lda,
-                       const float *B, int64_t ldb, float *C, int64_t ldc, int num_cus,
-                       hipStream_t s) {
+hipError_t launch_gemm(bool ax, bool bx, int M, int N, int K, float alpha, const float *A,
+                       int64_t lda, const float *B, int64_t ldb, float beta, float *C,
+                       int64_t ldc, int num_cus, hipStream_t s) {
     // 16-byte loads need the operand's contiguous extent, its leading
     // dimension and its base all to be multiples of 4 floats.
-    const bool ax = layout != GemmLayout::TN;     // A stored M x K
-    const bool bx = layout == GemmLayout::NT;     // B stored N x K
     const int a_contig = ax ? K : M;
     const int b_contig = bx ? K : N;
     const bool va = aligned16(A) && (lda % 4 == 0) && (a_contig % 4 == 0);
@@ -533,27 +545,27 @@ hipError_t launch_gemm(GemmLayout layout, int M, int N, int K, const float *A, i
     // (few output tiles) spread over the CUs.
     const int64_t tiles_128x64 = (int64_t)((M + 127) / 128) * ((N + 63) / 64);
     const bool big = tiles_128x64 >= 2 * (int64_t)num_cus;
-#define GG_GEMM_DIRECT(AX_, BX_)                                                         \
-    return big ? launch_direct<AX_, BX_, 128, 64>(M, N, K, A, lda, B, ldb, C, ldc, s) \
-               : launch_direct<AX_, BX_, 64, 64>(M, N, K, A, lda, B, ldb, C, ldc, s);
-#define GG_GEMM_SHAPE(AX_, BX_, VA_, VB_)                                                   \
-    return big ? launch_t<AX_, BX_, VA_, VB_, 128, 64>(M, N, K, A, lda, B, ldb, C, ldc, s) \
-               : launch_t<AX_, BX_, VA_, VB_, 64, 64>(M, N, K, A, lda, B, ldb, C, ldc, s);
+#define GG_ARGS M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s
+#define GG_GEMM_DIRECT(AX_, BX_)                                              \
+    return big ? launch_direct<AX_, BX_, 128, 64>(GG_ARGS)                 \
+               : launch_direct<AX_, BX_, 64, 64>(GG_ARGS);
+#define GG_GEMM_SHAPE(AX_, BX_, VA_, VB_)                                     \
+    return big ? launch_t<AX_, BX_, VA_, VB_, 128, 64>(GG_ARGS)            \
+               : launch_t<AX_, BX_, VA_, VB_, 64, 64>(GG_ARGS);
 #define GG_GEMM_CASE(AX_, BX_)                      \
     if (direct) { GG_GEMM_DIRECT(AX_, BX_) }        \
     if (va && vb) { GG_GEMM_SHAPE(AX_, BX_, 4, 4) } \
     if (va) { GG_GEMM_SHAPE(AX_, BX_, 4, 1) }       \
     if (vb) { GG_GEMM_SHAPE(AX_, BX_, 1, 4) }       \
     GG_GEMM_SHAPE(AX_, BX_, 1, 1)
-    switch (layout) {
-        case GemmLayout::NN: { GG_GEMM_CASE(true, false) }
-        case GemmLayout::TN: { GG_GEMM_CASE(false, false) }
-        case GemmLayout::NT: { GG_GEMM_CASE(true, true) }
-    }
+    if (ax && !bx) { GG_GEMM_CASE(true, false) }     // A.B
+    if (!ax && !bx) { GG_GEMM_CASE(false, false) }   // A^T.B
+    if (ax && bx) { GG_GEMM_CASE(true, true) }       // A.B^T
+    GG_GEMM_CASE(false, true)                        // A^T.B^T
 #undef GG_GEMM_CASE
 #undef GG_GEMM_SHAPE
 #undef GG_GEMM_DIRECT
-    return hipErrorInvalidValue;
+#undef GG_ARGS
 }
 
 }  // namespace gg

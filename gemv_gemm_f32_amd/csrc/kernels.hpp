@@ -11,13 +11,13 @@
 
 namespace gg {
 
-enum class GemmLayout { NN, TN, NT };
-
-// C = op(A).op(B) for the three layouts of gemvgemm.h; num_cus is the
-// device's compute-unit count (it picks the tile shape).
-hipError_t launch_gemm(GemmLayout layout, int M, int N, int K,
-                       const float *A, int64_t lda, const float *B, int64_t ldb,
-                       float *C, int64_t ldc, int num_cus, hipStream_t stream);
+// C = alpha * op(A).op(B) + beta * C (C not read when beta == 0).
+// ax: A stored M x K (else K x M, i.e. op(A) = A^T); bx: B stored N x K
+// (op(B) = B^T, else K x N).  num_cus is the device's compute-unit count (it
+// picks the tile shape).  K = 0 writes beta * C (zeros for beta = 0).
+hipError_t launch_gemm(bool ax, bool bx, int M, int N, int K, float alpha, const float *A,
+                       int64_t lda, const float *B, int64_t ldb, float beta, float *C,
+                       int64_t ldc, int num_cus, hipStream_t stream);
 
 // y = W.x, fp32.
 hipError_t launch_gemv_f32(int M, int K, const float *W, int64_t ldw,

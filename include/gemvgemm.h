@@ -95,6 +95,29 @@ int gemm_f32_nt(int64_t M, int64_t N, int64_t K,
                 float *C, int64_t ldc, gg_stream_t stream);
 
 /*
+ * C[M x N] = alpha * op(A) . op(B) + beta * C
+ *
+ * The scaled, accumulating form of the three products above, for gradient
+ * accumulation (dW += X^T.dY) in the hand-derived backward pass and AdamW
+ * training loop of "I built a GPT-2 in the browser, then made it
+ * 2.6x-12.1x faster", section "The architecture in 60 seconds".  The pages
+ * give no formula; this library reads it the BLAS way:
+ *   op(A) = A (stored M x K, A[i*lda + k], lda >= K)       if trans_a == 0,
+ *           A^T (stored K x M, A[k*lda + i], lda >= M)     if trans_a == 1;
+ *   op(B) = B (stored K x N, B[k*ldb + j], ldb >= N)       if trans_b == 0,
+ *           B^T (stored N x K, B[j*ldb + k], ldb >= K)     if trans_b == 1;
+ *   C[i*ldc + j], ldc >= N, read and written in place.
+ * beta == 0: C is not read (it may hold NaN).  alpha == 0 or K == 0: A and B
+ * are not read (they may be NULL) and C becomes beta * C.  trans flags other
+ * than 0 or 1 give GG_ERR_INVALID_ARG; C may not overlap A or B.  With
+ * alpha = 1 and beta = 0 the results equal gemm_f32 / _tn / _nt bit for bit.
+ */
+int gemm_f32_ex(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                float alpha, const float *A, int64_t lda,
+                const float *B, int64_t ldb, float beta,
+                float *C, int64_t ldc, gg_stream_t stream);
+
+/*
  * y[M] = W[M x K] . x[K]
  *
  * The single-row matrix-vector path kept beside the dense product ("More

@@ -144,7 +144,9 @@ void oracle_gemm_cells(int trans_a, int trans_b, int64_t K,
 /* C_out = alpha * op(A).op(B) + beta * C_in, one cell at a time:
  *   s  = sum_k opA(i,k) * opB(k,j), k = 0, 1, ..., K-1 (fp64)
  *   c  = alpha * s + beta * C_in[i*ldc + j]   (the C_in term only if beta != 0,
- *        so C_in is not read when beta == 0 and may hold anything)
+ *        so C_in is not read when beta == 0 and may hold anything; likewise
+ *        the product term only if alpha != 0 and K > 0, so A and B are then
+ *        not read)
  * with opA(i,k) = A[k*lda + i] if trans_a else A[i*lda + k] and
  *      opB(k,j) = B[j*ldb + k] if trans_b else B[k*ldb + j].
  * bound = |alpha| * sum_k |opA * opB| + |beta * C_in|.  C_out and bound are
@@ -157,13 +159,13 @@ void oracle_gemm_ex(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
     for (int64_t i = 0; i < M; ++i)
         for (int64_t j = 0; j < N; ++j) {
             double s = 0.0, t = 0.0;
-            for (int64_t k = 0; k < K; ++k) {
+            for (int64_t k = 0; alpha != 0.0 && k < K; ++k) {
                 double a = trans_a ? (double)A[k * lda + i] : (double)A[i * lda + k];
                 double b = trans_b ? (double)B[j * ldb + k] : (double)B[k * ldb + j];
                 s += a * b;
                 t += fabs(a * b);
             }
-            double c = alpha * s, u = fabs(alpha) * t;
+            double c = alpha != 0.0 ? alpha * s : 0.0, u = fabs(alpha) * t;
             if (beta != 0.0) {
                 double cin = beta * (double)C_in[i * ldc + j];
                 c += cin;

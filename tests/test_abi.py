@@ -116,6 +116,23 @@ def test_gemv_q2_validation():
     assert f(4, 100, PA, 25, PB, 2, PX, PB + 4, None) == bd.GG_ERR_ALIAS
 
 
+def test_gemm_ex_validation():
+    f = lib.gemm_f32_ex
+    # trans flags must be 0 or 1
+    assert f(2, 0, 4, 4, 4, 1.0, PA, 4, PB, 4, 0.0, PC, 4, None) == bd.GG_ERR_INVALID_ARG
+    assert f(0, -1, 4, 4, 4, 1.0, PA, 4, PB, 4, 0.0, PC, 4, None) == bd.GG_ERR_INVALID_ARG
+    # transposed A is K x M: lda >= M
+    assert f(1, 0, 8, 4, 4, 1.0, PA, 7, PB, 4, 0.0, PC, 4, None) == bd.GG_ERR_INVALID_ARG
+    # transposed B is N x K: ldb >= K
+    assert f(0, 1, 4, 8, 6, 1.0, PA, 6, PB, 5, 0.0, PC, 8, None) == bd.GG_ERR_INVALID_ARG
+    assert f(1, 1, 4, 4, 4, 1.0, PA, 4, PB, 4, 0.0, PA + 4, 4, None) == bd.GG_ERR_ALIAS
+    # alpha == 0: A and B are not read, so NULL operands are accepted
+    st = f(0, 0, 4, 4, 4, 0.0, None, 0, None, 0, 2.0, PC, 4, None)
+    assert st not in (bd.GG_ERR_ALIAS, bd.GG_ERR_INVALID_ARG)
+    assert f(0, 0, 4, 4, 4, 1.0, None, 4, PB, 4, 2.0, PC, 4, None) == bd.GG_ERR_INVALID_ARG
+    assert f(0, 0, 0, 4, 4, 1.0, None, 0, None, 0, 2.0, None, 0, None) == bd.GG_OK
+
+
 def test_gemv_q4_validation():
     f = lib.gemv_q4
     # K = 101: rows need ceil(101/2) = 51 bytes and ceil(101/64) = 2 scales

@@ -433,11 +433,13 @@ def test_gemm_ex_beta_zero_ignores_c():
 
 
 def test_gemm_ex_alpha_zero_scales_c_exactly():
-    A = inputs.uniform(RNG, (6, 5))
+    # alpha = 0: A and B are not read (NaN here), C is scaled exactly
+    A = np.full((6, 5), np.nan, np.float32)
     B = inputs.uniform(RNG, (5, 4))
     C = inputs.uniform(RNG, (6, 4))
-    out, _ = oracle.gemm_ex(A, B, C, 0.0, -2.0)
+    out, bound = oracle.gemm_ex(A, B, C, 0.0, -2.0)
     assert np.array_equal(out, -2.0 * C.astype(np.float64))
+    assert np.array_equal(bound, np.abs(2.0 * C.astype(np.float64)))
 
 
 def test_gemm_ex_integer_exact():

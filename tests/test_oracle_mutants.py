@@ -52,8 +52,8 @@ MUTANTS = {
     "q4_dot_drops_last": ("oracle_q4_unpack_row(i, K, Q, ldq, S, lds, w);\n        double s = 0.0, t = 0.0;\n        for (int64_t k = 0; k < K; ++k)",
                           "oracle_q4_unpack_row(i, K, Q, ldq, S, lds, w);\n        double s = 0.0, t = 0.0;\n        for (int64_t k = 0; k + 1 < K; ++k)"),
     "ex_bound_drops_beta": ("u += fabs(cin);", "u += 0.0;"),
-    "ex_beta_scales_product": ("double c = alpha * s, u = fabs(alpha) * t;",
-                               "double c = beta * s, u = fabs(alpha) * t;"),
+    "ex_beta_scales_product": ("double c = alpha != 0.0 ? alpha * s : 0.0, u = fabs(alpha) * t;",
+                               "double c = alpha != 0.0 ? beta * s : 0.0, u = fabs(alpha) * t;"),
     "ex_reads_c_when_beta_zero": ("if (beta != 0.0) {\n                double cin", "if (1) {\n                double cin"),
     "ex_trans_a_ignored": ("double a = trans_a ? (double)A[k * lda + i] : (double)A[i * lda + k];\n                double b = trans_b ? (double)B[j * ldb + k] : (double)B[k * ldb + j];\n                s += a * b;",
                            "double a = (double)A[i * lda + k];\n                double b = trans_b ? (double)B[j * ldb + k] : (double)B[k * ldb + j];\n                s += a * b;"),
