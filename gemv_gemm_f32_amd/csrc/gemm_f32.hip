@@ -8,10 +8,17 @@
 // (16 x 16 workgroup tiles, 4 x 4 register blocks); here the tile is shaped
 // for CDNA4 instead:
 //
-//  * One workgroup of 256 lanes (4 wave64s) owns a BM x BN tile of C (128 x 64
-//    or 64 x 64, picked per call from the grid size).  Each wave owns a
-//    quarter as 32 x 32 blocks of v_mfma_f32_32x32x2_f32, whose fp32
-//    accumulators stay in registers for the whole K walk.  The matrix core
+//  * A group of 4 wave64s owns a BM x BN tile of C (64 x 64 on the direct path;
+//    128 x 64 or 64 x 64 on the staged path, picked per call from the grid
+//    size).  Each wave owns a quarter as 32 x 32 blocks of
+//    v_mfma_f32_32x32x2_f32, whose fp32 accumulators stay in registers for
+//    the whole K walk.
+//  * Split K inside the workgroup (direct path): a workgroup holds KS = 1, 2
+//    or 4 such groups on one tile, group g taking k-slabs g, g + KS, ...
+//    through its own LDS stages; groups 1 .. KS-1 then hand their sums to
+//    group 0 through LDS, which adds them in group order.  Products with few
+//    output tiles (the K-heavy backward products, small squares) get 8 or 16
+//    waves per tile instead of 4, without a workspace or atomics.  The matrix core
 //    takes IEEE fp32 operands (no reduced-precision inputs) and accumulates
 //    in fp32.
 //  * Operand tiles are staged in LDS in k-slabs of BK = 32, double-buffered:
@@ -374,8 +381,12 @@ struct DirectOperand {
     }
 };
 
-template <int BM, int BN, bool AX, bool BX>
-__global__ __launch_bounds__(THREADS) void gemm_f32_direct(
+// KS groups of 4 waves split the k-slabs of one output tile: group g takes
+// slabs g, g + KS, g + 2 KS, ... through its own double-buffered stages.  At
+// the end groups 1 .. KS-1 hand their accumulators to group 0 through LDS,
+// which adds them in group order, so the sum is fixed for a given KS.
+template <int BM, int BN, bool AX, bool BX, int KS>
+__global__ __launch_bounds__(THREADS * KS) void gemm_f32_direct(
     int M, int N, int K, float alpha, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
     int tiles_m, int tiles_n) {
@@ -385,23 +396,28 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_direct(
     using OA = DirectOperand<BM, AX>;
     using OB = DirectOperand<BN, BX>;
     constexpr int STAGE = OA::STAGE + OB::STAGE;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+    constexpr int ACCW = IB * JB * 16;            // accumulator words per lane
+    static_assert(KS == 1 || (KS - 1) * THREADS * ACCW * 4 <= KS * 2 * STAGE,
+                  "the hand-over of partial sums must fit in the stages");
+    __shared__ __attribute__((aligned(1024))) char smem[KS * 2 * STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, wq = wave & 3;     // k-group, wave within the group
     const int h = lane >> 5, l32 = lane & 31;
     int tm, tn;
     tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
+    const int wm = (wq >> 1) * WM, wn = (wq & 1) * WN;
 
     OA oa;
     OB ob;
-    oa.init(lda, m0, M, lane, wave);
-    ob.init(ldb, n0, N, lane, wave);
+    oa.init(lda, m0, M, lane, wq);
+    ob.init(ldb, n0, N, lane, wq);
     const int exta = OA::extent(lda, M, K), extb = OB::extent(ldb, N, K);
-    auto stage_a = [&](int b) { return smem + b * STAGE; };
-    auto stage_b = [&](int b) { return smem + b * STAGE + OA::STAGE; };
+    char *const gsmem = smem + grp * 2 * STAGE;
+    auto stage_a = [&](int b) { return gsmem + b * STAGE; };
+    auto stage_b = [&](int b) { return gsmem + b * STAGE + OA::STAGE; };
     int aoff[IB][4], boff[JB][4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -420,64 +436,101 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_direct(
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int nk = (K + BK - 1) / BK;
-    if (nk > 0) {
-        oa.issue(stage_a(0), A, exta, lda, 0, wave);
-        ob.issue(stage_b(0), B, extb, ldb, 0, wave);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if (BK > K) {
-            oa.zero_tail(stage_a(0), 0, K, wave, lane);
-            ob.zero_tail(stage_b(0), 0, K, wave, lane);
+    const int rounds = (nk + KS - 1) / KS;        // the same for every group
+    if (rounds > 0) {
+        if (grp < nk) {
+            oa.issue(stage_a(0), A, exta, lda, grp * BK, wq);
+            ob.issue(stage_b(0), B, extb, ldb, grp * BK, wq);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (grp * BK + BK > K) {
+                oa.zero_tail(stage_a(0), grp * BK, K, wq, lane);
+                ob.zero_tail(stage_b(0), grp * BK, K, wq, lane);
+            }
         }
         __syncthreads();
     }
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        const int k1 = (kt + 1) * BK;
-        const bool more = kt + 1 < nk;
-        // slab kt+1 goes to the stage last read in slab kt-1, whose reads
-        // all finished before the previous barrier
-        if (more) {
-            oa.issue(stage_a(buf ^ 1), A, exta, lda, k1, wave);
-            ob.issue(stage_b(buf ^ 1), B, extb, ldb, k1, wave);
+    for (int r = 0; r < rounds; ++r) {
+        const int buf = r & 1;
+        const int kt = r * KS + grp;              // this group's slab in round r
+        const int kn = kt + KS;                   // and in round r + 1
+        const int k1 = kn * BK;
+        const bool more = r + 1 < rounds;
+        // slab kn goes to the stage last read in round r-1, whose reads all
+        // finished before the previous barrier
+        if (more && kn < nk) {
+            oa.issue(stage_a(buf ^ 1), A, exta, lda, k1, wq);
+            ob.issue(stage_b(buf ^ 1), B, extb, ldb, k1, wq);
         }
-        const char *as = stage_a(buf), *bs = stage_b(buf);
-        v4f fa[IB], fb[JB];
+        if (kt < nk) {
+            const char *as = stage_a(buf), *bs = stage_b(buf);
+            v4f fa[IB], fb[JB];
 #pragma unroll
-        for (int i = 0; i < IB; ++i) fa[i] = OA::frag(as, aoff[i][0]);
+            for (int i = 0; i < IB; ++i) fa[i] = OA::frag(as, aoff[i][0]);
 #pragma unroll
-        for (int j = 0; j < JB; ++j) fb[j] = OB::frag(bs, boff[j][0]);
+            for (int j = 0; j < JB; ++j) fb[j] = OB::frag(bs, boff[j][0]);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            v4f na[IB], nb[JB];
-#pragma unroll
-            for (int i = 0; i < IB; ++i) na[i] = g + 1 < 4 ? OA::frag(as, aoff[i][g + 1]) : fa[i];
-#pragma unroll
-            for (int j = 0; j < JB; ++j) nb[j] = g + 1 < 4 ? OB::frag(bs, boff[j][g + 1]) : fb[j];
-            // keep the next group's LDS reads ahead of this group's MFMAs
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int g = 0; g < 4; ++g) {
+                v4f na[IB], nb[JB];
 #pragma unroll
                 for (int i = 0; i < IB; ++i)
+                    na[i] = g + 1 < 4 ? OA::frag(as, aoff[i][g + 1]) : fa[i];
 #pragma unroll
-                    for (int j = 0; j < JB; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][t], fb[j][t],
-                                                                        acc[i][j], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
+                for (int j = 0; j < JB; ++j)
+                    nb[j] = g + 1 < 4 ? OB::frag(bs, boff[j][g + 1]) : fb[j];
+                // keep the next group's LDS reads ahead of this group's MFMAs
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < IB; ++i) fa[i] = na[i];
+                for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int j = 0; j < JB; ++j) fb[j] = nb[j];
+                    for (int i = 0; i < IB; ++i)
+#pragma unroll
+                        for (int j = 0; j < JB; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                                fa[i][t], fb[j][t], acc[i][j], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < IB; ++i) fa[i] = na[i];
+#pragma unroll
+                for (int j = 0; j < JB; ++j) fb[j] = nb[j];
+            }
         }
         if (more) {
             // the loads into LDS are tracked by vmcnt; the compiler does not
             // wait for them, so wait here before publishing the slab
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            if (k1 + BK > K) {
-                oa.zero_tail(stage_a(buf ^ 1), k1, K, wave, lane);
-                ob.zero_tail(stage_b(buf ^ 1), k1, K, wave, lane);
+            if (kn < nk && k1 + BK > K) {
+                oa.zero_tail(stage_a(buf ^ 1), k1, K, wq, lane);
+                ob.zero_tail(stage_b(buf ^ 1), k1, K, wq, lane);
             }
             __syncthreads();
+        }
+    }
+
+    if (KS > 1) {
+        // groups 1 .. KS-1 hand their sums to group 0 (word e of lane l of
+        // wave wq of group g at float index ((g-1)*4 + wq)*ACCW*64 + e*64 + l)
+        float *red = reinterpret_cast<float *>(smem);
+        __syncthreads();                          // every stage read is done
+        if (grp > 0) {
+            float *dst = red + ((grp - 1) * 4 + wq) * ACCW * 64 + lane;
+#pragma unroll
+            for (int i = 0; i < IB; ++i)
+#pragma unroll
+                for (int j = 0; j < JB; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dst[((i * JB + j) * 16 + r) * 64] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (grp > 0) return;
+#pragma unroll
+        for (int g = 1; g < KS; ++g) {
+            const float *src = red + ((g - 1) * 4 + wq) * ACCW * 64 + lane;
+#pragma unroll
+            for (int i = 0; i < IB; ++i)
+#pragma unroll
+                for (int j = 0; j < JB; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] += src[((i * JB + j) * 16 + r) * 64];
         }
     }
 
@@ -495,13 +548,13 @@ __global__ __launch_bounds__(THREADS) void gemm_f32_direct(
         }
 }
 
-template <bool AX, bool BX, int BM, int BN>
+template <bool AX, bool BX, int BM, int BN, int KS = 1>
 hipError_t launch_direct(int M, int N, int K, float alpha, const float *A, int64_t lda,
                          const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
                          hipStream_t s) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    hipLaunchKernelGGL((gemm_f32_direct<BM, BN, AX, BX>), dim3(tiles_m * tiles_n),
-                       dim3(THREADS), 0, s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+    hipLaunchKernelGGL((gemm_f32_direct<BM, BN, AX, BX, KS>), dim3(tiles_m * tiles_n),
+                       dim3(THREADS * KS), 0, s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                        tiles_m, tiles_n);
     return hipGetLastError();
 }
@@ -540,15 +593,22 @@ hipError_t launch_gemm(bool ax, bool bx, int M, int N, int K, float alpha, const
     };
     const bool direct = va && vb && K > 0 && extent(ax, M, lda, K) < (int64_t(1) << 31) &&
                         extent(bx, N, ldb, K) < (int64_t(1) << 31);
-    // Tile shape: 128 x 64 when that grid still gives every CU two tiles to
-    // interleave; otherwise 64 x 64, which keeps small and K-heavy products
-    // (few output tiles) spread over the CUs.
+    // Staged path: 128 x 64 tiles when that grid still gives every CU two
+    // tiles to interleave; otherwise 64 x 64, which keeps small and K-heavy
+    // products (few output tiles) spread over the CUs.
     const int64_t tiles_128x64 = (int64_t)((M + 127) / 128) * ((N + 63) / 64);
     const bool big = tiles_128x64 >= 2 * (int64_t)num_cus;
+    // Direct path: 64 x 64 tiles with the k-slabs split over KS groups of 4
+    // waves, 4 when there are no more tiles than CUs (each CU then runs one
+    // tile with 16 waves), else 2; fewer when K has too few slabs to share.
+    const int64_t tiles_64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
+    const int slabs = (K + 31) / 32;
+    const int ks = tiles_64 <= (int64_t)num_cus && slabs >= 8 ? 4 : (slabs >= 4 ? 2 : 1);
 #define GG_ARGS M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s
-#define GG_GEMM_DIRECT(AX_, BX_)                                              \
-    return big ? launch_direct<AX_, BX_, 128, 64>(GG_ARGS)                 \
-               : launch_direct<AX_, BX_, 64, 64>(GG_ARGS);
+#define GG_GEMM_DIRECT(AX_, BX_)                                                     \
+    return ks == 4 ? launch_direct<AX_, BX_, 64, 64, 4>(GG_ARGS)                  \
+           : ks == 2 ? launch_direct<AX_, BX_, 64, 64, 2>(GG_ARGS)                \
+                     : launch_direct<AX_, BX_, 64, 64, 1>(GG_ARGS);
 #define GG_GEMM_SHAPE(AX_, BX_, VA_, VB_)                                     \
     return big ? launch_t<AX_, BX_, VA_, VB_, 128, 64>(GG_ARGS)            \
                : launch_t<AX_, BX_, VA_, VB_, 64, 64>(GG_ARGS);
