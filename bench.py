@@ -25,8 +25,8 @@ launch over its average launch duration); the 2-bit GEMV's weight GB/s
 (codes + scales per call over its average duration) is in `q2_gemv`.  Both
 carry a roofline object.  `q2_gemv_batched` times the same tokens with each
 token's 40 products in one gemv_q2_batched launch; `q4_gemv` times the 4-bit
-product the same two ways, and `q2_gemv_transposed` the 2-bit product at the
-transposed 1,536 x 12,288 shape.  Before any number is
+product the same two ways, `q2_gemv_transposed` the 2-bit product at the
+transposed 1,536 x 12,288 shape, and `gemv_f32` the fp32 product.  Before any number is
 printed the outputs are checked against the CPU oracle on sampled cells; a
 failing kernel reports no speed.  `cpu_baseline` times the oracle itself on a bounded sample.
 """
@@ -59,6 +59,8 @@ Q4_WEIGHT_BYTES = Q4_CODE_BYTES + Q2_SCALE_BYTES   # 10,027,008
 Q4_ALG_BYTES = Q4_WEIGHT_BYTES + Q2_K * 4 + Q2_M * 4   # + x + y = 10,082,304
 Q4_ROTATION = 64                                   # 642 MB of codes+scales
 QT_M, QT_K = 1536, 12288                           # the transposed 2-bit shape
+F32_ROTATION = 8                                   # 604 MB of fp32 weights
+F32_ALG_BYTES = Q2_M * Q2_K * 4 + Q2_K * 4 + Q2_M * 4   # W + x + y = 75,552,768
 QT_ALG_BYTES = Q2_WEIGHT_BYTES + QT_K * 4 + QT_M * 4   # 5,363,712
 
 PEAK_FP32_MFMA_TFLOPS = 157.3      # MI355X dense fp32 matrix peak
@@ -296,6 +298,11 @@ def main():
         h4.update(S.tobytes())
         Q4d.append(torch.from_numpy(Q).to(dev))
         S4d.append(torch.from_numpy(S.view(np.int16)).to(dev))
+    # fp32 GEMV: 8 matrices of 12,288 x 1,536 (604 MB), the same x length
+    Wf = [torch.from_numpy(inputs.gemv_f32_weight(r)).to(dev) for r in range(F32_ROTATION)]
+    W0 = Wf[0].cpu().numpy()
+    xf = inputs.gemv_f32_x()
+    dxf = torch.from_numpy(xf).to(dev)
     # the transposed shape: 1,536 rows of 12,288 columns, same bytes per matrix
     xt = inputs.q2_x(QT_K)
     dxt = torch.from_numpy(xt).to(dev)
@@ -349,13 +356,16 @@ def main():
         rb, bb = oracle.gemv_q4(Qb, Sb, x)
         ok, worst, _ = oracle.check(dys[b].cpu().numpy(), rb, bb)
         q4b_ok, q4b_worst = q4b_ok and ok, max(q4b_worst, worst)
+    bd.gemv_f32(Wf[0], dxf, y=dy)
+    yfref, yfbound = oracle.gemv(W0, xf)
+    gf_ok, gf_worst, _ = oracle.check(dy.cpu().numpy(), yfref, yfbound)
     bd.gemv_q2(QTd[0], STd[0], dxt, y=dyt)
     ytref, ytbound = oracle.gemv_q2(QT0, ST0, xt)
     qt_ok, qt_worst, _ = oracle.check(dyt.cpu().numpy(), ytref, ytbound)
     log("parity: gemm worst %.3g, q2 worst %.3g, q2 batched worst %.3g, q4 worst %.3g, "
-        "q4 batched worst %.3g, q2 transposed worst %.3g (x 1e-4 bound)" %
+        "q4 batched worst %.3g, q2 transposed worst %.3g, gemv_f32 worst %.3g (x 1e-4 bound)" %
         (gemm_worst / 1e-4, q2_worst / 1e-4, qb_worst / 1e-4, q4_worst / 1e-4,
-         q4b_worst / 1e-4, qt_worst / 1e-4))
+         q4b_worst / 1e-4, qt_worst / 1e-4, gf_worst / 1e-4))
 
     if args.copy_calibration > 0:
         n = args.copy_calibration // 4
@@ -423,6 +433,11 @@ def main():
         bd.gemv_q2_batched([QTd[i] for i in idx], [STd[i] for i in idx],
                            [dxt] * CALLS_PER_TOKEN, ys=dyts)
 
+    def tokenf(t):
+        for c in range(CALLS_PER_TOKEN):
+            bd.gemv_f32(Wf[(t * CALLS_PER_TOKEN + c) % F32_ROTATION], dxf, y=dy)
+
+    tokf_graphs = [capture(lambda t=t: tokenf(t)) for t in range(n_tok)]
     tokt_graphs = [capture(lambda t=t: tokent(t)) for t in range(n_tok)]
     btokt_graphs = [capture(lambda t=t: tokent_batched(t)) for t in range(n_tok)]
     tok4_graphs = [capture(lambda t=t: token4(t)) for t in range(n_tok)]
@@ -499,6 +514,8 @@ def main():
     tokt_ms, n_qt, _ = timed(token_runner(tokt_graphs), args.warmup)
     btokt_ms, n_qtb, _ = timed(token_runner(btokt_graphs), args.warmup)
     qt_us = 1e3 * tokt_ms / n_qt
+    tokf_ms, n_gf, _ = timed(token_runner(tokf_graphs), args.warmup)
+    gf_us = 1e3 * tokf_ms / n_gf
     qtb_us = 1e3 * btokt_ms / n_qtb
     gemm_us = 1e3 * gemm_ms / n_gemm
     q2_us = 1e3 * tok_ms / n_q2
@@ -646,7 +663,24 @@ def main():
                 "frac": QT_ALG_BYTES / qtb_us / 1e3 / PEAK_HBM_GBS,
             },
         },
+        "gemv_f32": {
+            "metric": "fp32 GEMV GB/s at 12288x1536 (cold rotation over 8 matrices, 604 MB)",
+            "value": F32_ALG_BYTES / gf_us / 1e3 if gf_ok else None,
+            "unit": "GB/s",
+            "avg_launch_us": gf_us,
+            "roofline": {
+                "kernel": "gemv_f32 (12288x1536)",
+                "bound": "hbm",
+                "achieved": F32_ALG_BYTES / gf_us / 1e3,
+                "peak": PEAK_HBM_GBS,
+                "unit": "GB/s",
+                "frac": F32_ALG_BYTES / gf_us / 1e3 / PEAK_HBM_GBS,
+                "traffic": None,
+            },
+        },
         "parity": {"gemm_f32_2048": "pass" if gemm_ok else "FAIL",
+                   "gemv_f32": "pass" if gf_ok else "FAIL",
+                   "gemv_f32_worst_err_over_bound": gf_worst,
                    "gemv_q2_transposed": "pass" if qt_ok else "FAIL",
                    "q2_transposed_worst_err_over_bound": qt_worst,
                    "gemv_q4": "pass" if q4_ok else "FAIL",
@@ -665,7 +699,7 @@ def main():
         "wall_s_timed": t_wall,
     }
     print(json.dumps(out), flush=True)
-    return 0 if (gemm_ok and q2_ok and qb_ok and q4_ok and q4b_ok and qt_ok) else 1
+    return 0 if (gemm_ok and q2_ok and qb_ok and q4_ok and q4b_ok and qt_ok and gf_ok) else 1
 
 
 if __name__ == "__main__":
