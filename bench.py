@@ -202,11 +202,13 @@ def write_traffic(fetch_db, write_db):
              CALLS_PER_TOKEN * Q2_ALG_BYTES),
             (lambda n: n.startswith("gemv_packed_kernel<4, 32, 6,") and n.endswith(", 1>"),
              "traffic_gemv_q4_12288x1536.json", q2_srcs, Q4_ALG_BYTES),
-            (lambda n: n.startswith("gemv_packed_kernel<4, 32, 12,") and n.endswith(", 64>"),
+            (lambda n: n.startswith("gemv_packed_kernel<4, 32, 8,") and n.endswith(", 64>"),
              "traffic_gemv_q4_batched_12288x1536.json", q2_srcs,
              CALLS_PER_TOKEN * Q4_ALG_BYTES),
             (lambda n: n.startswith("gemv_packed_kernel<2, 256, 6,") and n.endswith(", 1>"),
-             "traffic_gemv_q2_1536x12288.json", q2_srcs, QT_ALG_BYTES)):
+             "traffic_gemv_q2_1536x12288.json", q2_srcs, QT_ALG_BYTES),
+            (lambda n: n.startswith("gemv_f32_kernel<1, 6, true>"),
+             "traffic_gemv_f32_12288x1536.json", ("gemv_f32.hip", "wave.hpp"), F32_ALG_BYTES)):
         k = [n for n in fetch if match(n)]
         if not k:
             continue
@@ -532,6 +534,8 @@ def main():
     q4_traffic = traffic_from_profile("traffic_gemv_q4_12288x1536.json", psha)
     q4b_traffic = traffic_from_profile("traffic_gemv_q4_batched_12288x1536.json", psha)
     qt_traffic = traffic_from_profile("traffic_gemv_q2_1536x12288.json", psha)
+    gf_traffic = traffic_from_profile("traffic_gemv_f32_12288x1536.json",
+                                      src_sha("gemv_f32.hip", "wave.hpp"))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -675,7 +679,7 @@ def main():
                 "peak": PEAK_HBM_GBS,
                 "unit": "GB/s",
                 "frac": F32_ALG_BYTES / gf_us / 1e3 / PEAK_HBM_GBS,
-                "traffic": None,
+                "traffic": gf_traffic,
             },
         },
         "parity": {"gemm_f32_2048": "pass" if gemm_ok else "FAIL",

@@ -346,8 +346,10 @@ __global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int6
 // A single product needs every SIMD busy: 6 rows per group of lanes gives
 // one wave per SIMD at 12,288 rows split 32 ways, or at 1,536 rows split 256
 // ways.  A batch has waves to spare, so each lane takes more rows and reuses
-// its x registers and unit sums longer.
-template <int BITS, int SPLIT, int NB, int RPL = (NB == 1 ? 6 : 12)>
+// its x registers and unit sums longer: 12 for 2-bit codes, 8 for 4-bit ones
+// (a sweep over 6..24 rows at 40 products of 12,288 x 1,536 put each width's
+// best there: 1.54 and 2.00 us per product).
+template <int BITS, int SPLIT, int NB, int RPL = (NB == 1 ? 6 : (BITS == 2 ? 12 : 8))>
 hipError_t launch_chunk(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
                         const uint16_t *const *S, int64_t lds, const float *const *x,
                         float *const *y, hipStream_t s) {
