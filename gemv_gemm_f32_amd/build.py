@@ -25,6 +25,8 @@ CFLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
     "-mcode-object-version=5",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the packed-weight GEMV multiplies binary16 subnormals: keep denormals
+    "-fno-gpu-flush-denormals-to-zero",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

@@ -27,24 +27,32 @@
 //    requested up front.
 //  * x: lane j keeps the 16 x values of each of its units in registers and
 //    reuses them for all RPL rows; x is 6 KiB and read from L2/L1.
-//  * Unpack: a shift and one and-or place two codes of a 32-bit word in the
-//    top fraction bits of a binary16 pair of 1.0 (bits 8-9 for 2-bit codes,
-//    6-9 for 4-bit), i.e. h = 1 + c / 2^b exactly for b-bit codes.  The
-//    multiply-add then reads h directly as a binary16 operand of
-//    v_fma_mix_f32, with x and the accumulator in fp32, so the product h*x is
-//    formed from exact operands.  With the zero point z = (2^b - 1) / 2 of
-//    the code-to-weight map w = (c - z) * s, per unit:
-//        a = -(1 + z / 2^b) X + sum h x = sum (c - z) x / 2^b,
-//    with X = sum x over the unit's columns, precomputed once per lane.  The
-//    row sum is y = 2^b * sum over units of s * a: about two instructions per
-//    weight, and one scale multiply per 16 weights.
-//  * Rounding: |c - z| >= 1/2, so sum |w x| >= s sum|x| / 2 over a unit.  A
-//    2-bit unit's chain starts at -(1 + z/4) X and its partial sums stay
-//    within 3.2 sum|x|: the fp32 error is below 2.5e-5 sum |w x|.  A 4-bit
-//    chain starts at zero and adds -(1 + z/16) X last, which keeps its
-//    partial sums within 1.94 sum|x| (started at -(1 + z/16) X they could
-//    reach 3.4 sum|x|, and the worst case would touch the 1e-4 bound): its
-//    error is below 6.5e-5 sum |w x|.  Both hold for any inputs.
+//  * Unpack: a code pair is masked out of its 32-bit word where it lies, one
+//    code in each 16-bit half, and the result read as two binary16 numbers.
+//    With the exponent field left at zero each half is a subnormal,
+//    h = c * 2^(pos - 24) exactly, for a code c at fraction bit pos; codes
+//    above bit 9 of a half are first shifted down by one shift per word.
+//    That is one v_and_b32 per two weights.  The multiply-add reads h
+//    directly as a binary16 operand of v_fma_mix_f32 (which converts
+//    subnormal binary16 operands exactly: the library is built without
+//    denormal flushing), with x and the accumulator in fp32.  Each x is
+//    scaled once per pass by 2^(K0 - pos) for the position pos its codes
+//    take, so every product is c * x * 2^(K0 - 24), formed from exact
+//    operands; K0 is 8 for 2-bit codes and 4 for 4-bit ones.  With the zero
+//    point z = (2^b - 1) / 2 of the code-to-weight map w = (c - z) * s,
+//    per unit:
+//        a = -z 2^(K0 - 24) X + sum h x' = 2^(K0 - 24) sum (c - z) x,
+//    with X = sum x over the unit's columns, precomputed once per lane and
+//    reused for every row.  The row sum is y = 2^(24 - K0) * sum over units
+//    of s * a: about 1.6 instructions per weight, and one scale multiply
+//    per 16 weights.
+//  * Rounding: a partial sum of a unit's chain is
+//    sum_{i<=n} (c_i - z) x_i - z sum_{i>n} x_i, within z sum|x|, and
+//    |c - z| >= 1/2, so sum |w x| >= s sum|x| / 2 over a unit.  The 17
+//    roundings of the chain and the 15 of X then keep the fp32 error below
+//    64 z 2^-24 sum |w x|: 6e-6 for 2-bit codes and 3e-5 for 4-bit ones, for
+//    any inputs whose scaled values and products stay normal fp32 numbers
+//    (|x| between 2^-100 and 2^100).
 //  * Reduction: the partial sums of a row are added within each wave with DPP
 //    and ds_swizzle (wave.hpp), without LDS or atomics; with SPLIT = 256 the
 //    four wave sums then meet in LDS and one lane adds them in wave order.
@@ -80,19 +88,23 @@ struct PackedPtrs {
     float *y[NB];
 };
 
-// Per-width constants of the unpack.
+// Per-width constants of the unpack.  Pair t of a word is code t of the low
+// half and code t + HALF of the high half, at the same bit of each half.
 template <int BITS>
 struct Codes {
     static constexpr int UW = BITS / 2;              // 32-bit words per unit
     static constexpr int CPD = 32 / BITS;            // codes per word
     static constexpr int HALF = CPD / 2;             // code pairs per word
-    static constexpr int TOP = 10 - BITS;            // fraction bit of the low code
     static constexpr unsigned FIELD = (1u << BITS) - 1u;
-    static constexpr unsigned MASK = (FIELD << TOP) | (FIELD << (TOP + 16));
-    static constexpr float INIT = -(1.f + (float)FIELD / 2.f / (float)(1 << BITS));
-    static constexpr float OUT = (float)(1 << BITS);
+    static constexpr int SH = BITS == 2 ? 6 : 8;     // shift for pairs above bit 9
+    static constexpr int K0 = BITS == 2 ? 8 : 4;     // x scaled by 2^(K0 - pos)
+    static constexpr float Z = (float)FIELD / 2.f;   // zero point
+    static constexpr float OUT = (float)(1 << (24 - K0));
+    // whether pair t is shifted down first, and its fraction bit after that
+    static constexpr bool shifted(int t) { return BITS * (t + 1) > 10; }
+    static constexpr int pos(int t) { return shifted(t) ? BITS * t - SH : BITS * t; }
+    static constexpr unsigned mask(int t) { return (FIELD << pos(t)) | (FIELD << (pos(t) + 16)); }
 };
-
 // The unit of 16 codes at unit index u of a row, as UW words: the fast
 // specialisation loads it whole; the generic one assembles it from bytes,
 // zeroing columns at or beyond K.
@@ -160,14 +172,6 @@ __global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int6
     float acc[RPL];
 #pragma unroll
     for (int m = 0; m < RPL; ++m) acc[m] = 0.f;
-
-    // Mask of the two code slots, and the binary16 pair (1.0, 1.0).  The
-    // empty asm pins both in VGPRs, so (sh & mask) | one is selected as one
-    // v_and_or_b32: gfx9 VOP3 forms take no literal operand, and with the
-    // constants left visible the compiler splits it into an AND and an OR.
-    unsigned mask = C::MASK, one = 0x3C003C00u;
-    asm volatile("" : "+v"(mask));
-    asm volatile("" : "+v"(one));
 
     for (int u0 = 0; u0 < units; u0 += UNITS_PER_PASS) {
         // ---- Loads.  Every load of a pass is issued first, unconditionally,
@@ -277,13 +281,18 @@ __global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int6
             }
         }
 
+        // ---- Per unit: X = sum x (unscaled) for the zero point, then each x
+        // scaled for the bit position its codes take.
         float init[UPL];
 #pragma unroll
         for (int q = 0; q < UPL; ++q) {
             float X = 0.f;
 #pragma unroll
             for (int p = 0; p < 16; ++p) X += xv[q][p];
-            init[q] = C::INIT * X;
+            init[q] = (-C::Z / C::OUT) * X;
+#pragma unroll
+            for (int p = 0; p < 16; ++p)
+                xv[q][p] *= (float)(1 << (C::K0 - C::pos((p % C::CPD) % C::HALF)));
         }
 
         // ---- Row by row; the UPL units of a row are independent
@@ -292,7 +301,7 @@ __global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int6
         for (int m = 0; m < RPL; ++m) {
             float a[UPL];
 #pragma unroll
-            for (int q = 0; q < UPL; ++q) a[q] = BITS == 2 ? init[q] : 0.f;
+            for (int q = 0; q < UPL; ++q) a[q] = init[q];
 #pragma unroll
             for (int i = 0; i < UW; ++i)
 #pragma unroll
@@ -300,19 +309,14 @@ __global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int6
 #pragma unroll
                     for (int q = 0; q < UPL; ++q) {
                         const unsigned d = craw[m][q][i];
-                        // codes t and t+HALF of the word moved to the top
-                        // fraction bits of the low and high halves
-                        const unsigned sh = BITS * t <= C::TOP ? (d << (C::TOP - BITS * t))
-                                                               : (d >> (BITS * t - C::TOP));
-                        const unsigned hb = (sh & mask) | one;
-                        const h2 hv = __builtin_bit_cast(h2, hb);
+                        const unsigned e = C::shifted(t) ? d >> C::SH : d;
+                        const h2 hv = __builtin_bit_cast(h2, e & C::mask(t));
                         a[q] = __builtin_fmaf((float)hv.x, xv[q][i * C::CPD + t], a[q]);
                         a[q] = __builtin_fmaf((float)hv.y, xv[q][i * C::CPD + t + C::HALF], a[q]);
                     }
                 }
 #pragma unroll
             for (int q = 0; q < UPL; ++q) {
-                if (BITS != 2) a[q] += init[q];
                 const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits[m][q]);
                 acc[m] = __builtin_fmaf(s, a[q], acc[m]);
             }
