@@ -175,9 +175,10 @@ __global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int6
 
     for (int u0 = 0; u0 < units; u0 += UNITS_PER_PASS) {
         // ---- Loads.  Every load of a pass is issued first, unconditionally,
-        // from clamped (always in-bounds) addresses: x, then codes and scales
-        // row by row, so that the rows can be consumed in the order their
-        // data arrives.  Predicated loads, or selects right after each load,
+        // from clamped (always in-bounds) addresses, unit by unit: a unit's x,
+        // then its codes and scale in every row.  The multiply-adds below run
+        // unit by unit across the rows too, so each unit's work can start as
+        // soon as its own data has arrived.  Predicated loads, or selects right after each load,
         // make the compiler wait for each load before issuing the next.  The
         // fast path addresses with 32-bit byte offsets from the base pointer.
         v4f xraw[UPL][4];
@@ -190,14 +191,12 @@ __global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int6
             const unsigned qb = (unsigned)row0 * (unsigned)ldq + (unsigned)(u0 + j) * UB;
             const unsigned sb = ((unsigned)row0 * (unsigned)lds + (unsigned)((u0 + j) >> 2)) * 2u;
 #pragma unroll
-            for (int q = 0; q < UPL; ++q)
+            for (int q = 0; q < UPL; ++q) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
                     xraw[q][c] = *reinterpret_cast<const v4f *>(xb + 64 * SPLIT * q + 16 * c);
 #pragma unroll
-            for (int m = 0; m < RPL; ++m)
-#pragma unroll
-                for (int q = 0; q < UPL; ++q) {
+                for (int m = 0; m < RPL; ++m) {
                     const char *qp = reinterpret_cast<const char *>(Q) + qb +
                                      (unsigned)m * (unsigned)ldq + (unsigned)(SPLIT * UB * q);
                     if (UW == 1) {
@@ -211,47 +210,46 @@ __global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int6
                         reinterpret_cast<const char *>(S) + sb + (unsigned)m * (unsigned)lds * 2u +
                         (unsigned)(SPLIT / 2 * q));
                 }
-        } else {
-#pragma unroll
-        for (int q = 0; q < UPL; ++q) {
-            const int ud = u0 + j + SPLIT * q;
-            const int udc = ud < units ? ud : units - 1;
-            if (FAST) {
-                const char *xb = reinterpret_cast<const char *>(x) + (unsigned)udc * 64u;
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    xraw[q][c] = *reinterpret_cast<const v4f *>(xb + 16 * c);
-            } else {
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int k = udc * 16 + 4 * c + e;
-                        xraw[q][c][e] = x[k < K ? k : K - 1];
-                    }
+                __builtin_amdgcn_sched_barrier(0);   // keep the unit order
             }
-        }
-#pragma unroll
-        for (int m = 0; m < RPL; ++m) {
-            const int row = row0 + m;
-            const int rowc = row < M ? row : row_last;
+        } else {
 #pragma unroll
             for (int q = 0; q < UPL; ++q) {
                 const int ud = u0 + j + SPLIT * q;
                 const int udc = ud < units ? ud : units - 1;
                 if (FAST) {
-                    const unsigned qo = (unsigned)rowc * (unsigned)ldq;
-                    const unsigned so = ((unsigned)rowc * (unsigned)lds + (unsigned)(udc >> 2)) * 2u;
-                    load_unit<BITS, true>(reinterpret_cast<const uint8_t *>(Q) + qo, udc, K,
-                                          craw[m][q]);
-                    sraw[m][q] = *reinterpret_cast<const uint16_t *>(
-                        reinterpret_cast<const char *>(S) + so);
+                    const char *xb = reinterpret_cast<const char *>(x) + (unsigned)udc * 64u;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        xraw[q][c] = *reinterpret_cast<const v4f *>(xb + 16 * c);
                 } else {
-                    load_unit<BITS, false>(Q + (int64_t)rowc * ldq, udc, K, craw[m][q]);
-                    sraw[m][q] = S[(int64_t)rowc * lds + (udc >> 2)];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int k = udc * 16 + 4 * c + e;
+                            xraw[q][c][e] = x[k < K ? k : K - 1];
+                        }
                 }
+#pragma unroll
+                for (int m = 0; m < RPL; ++m) {
+                    const int row = row0 + m;
+                    const int rowc = row < M ? row : row_last;
+                    if (FAST) {
+                        const unsigned qo = (unsigned)rowc * (unsigned)ldq;
+                        const unsigned so =
+                            ((unsigned)rowc * (unsigned)lds + (unsigned)(udc >> 2)) * 2u;
+                        load_unit<BITS, true>(reinterpret_cast<const uint8_t *>(Q) + qo, udc, K,
+                                              craw[m][q]);
+                        sraw[m][q] = *reinterpret_cast<const uint16_t *>(
+                            reinterpret_cast<const char *>(S) + so);
+                    } else {
+                        load_unit<BITS, false>(Q + (int64_t)rowc * ldq, udc, K, craw[m][q]);
+                        sraw[m][q] = S[(int64_t)rowc * lds + (udc >> 2)];
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);   // keep the unit order
             }
-        }
         }
         __builtin_amdgcn_sched_barrier(0);
 
@@ -281,45 +279,39 @@ __global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int6
             }
         }
 
-        // ---- Per unit: X = sum x (unscaled) for the zero point, then each x
-        // scaled for the bit position its codes take.
-        float init[UPL];
+        // ---- Unit by unit, in the order the loads were issued: X = sum x
+        // (unscaled) for the zero point, each x scaled for the bit position
+        // its codes take, then one multiply-add chain per row; the RPL rows'
+        // chains are independent and interleave.
 #pragma unroll
         for (int q = 0; q < UPL; ++q) {
             float X = 0.f;
 #pragma unroll
             for (int p = 0; p < 16; ++p) X += xv[q][p];
-            init[q] = (-C::Z / C::OUT) * X;
+            const float init = (-C::Z / C::OUT) * X;
 #pragma unroll
             for (int p = 0; p < 16; ++p)
                 xv[q][p] *= (float)(1 << (C::K0 - C::pos((p % C::CPD) % C::HALF)));
-        }
-
-        // ---- Row by row; the UPL units of a row are independent
-        // multiply-add chains, interleaved step by step.
 #pragma unroll
-        for (int m = 0; m < RPL; ++m) {
-            float a[UPL];
+            for (int m = 0; m < RPL; ++m) {
+                float a = init;
 #pragma unroll
-            for (int q = 0; q < UPL; ++q) a[q] = init[q];
+                for (int i = 0; i < UW; ++i)
 #pragma unroll
-            for (int i = 0; i < UW; ++i)
-#pragma unroll
-                for (int t = 0; t < C::HALF; ++t) {
-#pragma unroll
-                    for (int q = 0; q < UPL; ++q) {
+                    for (int t = 0; t < C::HALF; ++t) {
                         const unsigned d = craw[m][q][i];
                         const unsigned e = C::shifted(t) ? d >> C::SH : d;
                         const h2 hv = __builtin_bit_cast(h2, e & C::mask(t));
-                        a[q] = __builtin_fmaf((float)hv.x, xv[q][i * C::CPD + t], a[q]);
-                        a[q] = __builtin_fmaf((float)hv.y, xv[q][i * C::CPD + t + C::HALF], a[q]);
+                        a = __builtin_fmaf((float)hv.x, xv[q][i * C::CPD + t], a);
+                        a = __builtin_fmaf((float)hv.y, xv[q][i * C::CPD + t + C::HALF], a);
                     }
-                }
-#pragma unroll
-            for (int q = 0; q < UPL; ++q) {
                 const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits[m][q]);
-                acc[m] = __builtin_fmaf(s, a[q], acc[m]);
+                acc[m] = __builtin_fmaf(s, a, acc[m]);
             }
+            // A single product runs one wave per SIMD: keep the units apart so
+            // that each waits only for its own data.  (In a batch the scheduler
+            // interleaves them within the register budget of three waves.)
+            if (NB == 1) __builtin_amdgcn_sched_barrier(0);
         }
     }
 
