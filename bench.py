@@ -29,6 +29,10 @@ product the same two ways, `q2_gemv_transposed` the 2-bit product at the
 transposed 1,536 x 12,288 shape, and `gemv_f32` the fp32 product.  Before any number is
 printed the outputs are checked against the CPU oracle on sampled cells; a
 failing kernel reports no speed.  `cpu_baseline` times the oracle itself on a bounded sample.
+After the main timing, `spread` gives each kernel's per-launch median, p10,
+p90 and minimum over 16 single replays, and `context` the 2-bit GEMV on one
+cache-resident matrix (its launch-and-compute floor) and the rate of a plain
+device-to-device copy.
 """
 from __future__ import annotations
 
@@ -133,6 +137,17 @@ def cpu_baseline(A, B, Q, S, x, budget_s=12.0):
         "q2_gemv_weight_gbs": Q2_WEIGHT_BYTES / tq / 1e9,
         "cpu": platform.processor() or platform.machine(),
     }
+
+
+def host_cpu():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def _short_name(kernel):
@@ -465,6 +480,23 @@ def main():
             t = time.perf_counter() - t
         return e0.elapsed_time(e1), n, t
 
+    def spread(graphs, launches, n=16):
+        """Per-launch durations over n single replays of graphs (run after the
+        main timing, one event pair per replay): median, p10, p90, min in us."""
+        with torch.cuda.stream(stream):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+            ev[0].record(stream)
+            for k in range(n):
+                graphs[k % len(graphs)].replay()
+                ev[k + 1].record(stream)
+            stream.synchronize()
+        us = sorted(1e3 * ev[k].elapsed_time(ev[k + 1]) / launches for k in range(n))
+        q = lambda f: us[min(n - 1, int(round(f * (n - 1))))]
+        return {"median_us": q(0.5), "p10_us": q(0.1), "p90_us": q(0.9), "min_us": us[0],
+                "replays": n, "launches_per_replay": launches,
+                "note": ("an event pair per replay: medians run a few percent above "
+                         "the uninterrupted back-to-back averages")}
+
     def run_steps(i):
         if i is not None:
             step_graphs[i % n_tok].replay()
@@ -521,6 +553,39 @@ def main():
     qtb_us = 1e3 * btokt_ms / n_qtb
     gemm_us = 1e3 * gemm_ms / n_gemm
     q2_us = 1e3 * tok_ms / n_q2
+
+    # ---- context, after the main timing: the spread of per-launch times,
+    #      the 2-bit GEMV with one cache-resident matrix ("hot"), and what a
+    #      plain device-to-device copy streams on this GPU.
+    spreads = {
+        "gemm_f32": spread([gemm_graph], gemms_per_replay),
+        "gemv_q2": spread(tok_graphs, CALLS_PER_TOKEN),
+        "gemv_q2_batched": spread(btok_graphs, CALLS_PER_TOKEN),
+        "gemv_q4": spread(tok4_graphs, CALLS_PER_TOKEN),
+        "gemv_q4_batched": spread(btok4_graphs, CALLS_PER_TOKEN),
+        "gemv_q2_transposed": spread(tokt_graphs, CALLS_PER_TOKEN),
+        "gemv_q2_transposed_batched": spread(btokt_graphs, CALLS_PER_TOKEN),
+        "gemv_f32": spread(tokf_graphs, CALLS_PER_TOKEN),
+    }
+    hot_graph = capture(lambda: [bd.gemv_q2(Qd[0], Sd[0], dx, y=dy)
+                                 for _ in range(CALLS_PER_TOKEN)])
+    hot_ms, n_hot, _ = timed(token_runner([hot_graph] * n_tok), args.warmup)
+    q2_hot_us = 1e3 * hot_ms / n_hot
+    del hot_graph
+    copy_bytes = 1 << 30
+    csrc = torch.empty(copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    cdst = torch.empty_like(csrc)
+    with torch.cuda.stream(stream):
+        cdst.copy_(csrc)
+        stream.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            cdst.copy_(csrc)
+        e1.record(stream)
+        stream.synchronize()
+    copy_gbs = 2 * copy_bytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del csrc, cdst
 
     gemm_tflops = GEMM_FLOPS / gemm_us / 1e6
     q2_gbs = Q2_WEIGHT_BYTES / q2_us / 1e3
@@ -682,6 +747,15 @@ def main():
                 "traffic": gf_traffic,
             },
         },
+        "spread": spreads,
+        "context": {
+            "q2_gemv_hot_us": q2_hot_us,
+            "q2_gemv_hot_note": ("gemv_q2 12288x1536 on one matrix, 40 back-to-back calls: "
+                                 "weights resident in cache, the launch-and-compute floor"),
+            "hbm_copy_gbs": copy_gbs,
+            "hbm_copy_note": ("torch device-to-device copy of 1 GiB, 10 times, "
+                              "read + write bytes / time: what plain streaming reaches"),
+        },
         "parity": {"gemm_f32_2048": "pass" if gemm_ok else "FAIL",
                    "gemv_f32": "pass" if gf_ok else "FAIL",
                    "gemv_f32_worst_err_over_bound": gf_worst,
@@ -699,7 +773,9 @@ def main():
         "cpu_baseline": cpu,
         "inputs_sha256": hashes,
         "device": {"name": prop.name, "arch": getattr(prop, "gcnArchName", None),
-                   "cus": prop.multi_processor_count},
+                   "cus": prop.multi_processor_count, "torch": torch.__version__,
+                   "hip": getattr(torch.version, "hip", None), "host_cpu": host_cpu(),
+                   "host_cores_usable": len(os.sched_getaffinity(0))},
         "wall_s_timed": t_wall,
     }
     print(json.dumps(out), flush=True)
