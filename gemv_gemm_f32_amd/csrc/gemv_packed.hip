@@ -339,6 +339,224 @@ __global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int6
     }
 }
 
+// ---------------------------------------------------------------------------
+// Flat split.  A workgroup of three waves (192 lanes) reads a block of RPS
+// consecutive rows per step, lane f taking 16-byte chunk f of the block.
+// When a row holds CPR chunks and CPR divides 192 (RPS = 192 / CPR), lane f
+// always lands on chunk f mod CPR of row f / CPR: its columns -- and the x
+// values, position scales and unit sums that go with them -- are the same at
+// every step, so they are set up once per workgroup.  Each load instruction
+// then covers 1 KiB of weights, contiguous when rows are (ldq equal to the
+// row width), and each scale load 128 contiguous bytes.  A chunk is one scale
+// group of 2-bit codes or half a group of 4-bit codes, so a lane needs one
+// scale per chunk.  Per chunk the lane forms the UPC unit chains of the
+// unpack above, adds them in unit order and applies the scale; the CPR
+// partial sums of a row meet in LDS, where one lane adds them in chunk order.
+// The order is fixed for a given shape, so results repeat bit for bit.
+constexpr int FLAT_THREADS = 192;
+constexpr int FLAT_MIN_CPR = 8, FLAT_MAX_CPR = 48;
+
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+
+// Cache policy of the code loads: non-temporal (each code byte is read once).
+constexpr int NT = 2;
+
+// T steps per workgroup; a batch asks for four waves per SIMD (at most 128
+// VGPRs), which fits five three-wave workgroups on a compute unit.
+template <int BITS, int T, int NB>
+__global__ __launch_bounds__(FLAT_THREADS) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 1 : 4)))
+void gemv_packed_flat(int M, int cpr, int rdiv, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
+    using C = Codes<BITS>;
+    constexpr int CC = 128 / BITS;            // codes per 16-byte chunk
+    constexpr int UPC = CC / 16;              // units of 16 codes per chunk
+    constexpr int CPG = 64 / CC;              // chunks per 64-column scale group
+    constexpr int UW = C::UW;
+    constexpr int XP = CC + 4;                // LDS floats per chunk of scaled x (padded)
+    constexpr int MAX_RPS = FLAT_THREADS / FLAT_MIN_CPR;
+    __shared__ __attribute__((aligned(16))) float xs[FLAT_MAX_CPR * XP];
+    __shared__ float xi[FLAT_MAX_CPR * UPC];
+    __shared__ __attribute__((aligned(16))) float part[T * (FLAT_THREADS + 4 * MAX_RPS)];
+
+    const int b = NB == 1 ? 0 : (int)blockIdx.y;
+    const uint8_t *__restrict__ Q = ptrs.Q[b];
+    const uint16_t *__restrict__ S = ptrs.S[b];
+    const float *__restrict__ x = ptrs.x[b];
+    float *__restrict__ y = ptrs.y[b];
+    const int f = threadIdx.x;
+    const int rps = FLAT_THREADS / cpr;       // rows per step
+    const int rin = (f * rdiv) >> 16, c = f - rin * cpr;   // f / cpr (rdiv = ceil(2^16 / cpr))
+    const int row0 = (int)blockIdx.x * rps * T;
+    const int ps = cpr + 4;                   // LDS floats per row of partial sums
+
+    // ---- Set-up, one unit of 16 columns per lane: the chain start
+    // -z 2^(K0-24) X and the x values scaled for their codes' bit positions.
+    if (f < cpr * UPC) {
+        const v4f *xp = reinterpret_cast<const v4f *>(x) + 4 * f;
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const v4f t = xp[q];
+            v[4 * q] = t.x;
+            v[4 * q + 1] = t.y;
+            v[4 * q + 2] = t.z;
+            v[4 * q + 3] = t.w;
+        }
+        float X = 0.f;
+#pragma unroll
+        for (int p = 0; p < 16; ++p) X += v[p];
+        xi[f] = (-C::Z / C::OUT) * X;
+        float *dst = xs + (f / UPC) * XP + 16 * (f % UPC);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            v4f t;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                t[e] = v[4 * q + e] * (float)(1 << (C::K0 - C::pos(((4 * q + e) % C::CPD) % C::HALF)));
+            *reinterpret_cast<v4f *>(dst + 4 * q) = t;
+        }
+    }
+    __syncthreads();
+    float xv[CC];
+    float init[UPC];
+#pragma unroll
+    for (int q = 0; q < CC / 4; ++q) {
+        const v4f t = *reinterpret_cast<const v4f *>(xs + c * XP + 4 * q);
+        xv[4 * q] = t.x;
+        xv[4 * q + 1] = t.y;
+        xv[4 * q + 2] = t.z;
+        xv[4 * q + 3] = t.w;
+    }
+#pragma unroll
+    for (int i = 0; i < UPC; ++i) init[i] = xi[c * UPC + i];
+
+    // ---- Loads: every chunk and scale of the T steps, issued step by step
+    // before any is used.  The buffer resources start at the workgroup's
+    // first row and end at the matrix's last byte, so rows past M read zeros
+    // (they are never stored).
+    unsigned craw[T][4];
+    unsigned sraw[T];
+#if defined(__HIP_DEVICE_COMPILE__)
+    {
+        const int rows_left = M - row0;       // >= 1
+        const int extq = (int)((int64_t)(rows_left - 1) * ldq + 16 * cpr);
+        const int exts = (int)(((int64_t)(rows_left - 1) * lds + (cpr + CPG - 1) / CPG) * 2);
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(Q + (int64_t)row0 * ldq), (short)0, extq, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(S + (int64_t)row0 * lds), (short)0, exts, 0x00020000);
+        const unsigned vq = (unsigned)rin * (unsigned)ldq + 16u * (unsigned)c;
+        const unsigned vs = ((unsigned)rin * (unsigned)lds + (unsigned)(c / CPG)) * 2u;
+        const unsigned sq = (unsigned)rps * (unsigned)ldq;
+        const unsigned ss = (unsigned)rps * (unsigned)lds * 2u;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const u4 v = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(vq + t * sq), 0, NT);
+            craw[t][0] = v.x;
+            craw[t][1] = v.y;
+            craw[t][2] = v.z;
+            craw[t][3] = v.w;
+            sraw[t] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(vs + t * ss), 0, 0);
+            __builtin_amdgcn_sched_barrier(0);   // keep the step order
+        }
+    }
+#else
+    for (int t = 0; t < T; ++t) {
+        craw[t][0] = craw[t][1] = craw[t][2] = craw[t][3] = 0u;
+        sraw[t] = 0u;
+    }
+#endif
+
+    // ---- Step by step, in the order of the loads: the unit chains of the
+    // chunk, their sum in unit order, times the chunk's scale, into LDS.
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        float a[UPC];
+#pragma unroll
+        for (int i = 0; i < UPC; ++i) {
+            a[i] = init[i];
+#pragma unroll
+            for (int w = 0; w < UW; ++w)
+#pragma unroll
+                for (int h = 0; h < C::HALF; ++h) {
+                    const unsigned d = craw[t][i * UW + w];
+                    const unsigned e = C::shifted(h) ? d >> C::SH : d;
+                    const h2 hv = __builtin_bit_cast(h2, e & C::mask(h));
+                    a[i] = __builtin_fmaf((float)hv.x, xv[16 * i + w * C::CPD + h], a[i]);
+                    a[i] = __builtin_fmaf((float)hv.y, xv[16 * i + w * C::CPD + h + C::HALF], a[i]);
+                }
+        }
+        float p = a[0];
+#pragma unroll
+        for (int i = 1; i < UPC; ++i) p += a[i];
+        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sraw[t]);
+        part[(t * rps + rin) * ps + c] = s * p;
+        if (NB == 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+
+    // ---- One lane per row adds the row's partial sums in chunk order.
+    const int nrows = rps * T;
+    for (int r = f; r < nrows; r += FLAT_THREADS) {
+        if (row0 + r >= M) break;
+        const float *pr = part + r * ps;
+        float sum = 0.f;
+        for (int q = 0; q < cpr; q += 4) {
+            const v4f v = *reinterpret_cast<const v4f *>(pr + q);
+            sum += v.x;
+            sum += v.y;
+            sum += v.z;
+            sum += v.w;
+        }
+        y[row0 + r] = C::OUT * sum;
+    }
+}
+
+// Chunks per row for the flat split, or 0 where it does not apply: every row
+// a whole number of 16-byte chunks (K a multiple of 64), between 8 and 48
+// chunks dividing 192, chunk-aligned rows and bases, 16-byte aligned x, and
+// byte offsets within 31 bits.
+template <int BITS>
+int flat_cpr(int count, int M, int K, const uint8_t *const *Q, int64_t ldq, int64_t lds,
+             const float *const *x) {
+    if (K % 64 != 0 || ldq % 16 != 0) return 0;
+    const int cpr = K * BITS / 128;
+    if (cpr < FLAT_MIN_CPR || cpr > FLAT_MAX_CPR || FLAT_THREADS % cpr != 0) return 0;
+    if ((int64_t)M * ldq >= (int64_t(1) << 31) || (int64_t)M * lds * 2 >= (int64_t(1) << 31))
+        return 0;
+    for (int i = 0; i < count; ++i)
+        if (reinterpret_cast<uintptr_t>(Q[i]) % 16 != 0 ||
+            reinterpret_cast<uintptr_t>(x[i]) % 16 != 0)
+            return 0;
+    return cpr;
+}
+
+// Steps per workgroup.  A single product needs many workgroups to fill the
+// chip: one step (2-bit) or four (4-bit), whose rows are twice as long.  A
+// batch has workgroups to spare: eight steps.  (A sweep of 1, 2 and 4 steps
+// for single products and 4 to 16 for batches of 40 at 12,288 x 1,536 put
+// the best there.)
+template <int BITS, int NB, int T = (NB == 1 ? (BITS == 2 ? 1 : 4) : 8)>
+hipError_t launch_flat(int count, int M, int cpr, const uint8_t *const *Q, int64_t ldq,
+                       const uint16_t *const *S, int64_t lds, const float *const *x,
+                       float *const *y, hipStream_t s) {
+    const int rows_per_wg = FLAT_THREADS / cpr * T;
+    const dim3 grid((M + rows_per_wg - 1) / rows_per_wg, count);
+    PackedPtrs<NB> p;
+    for (int b = 0; b < NB; ++b) {
+        const int i = b < count ? b : 0;
+        p.Q[b] = Q[i];
+        p.S[b] = S[i];
+        p.x[b] = x[i];
+        p.y[b] = y[i];
+    }
+    // f / cpr as (f * rdiv) >> 16 is exact for f < 192 and cpr <= 48: the
+    // rounding excess f * (rdiv - 2^16 / cpr) / 2^16 stays below 1 / cpr.
+    const int rdiv = (65536 + cpr - 1) / cpr;
+    hipLaunchKernelGGL((gemv_packed_flat<BITS, T, NB>), grid, dim3(FLAT_THREADS), 0, s, M, cpr,
+                       rdiv, ldq, lds, p);
+    return hipGetLastError();
+}
+
 // A single product needs every SIMD busy: 6 rows per group of lanes gives
 // one wave per SIMD at 12,288 rows split 32 ways, or at 1,536 rows split 256
 // ways.  A batch has waves to spare, so each lane takes more rows and reuses
@@ -392,6 +610,8 @@ template <int BITS, int NB>
 hipError_t launch_split(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
                         const uint16_t *const *S, int64_t lds, const float *const *x,
                         float *const *y, hipStream_t s) {
+    const int cpr = flat_cpr<BITS>(count, M, K, Q, ldq, lds, x);
+    if (cpr) return launch_flat<BITS, NB>(count, M, cpr, Q, ldq, S, lds, x, y, s);
     return deep_split(M, K)
                ? launch_chunk<BITS, THREADS, NB>(count, M, K, Q, ldq, S, lds, x, y, s)
                : launch_chunk<BITS, 32, NB>(count, M, K, Q, ldq, S, lds, x, y, s);
