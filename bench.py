@@ -63,7 +63,7 @@ Q4_WEIGHT_BYTES = Q4_CODE_BYTES + Q2_SCALE_BYTES   # 10,027,008
 Q4_ALG_BYTES = Q4_WEIGHT_BYTES + Q2_K * 4 + Q2_M * 4   # + x + y = 10,082,304
 Q4_ROTATION = 64                                   # 642 MB of codes+scales
 QT_M, QT_K = 1536, 12288                           # the transposed 2-bit shape
-F32_ROTATION = 8                                   # 604 MB of fp32 weights
+F32_ROTATION = 48                                  # 3.375 GiB of fp32 weights
 F32_ALG_BYTES = Q2_M * Q2_K * 4 + Q2_K * 4 + Q2_M * 4   # W + x + y = 75,552,768
 QT_ALG_BYTES = Q2_WEIGHT_BYTES + QT_K * 4 + QT_M * 4   # 5,363,712
 
@@ -173,10 +173,8 @@ def summarize_trace(db_path):
     return "\n".join(lines)
 
 
-def _counter_per_kernel(db_path, counter):
-    """Per kernel name: the counter summed over its instances within each
-    dispatch, then the median over dispatches; for copy kernels, the largest
-    dispatch (the calibration copy dwarfs the input uploads)."""
+def _counter_dispatches(db_path, counter):
+    """Per kernel name: {dispatch id: the counter summed over its instances}."""
     import sqlite3
     db = sqlite3.connect(db_path)
     rows = db.execute("select kernel_name, dispatch_id, value from counters_collection "
@@ -185,24 +183,32 @@ def _counter_per_kernel(db_path, counter):
     for name, disp, v in rows:
         per.setdefault(_short_name(name), {}).setdefault(disp, 0.0)
         per[_short_name(name)][disp] += v
-    out = {}
-    for k, v in per.items():
-        vals = list(v.values())
-        out[k] = float(max(vals) if "copyBuffer" in k else np.median(vals))
-    return out
+    return per
+
+
+def _median_per_kernel(per):
+    return {k: float(np.median(list(v.values()))) for k, v in per.items()}
 
 
 def write_traffic(fetch_db, write_db):
     """HBM bytes per launch of the GEMM and the 2-bit GEMV: FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch, median over dispatches), each scaled by
     what the same counter reads for the calibration copy of known size."""
-    fetch = _counter_per_kernel(fetch_db, "FETCH_SIZE")
-    write = _counter_per_kernel(write_db, "WRITE_SIZE")
-    copy = [k for k in fetch if "copyBuffer" in k]
+    fetch_d = _counter_dispatches(fetch_db, "FETCH_SIZE")
+    write_d = _counter_dispatches(write_db, "WRITE_SIZE")
+    fetch, write = _median_per_kernel(fetch_d), _median_per_kernel(write_d)
+    copy = [k for k in write_d if "copyBuffer" in k]
     if not copy:
         sys.exit("no copy kernel in the trace: run with --copy-calibration")
     ck = copy[0]
     nbytes = CALIBRATION_BYTES
+    # The calibration copy is the copy dispatch that wrote closest to its
+    # size (input uploads are smaller, the copy-rate context larger); both
+    # runs execute the same program, so it has the same dispatch id in each.
+    disp = min(write_d[ck], key=lambda d: abs(write_d[ck][d] * 1024.0 - nbytes))
+    if disp not in fetch_d.get(ck, {}):
+        sys.exit("calibration copy (dispatch %d) missing from the FETCH_SIZE run" % disp)
+    fetch[ck], write[ck] = fetch_d[ck][disp], write_d[ck][disp]
     f_scale = nbytes / (fetch[ck] * 1024.0)
     w_scale = nbytes / (write[ck] * 1024.0)
     out = []
@@ -315,8 +321,12 @@ def main():
         h4.update(S.tobytes())
         Q4d.append(torch.from_numpy(Q).to(dev))
         S4d.append(torch.from_numpy(S.view(np.int16)).to(dev))
-    # fp32 GEMV: 8 matrices of 12,288 x 1,536 (604 MB), the same x length
-    Wf = [torch.from_numpy(inputs.gemv_f32_weight(r)).to(dev) for r in range(F32_ROTATION)]
+    # fp32 GEMV: 48 matrices of 12,288 x 1,536 (3.375 GiB), the same x
+    # length; drawn on a few host threads, uploaded one by one
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=min(8, len(os.sched_getaffinity(0)))) as pool:
+        Wf = [torch.from_numpy(W).to(dev)
+              for W in pool.map(inputs.gemv_f32_weight, range(F32_ROTATION))]
     W0 = Wf[0].cpu().numpy()
     xf = inputs.gemv_f32_x()
     dxf = torch.from_numpy(xf).to(dev)
@@ -733,7 +743,7 @@ def main():
             },
         },
         "gemv_f32": {
-            "metric": "fp32 GEMV GB/s at 12288x1536 (cold rotation over 8 matrices, 604 MB)",
+            "metric": "fp32 GEMV GB/s at 12288x1536 (cold rotation over 48 matrices, 3.375 GiB)",
             "value": F32_ALG_BYTES / gf_us / 1e3 if gf_ok else None,
             "unit": "GB/s",
             "avg_launch_us": gf_us,

@@ -355,160 +355,203 @@ __global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int6
 // The order is fixed for a given shape, so results repeat bit for bit.
 constexpr int FLAT_THREADS = 192;
 constexpr int FLAT_MIN_CPR = 8, FLAT_MAX_CPR = 48;
+constexpr int FLAT_MAX_RPS = FLAT_THREADS / FLAT_MIN_CPR;
 
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
 
 // Cache policy of the code loads: non-temporal (each code byte is read once).
 constexpr int NT = 2;
 
+// The per-lane pieces of the flat split, shared by the one-shot and the
+// streaming kernels so that both form every row the same way.
+template <int BITS>
+struct Flat {
+    using C = Codes<BITS>;
+    static constexpr int CC = 128 / BITS;     // codes per 16-byte chunk
+    static constexpr int UPC = CC / 16;       // units of 16 codes per chunk
+    static constexpr int CPG = 64 / CC;       // chunks per 64-column scale group
+    static constexpr int XP = CC + 4;         // LDS floats per chunk of scaled x (padded)
+
+    struct Smem {
+        float xs[FLAT_MAX_CPR * XP];
+        float xi[FLAT_MAX_CPR * UPC];
+    };
+
+    // One unit of 16 columns per lane: the chain start -z 2^(K0-24) X and
+    // the x values scaled for their codes' bit positions, into LDS; after a
+    // barrier each lane takes those of its chunk c.
+    static __device__ __forceinline__ void setup(const float *__restrict__ x, int cpr, int f,
+                                                 int c, Smem &sm, float (&xv)[CC],
+                                                 float (&init)[UPC]) {
+        if (f < cpr * UPC) {
+            const v4f *xp = reinterpret_cast<const v4f *>(x) + 4 * f;
+            float v[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const v4f t = xp[q];
+                v[4 * q] = t.x;
+                v[4 * q + 1] = t.y;
+                v[4 * q + 2] = t.z;
+                v[4 * q + 3] = t.w;
+            }
+            float X = 0.f;
+#pragma unroll
+            for (int p = 0; p < 16; ++p) X += v[p];
+            sm.xi[f] = (-C::Z / C::OUT) * X;
+            float *dst = sm.xs + (f / UPC) * XP + 16 * (f % UPC);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                v4f t;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    t[e] = v[4 * q + e] *
+                           (float)(1 << (C::K0 - C::pos(((4 * q + e) % C::CPD) % C::HALF)));
+                *reinterpret_cast<v4f *>(dst + 4 * q) = t;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < CC / 4; ++q) {
+            const v4f t = *reinterpret_cast<const v4f *>(sm.xs + c * XP + 4 * q);
+            xv[4 * q] = t.x;
+            xv[4 * q + 1] = t.y;
+            xv[4 * q + 2] = t.z;
+            xv[4 * q + 3] = t.w;
+        }
+#pragma unroll
+        for (int i = 0; i < UPC; ++i) init[i] = sm.xi[c * UPC + i];
+    }
+
+    // The lane's chunk of one step: the unit chains, their sum in unit
+    // order, times the chunk's scale.
+    static __device__ __forceinline__ float step(const unsigned (&w)[4], unsigned sbits,
+                                                 const float (&xv)[CC], const float (&init)[UPC]) {
+        float a[UPC];
+#pragma unroll
+        for (int i = 0; i < UPC; ++i) {
+            a[i] = init[i];
+#pragma unroll
+            for (int k = 0; k < C::UW; ++k)
+#pragma unroll
+                for (int h = 0; h < C::HALF; ++h) {
+                    const unsigned d = w[i * C::UW + k];
+                    const unsigned e = C::shifted(h) ? d >> C::SH : d;
+                    const h2 hv = __builtin_bit_cast(h2, e & C::mask(h));
+                    a[i] = __builtin_fmaf((float)hv.x, xv[16 * i + k * C::CPD + h], a[i]);
+                    a[i] = __builtin_fmaf((float)hv.y, xv[16 * i + k * C::CPD + h + C::HALF],
+                                          a[i]);
+                }
+        }
+        float p = a[0];
+#pragma unroll
+        for (int i = 1; i < UPC; ++i) p += a[i];
+        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits);
+        return s * p;
+    }
+
+    // Rows [0, nrows) of a block of partial sums (ps floats per row, cpr
+    // used), one lane per row, added in chunk order; row r goes to y[r] when
+    // r < rows_valid.
+    static __device__ __forceinline__ void rows(const float *part, int ps, int cpr, int nrows,
+                                                int rows_valid, float *__restrict__ y, int f) {
+        for (int r = f; r < nrows; r += FLAT_THREADS) {
+            if (r >= rows_valid) break;
+            const float *pr = part + r * ps;
+            float sum = 0.f;
+            for (int q = 0; q < cpr; q += 4) {
+                const v4f v = *reinterpret_cast<const v4f *>(pr + q);
+                sum += v.x;
+                sum += v.y;
+                sum += v.z;
+                sum += v.w;
+            }
+            y[r] = C::OUT * sum;
+        }
+    }
+};
+
+// Code and scale loads of the workgroup's rows from row0 on: buffer
+// resources that start at row0 and end at the matrix's last byte, so rows
+// past M read zeros (they are never stored), and per-lane offsets.
+struct FlatLoads {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __amdgpu_buffer_rsrc_t rq, rs;
+#endif
+    unsigned vq, vs, sq, ss;
+
+    __device__ __forceinline__ void init(const uint8_t *Q, const uint16_t *S, int M, int row0,
+                                         int cpr, int cpg, int rps, int rin, int c, int64_t ldq,
+                                         int64_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        const int rows_left = M - row0;       // >= 1
+        const int extq = (int)((int64_t)(rows_left - 1) * ldq + 16 * cpr);
+        const int exts = (int)(((int64_t)(rows_left - 1) * lds + (cpr + cpg - 1) / cpg) * 2);
+        rq = __builtin_amdgcn_make_buffer_rsrc((void *)(Q + (int64_t)row0 * ldq), (short)0, extq,
+                                               0x00020000);
+        rs = __builtin_amdgcn_make_buffer_rsrc((void *)(S + (int64_t)row0 * lds), (short)0, exts,
+                                               0x00020000);
+#endif
+        vq = (unsigned)rin * (unsigned)ldq + 16u * (unsigned)c;
+        vs = ((unsigned)rin * (unsigned)lds + (unsigned)(c / cpg)) * 2u;
+        sq = (unsigned)rps * (unsigned)ldq;
+        ss = (unsigned)rps * (unsigned)lds * 2u;
+    }
+
+    // Steps s0 .. s0 + T - 1, issued in step order.
+    template <int T>
+    __device__ __forceinline__ void issue(int s0, unsigned (&craw)[T][4], unsigned (&sraw)[T]) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const unsigned st = (unsigned)(s0 + t);
+            const u4 v = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(vq + st * sq), 0, NT);
+            craw[t][0] = v.x;
+            craw[t][1] = v.y;
+            craw[t][2] = v.z;
+            craw[t][3] = v.w;
+            sraw[t] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(vs + st * ss), 0, 0);
+            __builtin_amdgcn_sched_barrier(0);   // keep the step order
+        }
+#else
+        for (int t = 0; t < T; ++t) {
+            craw[t][0] = craw[t][1] = craw[t][2] = craw[t][3] = sraw[t] = 0u * (unsigned)s0;
+        }
+#endif
+    }
+};
+
 // T steps per workgroup; a batch asks for four waves per SIMD (at most 128
 // VGPRs), which fits five three-wave workgroups on a compute unit.
 template <int BITS, int T, int NB>
 __global__ __launch_bounds__(FLAT_THREADS) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 1 : 4)))
 void gemv_packed_flat(int M, int cpr, int rdiv, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
-    using C = Codes<BITS>;
-    constexpr int CC = 128 / BITS;            // codes per 16-byte chunk
-    constexpr int UPC = CC / 16;              // units of 16 codes per chunk
-    constexpr int CPG = 64 / CC;              // chunks per 64-column scale group
-    constexpr int UW = C::UW;
-    constexpr int XP = CC + 4;                // LDS floats per chunk of scaled x (padded)
-    constexpr int MAX_RPS = FLAT_THREADS / FLAT_MIN_CPR;
-    __shared__ __attribute__((aligned(16))) float xs[FLAT_MAX_CPR * XP];
-    __shared__ float xi[FLAT_MAX_CPR * UPC];
-    __shared__ __attribute__((aligned(16))) float part[T * (FLAT_THREADS + 4 * MAX_RPS)];
+    using F = Flat<BITS>;
+    __shared__ __attribute__((aligned(16))) typename F::Smem sm;
+    __shared__ __attribute__((aligned(16))) float part[T * (FLAT_THREADS + 4 * FLAT_MAX_RPS)];
 
     const int b = NB == 1 ? 0 : (int)blockIdx.y;
-    const uint8_t *__restrict__ Q = ptrs.Q[b];
-    const uint16_t *__restrict__ S = ptrs.S[b];
-    const float *__restrict__ x = ptrs.x[b];
-    float *__restrict__ y = ptrs.y[b];
     const int f = threadIdx.x;
     const int rps = FLAT_THREADS / cpr;       // rows per step
     const int rin = (f * rdiv) >> 16, c = f - rin * cpr;   // f / cpr (rdiv = ceil(2^16 / cpr))
     const int row0 = (int)blockIdx.x * rps * T;
     const int ps = cpr + 4;                   // LDS floats per row of partial sums
 
-    // ---- Set-up, one unit of 16 columns per lane: the chain start
-    // -z 2^(K0-24) X and the x values scaled for their codes' bit positions.
-    if (f < cpr * UPC) {
-        const v4f *xp = reinterpret_cast<const v4f *>(x) + 4 * f;
-        float v[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const v4f t = xp[q];
-            v[4 * q] = t.x;
-            v[4 * q + 1] = t.y;
-            v[4 * q + 2] = t.z;
-            v[4 * q + 3] = t.w;
-        }
-        float X = 0.f;
-#pragma unroll
-        for (int p = 0; p < 16; ++p) X += v[p];
-        xi[f] = (-C::Z / C::OUT) * X;
-        float *dst = xs + (f / UPC) * XP + 16 * (f % UPC);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            v4f t;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                t[e] = v[4 * q + e] * (float)(1 << (C::K0 - C::pos(((4 * q + e) % C::CPD) % C::HALF)));
-            *reinterpret_cast<v4f *>(dst + 4 * q) = t;
-        }
-    }
-    __syncthreads();
-    float xv[CC];
-    float init[UPC];
-#pragma unroll
-    for (int q = 0; q < CC / 4; ++q) {
-        const v4f t = *reinterpret_cast<const v4f *>(xs + c * XP + 4 * q);
-        xv[4 * q] = t.x;
-        xv[4 * q + 1] = t.y;
-        xv[4 * q + 2] = t.z;
-        xv[4 * q + 3] = t.w;
-    }
-#pragma unroll
-    for (int i = 0; i < UPC; ++i) init[i] = xi[c * UPC + i];
+    float xv[F::CC], init[F::UPC];
+    F::setup(ptrs.x[b], cpr, f, c, sm, xv, init);
 
-    // ---- Loads: every chunk and scale of the T steps, issued step by step
-    // before any is used.  The buffer resources start at the workgroup's
-    // first row and end at the matrix's last byte, so rows past M read zeros
-    // (they are never stored).
-    unsigned craw[T][4];
-    unsigned sraw[T];
-#if defined(__HIP_DEVICE_COMPILE__)
-    {
-        const int rows_left = M - row0;       // >= 1
-        const int extq = (int)((int64_t)(rows_left - 1) * ldq + 16 * cpr);
-        const int exts = (int)(((int64_t)(rows_left - 1) * lds + (cpr + CPG - 1) / CPG) * 2);
-        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(Q + (int64_t)row0 * ldq), (short)0, extq, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(S + (int64_t)row0 * lds), (short)0, exts, 0x00020000);
-        const unsigned vq = (unsigned)rin * (unsigned)ldq + 16u * (unsigned)c;
-        const unsigned vs = ((unsigned)rin * (unsigned)lds + (unsigned)(c / CPG)) * 2u;
-        const unsigned sq = (unsigned)rps * (unsigned)ldq;
-        const unsigned ss = (unsigned)rps * (unsigned)lds * 2u;
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const u4 v = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(vq + t * sq), 0, NT);
-            craw[t][0] = v.x;
-            craw[t][1] = v.y;
-            craw[t][2] = v.z;
-            craw[t][3] = v.w;
-            sraw[t] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(vs + t * ss), 0, 0);
-            __builtin_amdgcn_sched_barrier(0);   // keep the step order
-        }
-    }
-#else
-    for (int t = 0; t < T; ++t) {
-        craw[t][0] = craw[t][1] = craw[t][2] = craw[t][3] = 0u;
-        sraw[t] = 0u;
-    }
-#endif
-
-    // ---- Step by step, in the order of the loads: the unit chains of the
-    // chunk, their sum in unit order, times the chunk's scale, into LDS.
+    // Every chunk and scale of the T steps, issued step by step before any
+    // is used; then the steps in the same order, into LDS.
+    FlatLoads ld;
+    ld.init(ptrs.Q[b], ptrs.S[b], M, row0, cpr, F::CPG, rps, rin, c, ldq, lds);
+    unsigned craw[T][4], sraw[T];
+    ld.issue<T>(0, craw, sraw);
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-        float a[UPC];
-#pragma unroll
-        for (int i = 0; i < UPC; ++i) {
-            a[i] = init[i];
-#pragma unroll
-            for (int w = 0; w < UW; ++w)
-#pragma unroll
-                for (int h = 0; h < C::HALF; ++h) {
-                    const unsigned d = craw[t][i * UW + w];
-                    const unsigned e = C::shifted(h) ? d >> C::SH : d;
-                    const h2 hv = __builtin_bit_cast(h2, e & C::mask(h));
-                    a[i] = __builtin_fmaf((float)hv.x, xv[16 * i + w * C::CPD + h], a[i]);
-                    a[i] = __builtin_fmaf((float)hv.y, xv[16 * i + w * C::CPD + h + C::HALF], a[i]);
-                }
-        }
-        float p = a[0];
-#pragma unroll
-        for (int i = 1; i < UPC; ++i) p += a[i];
-        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sraw[t]);
-        part[(t * rps + rin) * ps + c] = s * p;
+        part[(t * rps + rin) * ps + c] = F::step(craw[t], sraw[t], xv, init);
         if (NB == 1) __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
-
-    // ---- One lane per row adds the row's partial sums in chunk order.
-    const int nrows = rps * T;
-    for (int r = f; r < nrows; r += FLAT_THREADS) {
-        if (row0 + r >= M) break;
-        const float *pr = part + r * ps;
-        float sum = 0.f;
-        for (int q = 0; q < cpr; q += 4) {
-            const v4f v = *reinterpret_cast<const v4f *>(pr + q);
-            sum += v.x;
-            sum += v.y;
-            sum += v.z;
-            sum += v.w;
-        }
-        y[row0 + r] = C::OUT * sum;
-    }
+    F::rows(part, ps, cpr, rps * T, M - row0, ptrs.y[b] + row0, f);
 }
 
 // Chunks per row for the flat split, or 0 where it does not apply: every row
@@ -531,7 +574,7 @@ int flat_cpr(int count, int M, int K, const uint8_t *const *Q, int64_t ldq, int6
 }
 
 // Steps per workgroup.  A single product needs many workgroups to fill the
-// chip: one step (2-bit) or four (4-bit), whose rows are twice as long.  A
+// chip: one step (2-bit) or four (4-bit, whose rows are twice as long).  A
 // batch has workgroups to spare: eight steps.  (A sweep of 1, 2 and 4 steps
 // for single products and 4 to 16 for batches of 40 at 12,288 x 1,536 put
 // the best there.)

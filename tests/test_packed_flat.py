@@ -166,3 +166,23 @@ def test_full_size_batch_of_forty(bits):
     for r in (0, 13, 39):
         ref, bound = _oracle(bits, *mats[r], x)
         assert_close(ys[r], ref, bound, "%d-bit batch product %d" % (bits, r))
+
+
+@pytest.mark.parametrize("bits,M,count", [(2, 5000, 64), (2, 12288, 50), (2, 777, 40),
+                                          (4, 3001, 33), (4, 12288, 7)])
+def test_large_batches(bits, M, count):
+    """Batches of 7 to 64 products, with a partial last workgroup at 5,000,
+    777 and 3,001 rows: sampled products against the oracle, and the same
+    bits as single calls."""
+    K = 1536
+    rng = np.random.default_rng(7 * M + count)
+    x = inputs.normal(rng, (K,))
+    dx = dev(x)
+    mats = [_operands(M, K, bits, rng=rng)[:2] for _ in range(count)]
+    dQ = [dev(Q) for Q, _ in mats]
+    dS = [dev(S.view(np.int16)) for _, S in mats]
+    ys = _batched(bits, dQ, dS, [dx] * count)
+    for r in (0, count // 2, count - 1):
+        ref, bound = _oracle(bits, *mats[r], x)
+        assert_close(ys[r], ref, bound, "%d-bit batch product %d of %d, M=%d" % (bits, r, count, M))
+        assert np.array_equal(ys[r], _single(bits, dQ[r], dS[r], dx))
