@@ -216,14 +216,14 @@ def write_traffic(fetch_db, write_db):
     for match, fname, srcs, alg in (
             (lambda n: n.startswith("gemm_f32_direct<64, 64, true, false, 2>"),
              "traffic_gemm_f32_2048.json", ("gemm_f32.hip",), 3 * 4 * GEMM_N * GEMM_N),
-            (lambda n: n.startswith("gemv_packed_flat<2, 1, 1>"),
+            (lambda n: n.startswith("gemv_packed_flat<2, 1, 1,"),
              "traffic_gemv_q2_12288x1536.json", q2_srcs, Q2_ALG_BYTES),
-            (lambda n: n.startswith("gemv_packed_flat<2, 8, 64>"),
+            (lambda n: n.startswith("gemv_packed_flat<2, 8, 64,"),
              "traffic_gemv_q2_batched_12288x1536.json", q2_srcs,
              CALLS_PER_TOKEN * Q2_ALG_BYTES),
-            (lambda n: n.startswith("gemv_packed_flat<4, 4, 1>"),
+            (lambda n: n.startswith("gemv_packed_flat<4, 4, 1,"),
              "traffic_gemv_q4_12288x1536.json", q2_srcs, Q4_ALG_BYTES),
-            (lambda n: n.startswith("gemv_packed_flat<4, 8, 64>"),
+            (lambda n: n.startswith("gemv_packed_flat<4, 8, 64,"),
              "traffic_gemv_q4_batched_12288x1536.json", q2_srcs,
              CALLS_PER_TOKEN * Q4_ALG_BYTES),
             (lambda n: n.startswith("gemv_packed_kernel<2, 256, 6,") and n.endswith(", 1>"),
