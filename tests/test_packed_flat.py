@@ -186,3 +186,39 @@ def test_large_batches(bits, M, count):
         ref, bound = _oracle(bits, *mats[r], x)
         assert_close(ys[r], ref, bound, "%d-bit batch product %d of %d, M=%d" % (bits, r, count, M))
         assert np.array_equal(ys[r], _single(bits, dQ[r], dS[r], dx))
+
+
+@pytest.mark.parametrize("bits,K", [(2, 12288), (4, 6144)])
+@pytest.mark.parametrize("M", [1, 7, 1001, 1536])
+def test_long_rows(bits, M, K):
+    """Rows of 192 chunks of 16 bytes (the transposed 12,288-input shape for
+    2-bit codes), which the row-split kernel serves with a row over a whole
+    workgroup: single and batched calls against the oracle and bit for bit
+    against each other, and integer inputs exactly."""
+    Q, S, x = _operands(M, K, bits)
+    ref, bound = _oracle(bits, Q, S, x)
+    y = _single(bits, dev(Q), dev(S.view(np.int16)), dev(x))
+    assert_close(y, ref, bound, "%d-bit long %dx%d" % (bits, M, K))
+    Q1, S1, x1 = _operands(M, K, bits)
+    ys = _batched(bits, [dev(Q1), dev(Q)], [dev(S1.view(np.int16)), dev(S.view(np.int16))],
+                  [dev(x1), dev(x)])
+    assert np.array_equal(y, ys[1])
+    r1, b1 = _oracle(bits, Q1, S1, x1)
+    assert_close(ys[0], r1, b1, "%d-bit long batched %dx%d" % (bits, M, K))
+    Qi, Si, xi = _operands(M, K, bits, integer=True)
+    refi, _ = _oracle(bits, Qi, Si, xi)
+    assert np.array_equal(_single(bits, dev(Qi), dev(Si.view(np.int16)), dev(xi)).astype(np.float64), refi)
+
+
+@pytest.mark.parametrize("bits,K", [(2, 12288), (4, 6144)])
+def test_long_rows_padded(bits, K):
+    """The same long rows with ldq padded by 32 bytes and lds by 3 halves,
+    padding full of random bits."""
+    M = 301
+    Q, S, x = _operands(M, K, bits)
+    ref, bound = _oracle(bits, Q, S, x)
+    dQ = dev(_padded(Q, 32, RNG))[:, :Q.shape[1]]
+    dS = dev(_padded(S, 3, RNG).view(np.int16))[:, :S.shape[1]]
+    assert_close(_single(bits, dQ, dS, dev(x)), ref, bound, "%d-bit long padded" % bits)
+    ys = _batched(bits, [dQ] * 3, [dS] * 3, [dev(x)] * 3)
+    assert_close(ys[2], ref, bound, "%d-bit long padded batched" % bits)
