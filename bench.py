@@ -139,6 +139,56 @@ def cpu_baseline(A, B, Q, S, x, budget_s=12.0):
     }
 
 
+def vendor_context(torch, stream, capture, timed, token_runner, n_tok, per_replay, dA, dB, Wf,
+                   dx, A, B, args):
+    """The vendor library on the same inputs, for context only (never part of
+    the library's path): torch.matmul in fp32 with TF32 off (hipBLASLt or
+    rocBLAS) at 2048^3, and torch.mv over the fp32 GEMV rotation set, timed
+    like the library's kernels (back-to-back launches in graph replays)."""
+    out = {"note": ("torch.matmul / torch.mv in fp32 with TF32 off on the same operands, "
+                    "graph-replayed back to back like the library's kernels: context, "
+                    "not part of the library")}
+    try:
+        torch.backends.cuda.matmul.allow_tf32 = False
+        C = torch.empty_like(dA)
+        with torch.cuda.stream(stream):
+            torch.matmul(dA, dB, out=C)
+            stream.synchronize()
+        ref = (A[:4].astype(np.float64) @ B.astype(np.float64))
+        err = float(np.max(np.abs(C[:4].cpu().numpy() - ref)))
+        g = capture(lambda: [torch.matmul(dA, dB, out=C) for _ in range(per_replay)])
+        reps = max(1, (args.steps + per_replay - 1) // per_replay)
+
+        def run(i):
+            if i is not None:
+                g.replay()
+                return 1
+            for _ in range(reps):
+                g.replay()
+            return reps * per_replay
+        ms, n, _ = timed(run, 2)
+        us = 1e3 * ms / n
+        out["matmul_2048_us"] = us
+        out["matmul_2048_tflops"] = GEMM_FLOPS / us / 1e6
+        out["matmul_2048_max_abs_err_first_rows"] = err
+        y = torch.empty(Q2_M, dtype=torch.float32, device=dA.device)
+
+        def tok(t):
+            for c in range(CALLS_PER_TOKEN):
+                torch.mv(Wf[(t * CALLS_PER_TOKEN + c) % F32_ROTATION], dx, out=y)
+        with torch.cuda.stream(stream):
+            tok(0)
+            stream.synchronize()
+        graphs = [capture(lambda t=t: tok(t)) for t in range(n_tok)]
+        ms, n, _ = timed(token_runner(graphs), 2)
+        us = 1e3 * ms / n
+        out["mv_12288x1536_us"] = us
+        out["mv_12288x1536_gbs"] = F32_ALG_BYTES / us / 1e3
+    except Exception as e:   # context only: report, never fail the bench
+        out["error"] = "%s: %s" % (type(e).__name__, e)
+    return out
+
+
 def host_cpu():
     try:
         with open("/proc/cpuinfo") as f:
@@ -596,6 +646,8 @@ def main():
         stream.synchronize()
     copy_gbs = 2 * copy_bytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del csrc, cdst
+    vendor = vendor_context(torch, stream, capture, timed, token_runner, n_tok, gemms_per_replay,
+                            dA, dB, Wf, dxf, A, B, args)
 
     gemm_tflops = GEMM_FLOPS / gemm_us / 1e6
     q2_gbs = Q2_WEIGHT_BYTES / q2_us / 1e3
@@ -765,6 +817,7 @@ def main():
             "hbm_copy_gbs": copy_gbs,
             "hbm_copy_note": ("torch device-to-device copy of 1 GiB, 10 times, "
                               "read + write bytes / time: what plain streaming reaches"),
+            "vendor_library": vendor,
         },
         "parity": {"gemm_f32_2048": "pass" if gemm_ok else "FAIL",
                    "gemv_f32": "pass" if gf_ok else "FAIL",
