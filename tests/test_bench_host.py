@@ -1,0 +1,104 @@
+"""Host logic of bench.py, on the CPU: the kernel-trace summary and the
+calibrated traffic computed from synthetic rocprofv3 databases (the tables and
+columns rocprofv3 writes), the source-hash gate on stored traffic, and the
+one-GPU guard."""
+import importlib.util
+import json
+import os
+import sqlite3
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+GEMM = "void gg::(anonymous namespace)::gemm_f32_direct<64, 64, true, false, 2>(int, int, int)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def _trace_db(path, rows):
+    db = sqlite3.connect(path)
+    db.execute("create table kernels (name text, duration integer)")
+    db.executemany("insert into kernels values (?, ?)", rows)
+    db.commit()
+    db.close()
+
+
+def _counter_db(path, counter, rows):
+    """rows: (kernel name, dispatch id, value in KiB), one row per instance."""
+    db = sqlite3.connect(path)
+    db.execute("create table counters_collection (kernel_name text, dispatch_id integer, "
+               "counter_name text, value real)")
+    db.executemany("insert into counters_collection values (?, ?, ?, ?)",
+                   [(k, d, counter, v) for k, d, v in rows])
+    db.commit()
+    db.close()
+
+
+def test_summarize_trace(bench, tmp_path):
+    p = str(tmp_path / "t.db")
+    _trace_db(p, [(GEMM, 130000), (GEMM, 134000), (COPY, 5000)])
+    lines = bench.summarize_trace(p).splitlines()
+    assert lines[0].startswith("| kernel | calls |")
+    row = [l for l in lines if "gemm_f32_direct<64, 64, true, false, 2>" in l][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[0] == "gemm_f32_direct<64, 64, true, false, 2>"   # namespace and arguments cut
+    assert cells[1] == "2"
+    assert float(cells[2]) == pytest.approx(264.0)       # total us
+    assert float(cells[3]) == pytest.approx(132.0)       # average us
+    assert float(cells[4]) == pytest.approx(130.0) and float(cells[5]) == pytest.approx(134.0)
+    assert lines[2].find("gemm") > 0                     # sorted by total time
+
+
+def test_traffic_uses_the_calibration_copy(bench, tmp_path, monkeypatch):
+    """The calibration copy is the copy dispatch whose WRITE_SIZE is closest to
+    its size: neither the input uploads nor the larger context copies."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    cal = bench.CALIBRATION_BYTES // 1024                 # KiB
+    fetch_rows = [(COPY, 5, 100.0), (COPY, 36, cal / 2.0), (COPY, 90, 4.0 * cal / 2.0),
+                  (COPY, 91, 4.0 * cal / 2.0)]
+    write_rows = [(COPY, 5, 200.0), (COPY, 36, float(cal)), (COPY, 90, 4.0 * cal),
+                  (COPY, 91, 4.0 * cal)]
+    # the GEMM: two instances per dispatch (summed), three dispatches (median)
+    for d, f in ((40, 40000.0), (41, 41000.0), (42, 45000.0)):
+        fetch_rows += [(GEMM, d, f / 2), (GEMM, d, f / 2)]
+        write_rows += [(GEMM, d, 8192.0), (GEMM, d, 8192.0)]
+    fdb, wdb = str(tmp_path / "f.db"), str(tmp_path / "w.db")
+    _counter_db(fdb, "FETCH_SIZE", fetch_rows)
+    _counter_db(wdb, "WRITE_SIZE", write_rows)
+    assert bench.write_traffic(fdb, wdb) == 0
+    with open(tmp_path / "traffic_gemm_f32_2048.json") as f:
+        d = json.load(f)
+    assert d["fetch_scale"] == pytest.approx(2.0)
+    assert d["write_scale"] == pytest.approx(1.0)
+    assert d["fetch_kib_raw"] == pytest.approx(41000.0)
+    assert d["write_kib_raw"] == pytest.approx(16384.0)
+    expect = 41000.0 * 1024 * 2.0 + 16384.0 * 1024
+    assert d["hbm_bytes_per_launch"] == pytest.approx(expect)
+    assert d["traffic_over_algorithmic"] == pytest.approx(expect / (3 * 4 * 2048 * 2048))
+
+
+def test_traffic_gated_by_source_hash(bench, tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    with open(tmp_path / "x.json", "w") as f:
+        json.dump({"kernel_src_sha": "abc", "hbm_bytes_per_launch": 123.0}, f)
+    assert bench.traffic_from_profile("x.json", "abc") == 123.0
+    assert bench.traffic_from_profile("x.json", "def") is None
+    assert bench.traffic_from_profile("missing.json", "abc") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
