@@ -453,21 +453,42 @@ struct Flat {
         return s * p;
     }
 
+    // The NQ * 4 partial sums of a row: every read issued first, then a
+    // pairwise tree in a fixed order (one LDS round trip and log2 levels of
+    // adds on the workgroup's last step, instead of a chain through it).
+    template <int NQ>
+    static __device__ __forceinline__ float row_sum(const float *pr) {
+        float v[4 * NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const v4f t = *reinterpret_cast<const v4f *>(pr + 4 * q);
+            v[4 * q] = t.x;
+            v[4 * q + 1] = t.y;
+            v[4 * q + 2] = t.z;
+            v[4 * q + 3] = t.w;
+        }
+#pragma unroll
+        for (int w = 1; w < 4 * NQ; w *= 2)
+#pragma unroll
+            for (int i = 0; i + w < 4 * NQ; i += 2 * w) v[i] += v[i + w];
+        return v[0];
+    }
+
     // Rows [0, nrows) of a block of partial sums (ps floats per row, cpr
-    // used), one lane per row, added in chunk order; row r goes to y[r] when
-    // r < rows_valid.
+    // used), one lane per row; row r goes to y[r] when r < rows_valid.
     static __device__ __forceinline__ void rows(const float *part, int ps, int cpr, int nrows,
                                                 int rows_valid, float *__restrict__ y, int f) {
         for (int r = f; r < nrows; r += FLAT_THREADS) {
             if (r >= rows_valid) break;
             const float *pr = part + r * ps;
-            float sum = 0.f;
-            for (int q = 0; q < cpr; q += 4) {
-                const v4f v = *reinterpret_cast<const v4f *>(pr + q);
-                sum += v.x;
-                sum += v.y;
-                sum += v.z;
-                sum += v.w;
+            float sum;
+            switch (cpr) {   // the chunk counts the flat split takes
+            case 8: sum = row_sum<2>(pr); break;
+            case 12: sum = row_sum<3>(pr); break;
+            case 16: sum = row_sum<4>(pr); break;
+            case 24: sum = row_sum<6>(pr); break;
+            case 32: sum = row_sum<8>(pr); break;
+            default: sum = row_sum<12>(pr); break;   // 48
             }
             y[r] = C::OUT * sum;
         }
