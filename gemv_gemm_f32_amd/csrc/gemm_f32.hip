@@ -308,22 +308,23 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ int xswz(int r) { return (r ^ (r >> 3)) & 7; }
 
 // One operand's k-slab (TX values of x by 32 of k) as NI buffer loads per
-// wave; instruction j of wave w fills the 1 KB block 4j + w of the stage.
+// wave of a group of WPG waves; instruction j of wave w fills the 1 KB block
+// WPG*j + w of the stage.
 //   XMAJOR: element (x, k) at P[x*ld + k]; the stage holds TX rows of 128 B.
 //   else  : element (x, k) at P[k*ld + x]; the stage holds 32 rows of TX*4 B.
-template <int TX, bool XMAJOR>
+template <int TX, bool XMAJOR, int WPG = 4>
 struct DirectOperand {
     static constexpr int BK = 32;
     static constexpr int STAGE = TX * BK * 4;     // bytes per stage
-    static constexpr int NI = STAGE / 1024 / 4;   // loads per wave per slab
-    static_assert(NI >= 1, "tile too small");
+    static constexpr int NI = STAGE / 1024 / WPG; // loads per wave per slab
+    static_assert(NI >= 1 && NI * 1024 * WPG == STAGE, "tile must split over the waves");
     unsigned voff[NI];   // byte offset of this lane's chunk at k = 0
     int kof[NI];         // k of this lane's chunk (x-major) or row (k-major) in the slab
 
     __device__ __forceinline__ void init(int64_t ld, int x0, int X, int lane, int wave) {
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-            const int blk = 4 * j + wave;
+            const int blk = WPG * j + wave;
             if (XMAJOR) {
                 const int row = 8 * blk + lane / 8;
                 const int c = (lane % 8) ^ xswz(row);
@@ -353,7 +354,7 @@ struct DirectOperand {
 #pragma unroll
         for (int j = 0; j < NI; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc, (lds_void *)(stage + (4 * j + wave) * 1024), 16, voff[j], so, 0, 0);
+                rsrc, (lds_void *)(stage + (WPG * j + wave) * 1024), 16, voff[j], so, 0, 0);
 #endif
     }
     // after this wave's loads of the slab at k0 have landed: zero what lies at k >= K
@@ -361,7 +362,7 @@ struct DirectOperand {
 #pragma unroll
         for (int j = 0; j < NI; ++j)
             if (k0 + kof[j] >= K)
-                *reinterpret_cast<v4f *>(stage + (4 * j + wave) * 1024 + lane * 16) =
+                *reinterpret_cast<v4f *>(stage + (WPG * j + wave) * 1024 + lane * 16) =
                     v4f{0.f, 0.f, 0.f, 0.f};
     }
     // byte offset, within a stage, of lane (l32, h)'s operand of k-group g
@@ -381,34 +382,40 @@ struct DirectOperand {
     }
 };
 
-// KS groups of 4 waves split the k-slabs of one output tile: group g takes
+// KS groups of WPG waves split the k-slabs of one output tile: group g takes
 // slabs g, g + KS, g + 2 KS, ... through its own double-buffered stages.  At
 // the end groups 1 .. KS-1 hand their accumulators to group 0 through LDS,
-// which adds them in group order, so the sum is fixed for a given KS.
-template <int BM, int BN, bool AX, bool BX, int KS>
-__global__ __launch_bounds__(THREADS * KS) void gemm_f32_direct(
+// which adds them in group order, so the sum is fixed for a given KS.  The
+// WPG waves of a group lay out as 2 x 2 (WPG = 4), 1 x 2 or 2 x 1 (WPG = 2,
+// along the longer side of the tile) or 1 x 1 over the tile, each wave
+// holding 32 x 32 MFMA blocks.
+template <int BM, int BN, bool AX, bool BX, int KS, int WPG = 4>
+__global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
     int M, int N, int K, float alpha, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
     int tiles_m, int tiles_n) {
     constexpr int BK = 32;
-    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int WC = WPG == 4 ? 2 : (WPG == 2 && BN >= BM ? 2 : 1);   // wave columns
+    constexpr int WR = WPG / WC;                  // wave rows
+    constexpr int WM = BM / WR, WN = BN / WC;
     constexpr int IB = WM / 32, JB = WN / 32;
-    using OA = DirectOperand<BM, AX>;
-    using OB = DirectOperand<BN, BX>;
+    static_assert(IB * 32 == WM && JB * 32 == WN && WR * WC == WPG, "tile must split into 32-blocks");
+    using OA = DirectOperand<BM, AX, WPG>;
+    using OB = DirectOperand<BN, BX, WPG>;
     constexpr int STAGE = OA::STAGE + OB::STAGE;
     constexpr int ACCW = IB * JB * 16;            // accumulator words per lane
-    static_assert(KS == 1 || (KS - 1) * THREADS * ACCW * 4 <= KS * 2 * STAGE,
+    static_assert(KS == 1 || (KS - 1) * 64 * WPG * ACCW * 4 <= KS * 2 * STAGE,
                   "the hand-over of partial sums must fit in the stages");
     __shared__ __attribute__((aligned(1024))) char smem[KS * 2 * STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = wave >> 2, wq = wave & 3;     // k-group, wave within the group
+    const int grp = wave / WPG, wq = wave % WPG;  // k-group, wave within the group
     const int h = lane >> 5, l32 = lane & 31;
     int tm, tn;
     tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int wm = (wq >> 1) * WM, wn = (wq & 1) * WN;
+    const int wm = (wq / WC) * WM, wn = (wq % WC) * WN;
 
     OA oa;
     OB ob;
@@ -508,11 +515,11 @@ __global__ __launch_bounds__(THREADS * KS) void gemm_f32_direct(
 
     if (KS > 1) {
         // groups 1 .. KS-1 hand their sums to group 0 (word e of lane l of
-        // wave wq of group g at float index ((g-1)*4 + wq)*ACCW*64 + e*64 + l)
+        // wave wq of group g at float index ((g-1)*WPG + wq)*ACCW*64 + e*64 + l)
         float *red = reinterpret_cast<float *>(smem);
         __syncthreads();                          // every stage read is done
         if (grp > 0) {
-            float *dst = red + ((grp - 1) * 4 + wq) * ACCW * 64 + lane;
+            float *dst = red + ((grp - 1) * WPG + wq) * ACCW * 64 + lane;
 #pragma unroll
             for (int i = 0; i < IB; ++i)
 #pragma unroll
@@ -524,7 +531,7 @@ __global__ __launch_bounds__(THREADS * KS) void gemm_f32_direct(
         if (grp > 0) return;
 #pragma unroll
         for (int g = 1; g < KS; ++g) {
-            const float *src = red + ((g - 1) * 4 + wq) * ACCW * 64 + lane;
+            const float *src = red + ((g - 1) * WPG + wq) * ACCW * 64 + lane;
 #pragma unroll
             for (int i = 0; i < IB; ++i)
 #pragma unroll
@@ -548,15 +555,30 @@ __global__ __launch_bounds__(THREADS * KS) void gemm_f32_direct(
         }
 }
 
-template <bool AX, bool BX, int BM, int BN, int KS = 1>
+template <bool AX, bool BX, int BM, int BN, int KS = 1, int WPG = 4>
 hipError_t launch_direct(int M, int N, int K, float alpha, const float *A, int64_t lda,
                          const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
                          hipStream_t s) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    hipLaunchKernelGGL((gemm_f32_direct<BM, BN, AX, BX, KS>), dim3(tiles_m * tiles_n),
-                       dim3(THREADS * KS), 0, s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+    hipLaunchKernelGGL((gemm_f32_direct<BM, BN, AX, BX, KS, WPG>), dim3(tiles_m * tiles_n),
+                       dim3(64 * WPG * KS), 0, s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                        tiles_m, tiles_n);
     return hipGetLastError();
+}
+
+// Small-grid tiles: 32 x 64 when A is x-major, else 64 x 32 (B x-major);
+// two waves per k-group, KS k-groups.
+template <bool AX, bool BX>
+hipError_t launch_small(int ks, int M, int N, int K, float alpha, const float *A, int64_t lda,
+                        const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
+                        hipStream_t s) {
+    constexpr int BM = AX ? 32 : 64, BN = AX ? 64 : 32;
+    if constexpr (!AX && !BX) {
+        return hipErrorInvalidValue;   // never called: a 32-wide tile needs an x-major operand
+    } else
+    return ks == 4 ? launch_direct<AX, BX, BM, BN, 4, 2>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s)
+           : ks == 2 ? launch_direct<AX, BX, BM, BN, 2, 2>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s)
+                     : launch_direct<AX, BX, BM, BN, 1, 2>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
 }
 
 constexpr int PROD_BK = 32;
@@ -604,8 +626,17 @@ hipError_t launch_gemm(bool ax, bool bx, int M, int N, int K, float alpha, const
     const int64_t tiles_64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
     const int slabs = (K + 31) / 32;
     const int ks = tiles_64 <= (int64_t)num_cus && slabs >= 8 ? 4 : (slabs >= 4 ? 2 : 1);
+    // Small grids (a 64 x 64 tile for fewer than half the CUs): half-height
+    // or half-width tiles, 32 x 64 (or 64 x 32), with two waves per k-group,
+    // double the workgroups.  The 32-wide operand must be x-major (its LDS
+    // rows are 128 B), so A . B^T-shaped and A . B products take 32 x 64,
+    // A^T . B^T takes 64 x 32, and A^T . B keeps 64 x 64.  346 x 768 x 768
+    // went from 17.3 to 11.4 us and 256^3 from 8.5 to 6.3 us (same box).
+    const bool small = tiles_64 * 2 < (int64_t)num_cus;
+    const int kss = slabs >= 8 ? 4 : (slabs >= 4 ? 2 : 1);
 #define GG_ARGS M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s
 #define GG_GEMM_DIRECT(AX_, BX_)                                                     \
+    if (small && (AX_ || BX_)) return launch_small<AX_, BX_>(kss, GG_ARGS);         \
     return ks == 4 ? launch_direct<AX_, BX_, 64, 64, 4>(GG_ARGS)                  \
            : ks == 2 ? launch_direct<AX_, BX_, 64, 64, 2>(GG_ARGS)                \
                      : launch_direct<AX_, BX_, 64, 64, 1>(GG_ARGS);
