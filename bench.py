@@ -264,7 +264,7 @@ def write_traffic(fetch_db, write_db):
     out = []
     q2_srcs = ("gemv_packed.hip", "wave.hpp")
     for match, fname, srcs, alg in (
-            (lambda n: n.startswith("gemm_f32_direct<64, 64, true, false, 2>"),
+            (lambda n: n.startswith("gemm_f32_direct<64, 64, true, false, 2,"),
              "traffic_gemm_f32_2048.json", ("gemm_f32.hip",), 3 * 4 * GEMM_N * GEMM_N),
             (lambda n: n.startswith("gemv_packed_flat<2, 1, 1,"),
              "traffic_gemv_q2_12288x1536.json", q2_srcs, Q2_ALG_BYTES),
