@@ -22,7 +22,7 @@ def bench():
     return mod
 
 
-GEMM = "void gg::(anonymous namespace)::gemm_f32_direct<64, 64, true, false, 2>(int, int, int)"
+GEMM = "void gg::(anonymous namespace)::gemm_f32_direct<64, 64, true, false, 2, 4>(int, int, int)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -50,9 +50,9 @@ def test_summarize_trace(bench, tmp_path):
     _trace_db(p, [(GEMM, 130000), (GEMM, 134000), (COPY, 5000)])
     lines = bench.summarize_trace(p).splitlines()
     assert lines[0].startswith("| kernel | calls |")
-    row = [l for l in lines if "gemm_f32_direct<64, 64, true, false, 2>" in l][0]
+    row = [l for l in lines if "gemm_f32_direct<64, 64, true, false, 2, 4>" in l][0]
     cells = [c.strip() for c in row.strip("|").split("|")]
-    assert cells[0] == "gemm_f32_direct<64, 64, true, false, 2>"   # namespace and arguments cut
+    assert cells[0] == "gemm_f32_direct<64, 64, true, false, 2, 4>"   # namespace and arguments cut
     assert cells[1] == "2"
     assert float(cells[2]) == pytest.approx(264.0)       # total us
     assert float(cells[3]) == pytest.approx(132.0)       # average us
