@@ -318,6 +318,11 @@ struct DirectOperand {
     static constexpr int STAGE = TX * BK * 4;     // bytes per stage
     static constexpr int NI = STAGE / 1024 / WPG; // loads per wave per slab
     static_assert(NI >= 1 && NI * 1024 * WPG == STAGE, "tile must split over the waves");
+    // k-major rows swap their two 128-byte halves on every other group of
+    // four rows, so that the two half-waves of a fragment read (4 rows
+    // apart) use different banks; rows of 32 floats have no second half and
+    // take 2-way conflicts instead.
+    static constexpr int KSW = TX >= 64 ? 8 : 0;
     unsigned voff[NI];   // byte offset of this lane's chunk at k = 0
     int kof[NI];         // k of this lane's chunk (x-major) or row (k-major) in the slab
 
@@ -334,7 +339,7 @@ struct DirectOperand {
                 constexpr int CPR = TX / 4;       // chunks per row
                 constexpr int RPB = 64 / CPR;     // rows per 1 KB block
                 const int row = RPB * blk + lane / CPR;
-                const int c = (lane % CPR) ^ (8 * ((row >> 2) & 1));
+                const int c = (lane % CPR) ^ (KSW * ((row >> 2) & 1));
                 voff[j] = (unsigned)(((int64_t)row * ld + min(x0 + 4 * c, X - 4)) * 4);
                 kof[j] = row;
             }
@@ -373,7 +378,7 @@ struct DirectOperand {
             return r * 128 + (((2 * g + h) ^ xswz(r)) * 16);
         }
         const int x = xb + l32;
-        return (8 * g + 4 * h) * TX * 4 + (((x >> 2) ^ (8 * h)) * 16) + (x & 3) * 4;
+        return (8 * g + 4 * h) * TX * 4 + (((x >> 2) ^ (KSW * h)) * 16) + (x & 3) * 4;
     }
     static __device__ __forceinline__ v4f frag(const char *stage, int off) {
         if (XMAJOR) return *reinterpret_cast<const v4f *>(stage + off);
@@ -566,19 +571,27 @@ hipError_t launch_direct(int M, int N, int K, float alpha, const float *A, int64
     return hipGetLastError();
 }
 
-// Small-grid tiles: 32 x 64 when A is x-major, else 64 x 32 (B x-major);
-// two waves per k-group, KS k-groups.
+// Narrow tiles: 64 x 32 when A is x-major, else 32 x 64, so the narrow side
+// falls on B in A . B and A . B^T and on A in A^T . B and A^T . B^T; two
+// waves per k-group, KS k-groups.
 template <bool AX, bool BX>
-hipError_t launch_small(int ks, int M, int N, int K, float alpha, const float *A, int64_t lda,
-                        const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
-                        hipStream_t s) {
-    constexpr int BM = AX ? 32 : 64, BN = AX ? 64 : 32;
-    if constexpr (!AX && !BX) {
-        return hipErrorInvalidValue;   // never called: a 32-wide tile needs an x-major operand
-    } else
+hipError_t launch_half(int ks, int M, int N, int K, float alpha, const float *A, int64_t lda,
+                       const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
+                       hipStream_t s) {
+    constexpr int BM = AX ? 64 : 32, BN = AX ? 32 : 64;
     return ks == 4 ? launch_direct<AX, BX, BM, BN, 4, 2>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s)
            : ks == 2 ? launch_direct<AX, BX, BM, BN, 2, 2>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s)
                      : launch_direct<AX, BX, BM, BN, 1, 2>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+}
+
+// Quarter tiles: 32 x 32, one wave per k-group, KS k-groups.
+template <bool AX, bool BX>
+hipError_t launch_quarter(int ks, int M, int N, int K, float alpha, const float *A, int64_t lda,
+                          const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
+                          hipStream_t s) {
+    return ks == 4 ? launch_direct<AX, BX, 32, 32, 4, 1>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s)
+           : ks == 2 ? launch_direct<AX, BX, 32, 32, 2, 1>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s)
+                     : launch_direct<AX, BX, 32, 32, 1, 1>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
 }
 
 constexpr int PROD_BK = 32;
@@ -626,17 +639,33 @@ hipError_t launch_gemm(bool ax, bool bx, int M, int N, int K, float alpha, const
     const int64_t tiles_64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
     const int slabs = (K + 31) / 32;
     const int ks = tiles_64 <= (int64_t)num_cus && slabs >= 8 ? 4 : (slabs >= 4 ? 2 : 1);
-    // Small grids (a 64 x 64 tile for fewer than half the CUs): half-height
-    // or half-width tiles, 32 x 64 (or 64 x 32), with two waves per k-group,
-    // double the workgroups.  The 32-wide operand must be x-major (its LDS
-    // rows are 128 B), so A . B^T-shaped and A . B products take 32 x 64,
-    // A^T . B^T takes 64 x 32, and A^T . B keeps 64 x 64.  346 x 768 x 768
-    // went from 17.3 to 11.4 us and 256^3 from 8.5 to 6.3 us (same box).
+    // Smaller tiles where 64 x 64 balances badly over the CUs.  The largest
+    // per-CU share of tiles is ceil(tiles / CUs); a narrow tile (64 x 32 or
+    // 32 x 64) costs about half a 64 x 64 one, a little more than half on a
+    // busy CU.
+    //  - Small grids (64 x 64 tiles for fewer than half the CUs): 32 x 32
+    //    tiles when those still fit one per CU, else narrow tiles, with
+    //    the k-slabs split four ways where K allows.  256^3 took 6.3 -> 5.5
+    //    us and 500 x 500 x 2000 23.5 -> 18.4 us with 32 x 32 tiles.
+    //  - More tiles than CUs: narrow tiles when the share of 64 x 64 tiles
+    //    is at least 1.2 times that of narrow ones in 64 x 64 units, i.e. a
+    //    last round of 64 x 64 tiles that would leave most CUs idle.  On
+    //    1024 x 2304 x 768 (576 tiles) 43.1 -> 40.6 us and on 1024 x 1216 x
+    //    1024 (304 tiles) 35.1 -> 31.2 us; 432, 700, 768 and 1024 tiles
+    //    stay on 64 x 64, where narrow tiles measured 6-24% slower.
+    const int64_t tiles_32 = (int64_t)((M + 31) / 32) * ((N + 31) / 32);
+    const int64_t tiles_h = ax ? (int64_t)((M + 63) / 64) * ((N + 31) / 32)
+                               : (int64_t)((M + 31) / 32) * ((N + 63) / 64);
+    const auto share = [num_cus](int64_t t) { return (t + num_cus - 1) / num_cus; };
     const bool small = tiles_64 * 2 < (int64_t)num_cus;
+    const bool quarter = small && tiles_32 <= (int64_t)num_cus;
+    const bool half = small ? !quarter
+                            : tiles_64 > (int64_t)num_cus && 10 * share(tiles_64) >= 6 * share(tiles_h);
     const int kss = slabs >= 8 ? 4 : (slabs >= 4 ? 2 : 1);
 #define GG_ARGS M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s
 #define GG_GEMM_DIRECT(AX_, BX_)                                                     \
-    if (small && (AX_ || BX_)) return launch_small<AX_, BX_>(kss, GG_ARGS);         \
+    if (quarter) return launch_quarter<AX_, BX_>(kss, GG_ARGS);                    \
+    if (half) return launch_half<AX_, BX_>(small ? kss : ks, GG_ARGS);             \
     return ks == 4 ? launch_direct<AX_, BX_, 64, 64, 4>(GG_ARGS)                  \
            : ks == 2 ? launch_direct<AX_, BX_, 64, 64, 2>(GG_ARGS)                \
                      : launch_direct<AX_, BX_, 64, 64, 1>(GG_ARGS);
