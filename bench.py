@@ -32,7 +32,9 @@ failing kernel reports no speed.  `cpu_baseline` times the oracle itself on a bo
 After the main timing, `spread` gives each kernel's per-launch median, p10,
 p90 and minimum over 16 single replays, and `context` the 2-bit GEMV on one
 cache-resident matrix (its launch-and-compute floor) and the rate of a plain
-device-to-device copy.
+device-to-device copy.  `gemm_configs` checks and times the other GEMM
+configurations: the nine products of a GPT-2-small block at 1,024 tokens
+(alone and as one graph), the 346 x 768 x 768 classifier layer and 256^3.
 """
 from __future__ import annotations
 
@@ -189,6 +191,97 @@ def vendor_context(torch, stream, capture, timed, token_runner, n_tok, per_repla
     return out
 
 
+def gemm_configs(torch, bd, inputs, oracle, dev, stream, capture, timed, steps, per_replay=8):
+    """The GEMM configurations besides 2048^3, each checked against the oracle
+    on sampled cells before it is timed: the nine products of a GPT-2-small
+    block at 1,024 tokens (three forward, six backward; "I built a GPT-2 in
+    the browser...", section "The kernel sweep", where matmul is most of
+    training time), the 346 x 768 x 768 classifier layer (the 346-token
+    prompt of the polyomino classifier page) and 256^3.  Each product is
+    timed over back-to-back launches in graph replays, the block's nine
+    products also as one graph; torch.matmul (fp32, TF32 off) on the same
+    operands is context only.  A product that fails parity reports no time."""
+    torch.backends.cuda.matmul.allow_tf32 = False
+    entry = {"nn": bd.gemm_f32, "tn": bd.gemm_f32_tn, "nt": bd.gemm_f32_nt}
+    rng = np.random.default_rng(77)
+    t = inputs.gpt2_tensors(2)
+    ops = [(name, lay, M, N, K, t[an], t[bn]) for name, lay, M, N, K, (an, bn) in inputs.GPT2_OPS]
+    A346, B346 = inputs.classifier(33)
+    A256, B256 = inputs.small_square(0)
+    ops += [("classifier_346x768x768", "nn", 346, 768, 768, A346, B346),
+            ("square_256", "nn", 256, 256, 256, A256, B256)]
+    reps = max(1, (steps + per_replay - 1) // per_replay)
+    out, launches, all_ok = {}, [], True
+    for name, lay, M, N, K, A, B in ops:
+        dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+        dC = torch.empty((M, N), dtype=torch.float32, device=dev)
+        f = entry[lay]
+        f(dA, dB, C=dC)
+        C = dC.cpu().numpy()
+        rows = np.concatenate([rng.integers(0, M, 384), [0, 0, M - 1, M - 1]])
+        cols = np.concatenate([rng.integers(0, N, 384), [0, N - 1, 0, N - 1]])
+        ref, bound = oracle.gemm_cells(A, B, rows, cols, trans_a=lay == "tn", trans_b=lay == "nt")
+        ok, worst, _ = oracle.check(C[rows, cols], ref, bound)
+        all_ok = all_ok and ok
+        d = {"shape": "%s %dx%dx%d" % (lay.upper(), M, N, K), "parity": "pass" if ok else "FAIL",
+             "worst_err_over_bound": worst}
+        flops = 2.0 * M * N * K
+        if ok:
+            g = capture(lambda f=f, dA=dA, dB=dB, dC=dC: [f(dA, dB, C=dC) for _ in range(per_replay)])
+
+            def run(i, g=g):
+                if i is not None:
+                    g.replay()
+                    return 1
+                for _ in range(reps):
+                    g.replay()
+                return reps * per_replay
+            ms, n, _ = timed(run, 2)
+            d["us"] = 1e3 * ms / n
+            d["tflops"] = flops / d["us"] / 1e6
+            d["frac_of_fp32_mfma_peak"] = d["tflops"] / PEAK_FP32_MFMA_TFLOPS
+            try:
+                oa = dA.t() if lay == "tn" else dA
+                ob = dB.t() if lay == "nt" else dB
+                gv = capture(lambda oa=oa, ob=ob, dC=dC: [torch.matmul(oa, ob, out=dC)
+                                                          for _ in range(per_replay)])
+
+                def runv(i, gv=gv):
+                    if i is not None:
+                        gv.replay()
+                        return 1
+                    for _ in range(reps):
+                        gv.replay()
+                    return reps * per_replay
+                ms, n, _ = timed(runv, 2)
+                d["vendor_torch_matmul_us"] = 1e3 * ms / n
+            except Exception as e:   # context only
+                d["vendor_error"] = "%s: %s" % (type(e).__name__, e)
+        out[name] = d
+        if name in {o[0] for o in inputs.GPT2_OPS}:
+            launches.append((f, dA, dB, dC, flops))
+    if all_ok:
+        g = capture(lambda: [f(dA, dB, C=dC) for f, dA, dB, dC, _ in launches])
+
+        def runb(i):
+            if i is not None:
+                g.replay()
+                return 1
+            for _ in range(steps):
+                g.replay()
+            return steps
+        ms, n, _ = timed(runb, 2)
+        us = 1e3 * ms / n
+        total = sum(fl for *_, fl in launches)
+        out["gpt2_block_9_products"] = {
+            "us": us, "tflops": total / us / 1e6,
+            "frac_of_fp32_mfma_peak": total / us / 1e6 / PEAK_FP32_MFMA_TFLOPS,
+            "vendor_torch_matmul_us_sum": sum(out[o[0]].get("vendor_torch_matmul_us", float("nan"))
+                                              for o in inputs.GPT2_OPS),
+            "note": "F1..B3w back to back in one graph, 39,862,665,216 flop per block"}
+    return out, all_ok
+
+
 def host_cpu():
     try:
         with open("/proc/cpuinfo") as f:
@@ -205,34 +298,56 @@ def _short_name(kernel):
     return k.split("(")[0]
 
 
+def _key(kernel, grid=None, wg=None):
+    """A kernel's short name, and its workgroup count when the database gives
+    the launch shape: one kernel launched at several shapes gets a row per
+    shape."""
+    k = _short_name(kernel)
+    if grid and wg:
+        k += " @%dwg" % (grid // wg)
+    return k
+
+
 def summarize_trace(db_path):
-    """Per-kernel count / total / average / min / max duration (us) from a
-    rocprofv3 results database."""
+    """Per-kernel (and launch shape) count / total / average / min / max /
+    median duration (us) from a rocprofv3 results database."""
     import sqlite3
     db = sqlite3.connect(db_path)
-    rows = db.execute("select name, duration from kernels").fetchall()
+    try:
+        rows = db.execute("select name, duration, grid_x * grid_y * grid_z, "
+                          "workgroup_x * workgroup_y * workgroup_z from kernels").fetchall()
+    except sqlite3.OperationalError:
+        rows = [(n, d, None, None) for n, d in
+                db.execute("select name, duration from kernels").fetchall()]
     by = {}
-    for name, dur in rows:
-        by.setdefault(_short_name(name), []).append(dur / 1e3)
-    lines = ["| kernel | calls | total us | avg us | min us | max us |",
-             "|---|---|---|---|---|---|"]
+    for name, dur, grid, wg in rows:
+        by.setdefault(_key(name, grid, wg), []).append(dur / 1e3)
+    lines = ["| kernel | calls | total us | avg us | min us | max us | median us |",
+             "|---|---|---|---|---|---|---|"]
     for k, d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
         d = np.array(d)
-        lines.append("| %s | %d | %.1f | %.3f | %.3f | %.3f |" %
-                     (k, len(d), d.sum(), d.mean(), d.min(), d.max()))
+        lines.append("| %s | %d | %.1f | %.3f | %.3f | %.3f | %.3f |" %
+                     (k, len(d), d.sum(), d.mean(), d.min(), d.max(), np.median(d)))
     return "\n".join(lines)
 
 
 def _counter_dispatches(db_path, counter):
-    """Per kernel name: {dispatch id: the counter summed over its instances}."""
+    """Per kernel key: {dispatch id: the counter summed over its instances}."""
     import sqlite3
     db = sqlite3.connect(db_path)
-    rows = db.execute("select kernel_name, dispatch_id, value from counters_collection "
-                      "where counter_name = ?", (counter,)).fetchall()
+    try:
+        rows = db.execute("select kernel_name, dispatch_id, value, grid_size, workgroup_size "
+                          "from counters_collection where counter_name = ?",
+                          (counter,)).fetchall()
+    except sqlite3.OperationalError:
+        rows = [r + (None, None) for r in
+                db.execute("select kernel_name, dispatch_id, value from counters_collection "
+                           "where counter_name = ?", (counter,)).fetchall()]
     per = {}
-    for name, disp, v in rows:
-        per.setdefault(_short_name(name), {}).setdefault(disp, 0.0)
-        per[_short_name(name)][disp] += v
+    for name, disp, v, grid, wg in rows:
+        k = _key(name, grid, wg)
+        per.setdefault(k, {}).setdefault(disp, 0.0)
+        per[k][disp] += v
     return per
 
 
@@ -247,15 +362,14 @@ def write_traffic(fetch_db, write_db):
     fetch_d = _counter_dispatches(fetch_db, "FETCH_SIZE")
     write_d = _counter_dispatches(write_db, "WRITE_SIZE")
     fetch, write = _median_per_kernel(fetch_d), _median_per_kernel(write_d)
-    copy = [k for k in write_d if "copyBuffer" in k]
-    if not copy:
+    copies = [(k, d) for k in write_d if "copyBuffer" in k for d in write_d[k]]
+    if not copies:
         sys.exit("no copy kernel in the trace: run with --copy-calibration")
-    ck = copy[0]
     nbytes = CALIBRATION_BYTES
     # The calibration copy is the copy dispatch that wrote closest to its
     # size (input uploads are smaller, the copy-rate context larger); both
     # runs execute the same program, so it has the same dispatch id in each.
-    disp = min(write_d[ck], key=lambda d: abs(write_d[ck][d] * 1024.0 - nbytes))
+    ck, disp = min(copies, key=lambda kd: abs(write_d[kd[0]][kd[1]] * 1024.0 - nbytes))
     if disp not in fetch_d.get(ck, {}):
         sys.exit("calibration copy (dispatch %d) missing from the FETCH_SIZE run" % disp)
     fetch[ck], write[ck] = fetch_d[ck][disp], write_d[ck][disp]
@@ -264,7 +378,8 @@ def write_traffic(fetch_db, write_db):
     out = []
     q2_srcs = ("gemv_packed.hip", "wave.hpp")
     for match, fname, srcs, alg in (
-            (lambda n: n.startswith("gemm_f32_direct<64, 64, true, false, 2,"),
+            (lambda n: n.startswith("gemm_f32_direct<64, 64, true, false, 2,")
+             and ("@" not in n or n.endswith(" @%dwg" % (GEMM_N // 64) ** 2)),
              "traffic_gemm_f32_2048.json", ("gemm_f32.hip",), 3 * 4 * GEMM_N * GEMM_N),
             (lambda n: n.startswith("gemv_packed_flat<2, 1, 1,"),
              "traffic_gemv_q2_12288x1536.json", q2_srcs, Q2_ALG_BYTES),
@@ -276,7 +391,8 @@ def write_traffic(fetch_db, write_db):
             (lambda n: n.startswith("gemv_packed_flat<4, 8, 64,"),
              "traffic_gemv_q4_batched_12288x1536.json", q2_srcs,
              CALLS_PER_TOKEN * Q4_ALG_BYTES),
-            (lambda n: n.startswith("gemv_packed_kernel<2, 256, 6,") and n.endswith(", 1>"),
+            (lambda n: n.startswith("gemv_packed_kernel<2, 256, 6,")
+             and n.split(" @")[0].endswith(", 1>"),
              "traffic_gemv_q2_1536x12288.json", q2_srcs, QT_ALG_BYTES),
             (lambda n: n.startswith("gemv_f32_kernel<1, 6, true>"),
              "traffic_gemv_f32_12288x1536.json", ("gemv_f32.hip", "wave.hpp"), F32_ALG_BYTES)):
@@ -648,6 +764,8 @@ def main():
     del csrc, cdst
     vendor = vendor_context(torch, stream, capture, timed, token_runner, n_tok, gemms_per_replay,
                             dA, dB, Wf, dxf, A, B, args)
+    configs, configs_ok = gemm_configs(torch, bd, inputs, oracle, dev, stream, capture, timed,
+                                       args.steps)
 
     gemm_tflops = GEMM_FLOPS / gemm_us / 1e6
     q2_gbs = Q2_WEIGHT_BYTES / q2_us / 1e3
@@ -809,6 +927,7 @@ def main():
                 "traffic": gf_traffic,
             },
         },
+        "gemm_configs": configs,
         "spread": spreads,
         "context": {
             "q2_gemv_hot_us": q2_hot_us,
@@ -820,6 +939,7 @@ def main():
             "vendor_library": vendor,
         },
         "parity": {"gemm_f32_2048": "pass" if gemm_ok else "FAIL",
+                   "gemm_configs": "pass" if configs_ok else "FAIL",
                    "gemv_f32": "pass" if gf_ok else "FAIL",
                    "gemv_f32_worst_err_over_bound": gf_worst,
                    "gemv_q2_transposed": "pass" if qt_ok else "FAIL",
@@ -842,7 +962,8 @@ def main():
         "wall_s_timed": t_wall,
     }
     print(json.dumps(out), flush=True)
-    return 0 if (gemm_ok and q2_ok and qb_ok and q4_ok and q4b_ok and qt_ok and gf_ok) else 1
+    return 0 if (gemm_ok and q2_ok and qb_ok and q4_ok and q4b_ok and qt_ok and gf_ok
+                 and configs_ok) else 1
 
 
 if __name__ == "__main__":

@@ -57,6 +57,7 @@ def test_summarize_trace(bench, tmp_path):
     assert float(cells[2]) == pytest.approx(264.0)       # total us
     assert float(cells[3]) == pytest.approx(132.0)       # average us
     assert float(cells[4]) == pytest.approx(130.0) and float(cells[5]) == pytest.approx(134.0)
+    assert float(cells[6]) == pytest.approx(132.0)       # median us
     assert lines[2].find("gemm") > 0                     # sorted by total time
 
 
@@ -86,6 +87,63 @@ def test_traffic_uses_the_calibration_copy(bench, tmp_path, monkeypatch):
     expect = 41000.0 * 1024 * 2.0 + 16384.0 * 1024
     assert d["hbm_bytes_per_launch"] == pytest.approx(expect)
     assert d["traffic_over_algorithmic"] == pytest.approx(expect / (3 * 4 * 2048 * 2048))
+
+
+def _trace_db_shapes(path, rows):
+    """rows: (name, duration, grid work-items, workgroup size)"""
+    db = sqlite3.connect(path)
+    db.execute("create table kernels (name text, duration integer, grid_x integer, "
+               "grid_y integer, grid_z integer, workgroup_x integer, workgroup_y integer, "
+               "workgroup_z integer)")
+    db.executemany("insert into kernels values (?, ?, ?, 1, 1, ?, 1, 1)", rows)
+    db.commit()
+    db.close()
+
+
+def _counter_db_shapes(path, counter, rows):
+    """rows: (kernel name, dispatch id, value in KiB, grid work-items, workgroup size)"""
+    db = sqlite3.connect(path)
+    db.execute("create table counters_collection (kernel_name text, dispatch_id integer, "
+               "counter_name text, value real, grid_size integer, workgroup_size integer)")
+    db.executemany("insert into counters_collection values (?, ?, ?, ?, ?, ?)",
+                   [(k, d, counter, v, g, w) for k, d, v, g, w in rows])
+    db.commit()
+    db.close()
+
+
+def test_one_kernel_at_two_shapes(bench, tmp_path, monkeypatch):
+    """The same GEMM kernel launched at 1,024 workgroups (2048^3) and at 768
+    (a smaller product) gives a trace row per shape, and the traffic of the
+    2048^3 launches alone."""
+    p = str(tmp_path / "t.db")
+    _trace_db_shapes(p, [(GEMM, 130000, 524288, 512), (GEMM, 134000, 524288, 512),
+                         (GEMM, 40000, 393216, 512)])
+    lines = bench.summarize_trace(p).splitlines()
+    big = [l for l in lines if "@1024wg" in l][0]
+    small = [l for l in lines if "@768wg" in l][0]
+    assert float(big.strip("|").split("|")[3]) == pytest.approx(132.0)
+    assert float(small.strip("|").split("|")[3]) == pytest.approx(40.0)
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    cal = bench.CALIBRATION_BYTES // 1024
+    # copies at two shapes: the upload (small) and the calibration copy
+    fetch_rows = [(COPY, 5, 100.0, 512, 512), (COPY, 36, cal / 2.0, 65536, 512)]
+    write_rows = [(COPY, 5, 200.0, 512, 512), (COPY, 36, float(cal), 65536, 512)]
+    for d in (40, 41, 42):
+        fetch_rows.append((GEMM, d, 40000.0, 524288, 512))
+        write_rows.append((GEMM, d, 16384.0, 524288, 512))
+    for d in (50, 51):
+        fetch_rows.append((GEMM, d, 9000.0, 393216, 512))
+        write_rows.append((GEMM, d, 3000.0, 393216, 512))
+    fdb, wdb = str(tmp_path / "f.db"), str(tmp_path / "w.db")
+    _counter_db_shapes(fdb, "FETCH_SIZE", fetch_rows)
+    _counter_db_shapes(wdb, "WRITE_SIZE", write_rows)
+    assert bench.write_traffic(fdb, wdb) == 0
+    with open(tmp_path / "traffic_gemm_f32_2048.json") as f:
+        d = json.load(f)
+    assert d["kernel"].endswith("@1024wg")
+    assert d["fetch_kib_raw"] == pytest.approx(40000.0)
+    assert d["write_kib_raw"] == pytest.approx(16384.0)
+    assert d["fetch_scale"] == pytest.approx(2.0)
 
 
 def test_traffic_gated_by_source_hash(bench, tmp_path, monkeypatch):
