@@ -318,11 +318,15 @@ struct DirectOperand {
     static constexpr int STAGE = TX * BK * 4;     // bytes per stage
     static constexpr int NI = STAGE / 1024 / WPG; // loads per wave per slab
     static_assert(NI >= 1 && NI * 1024 * WPG == STAGE, "tile must split over the waves");
-    // k-major rows swap their two 128-byte halves on every other group of
-    // four rows, so that the two half-waves of a fragment read (4 rows
-    // apart) use different banks; rows of 32 floats have no second half and
-    // take 2-way conflicts instead.
-    static constexpr int KSW = TX >= 64 ? 8 : 0;
+    // k-major rows of CPR 16-byte chunks turn by 8 chunks (128 bytes) on
+    // every other group of four rows, so that the two half-waves of a
+    // fragment read (4 rows apart) use different banks; rows of 32 floats
+    // have no second half and take 2-way conflicts instead.
+    static constexpr int CPR = TX / 4;
+    static_assert(XMAJOR || CPR % 8 == 0, "k-major tiles are a multiple of 32 wide");
+    static __device__ __forceinline__ int kslot(int c, int row) {
+        return (c + 8 * ((row >> 2) & 1)) % CPR;
+    }
     unsigned voff[NI];   // byte offset of this lane's chunk at k = 0
     int kof[NI];         // k of this lane's chunk (x-major) or row (k-major) in the slab
 
@@ -336,10 +340,11 @@ struct DirectOperand {
                 voff[j] = (unsigned)(((int64_t)min(x0 + row, X - 1) * ld + 4 * c) * 4);
                 kof[j] = 4 * c;
             } else {
-                constexpr int CPR = TX / 4;       // chunks per row
-                constexpr int RPB = 64 / CPR;     // rows per 1 KB block
-                const int row = RPB * blk + lane / CPR;
-                const int c = (lane % CPR) ^ (KSW * ((row >> 2) & 1));
+                // the lane writes LDS chunk q of the stage (row q / CPR, slot
+                // q % CPR), so it fetches the chunk of that row whose slot it is
+                const int q = 64 * blk + lane;
+                const int row = q / CPR;
+                const int c = (q % CPR + CPR - 8 * ((row >> 2) & 1) % CPR) % CPR;
                 voff[j] = (unsigned)(((int64_t)row * ld + min(x0 + 4 * c, X - 4)) * 4);
                 kof[j] = row;
             }
@@ -378,7 +383,7 @@ struct DirectOperand {
             return r * 128 + (((2 * g + h) ^ xswz(r)) * 16);
         }
         const int x = xb + l32;
-        return (8 * g + 4 * h) * TX * 4 + (((x >> 2) ^ (KSW * h)) * 16) + (x & 3) * 4;
+        return (8 * g + 4 * h) * TX * 4 + kslot(x >> 2, 4 * h) * 16 + (x & 3) * 4;
     }
     static __device__ __forceinline__ v4f frag(const char *stage, int off) {
         if (XMAJOR) return *reinterpret_cast<const v4f *>(stage + off);

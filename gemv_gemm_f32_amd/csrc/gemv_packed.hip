@@ -378,21 +378,26 @@ struct Flat {
     };
 
     // Set-up, one unit of 16 columns per lane: load_x fetches the unit's x
-    // (lanes past the last unit fetch the last one again, so the loads need
-    // no predicate); stage turns them into the chain start -z 2^(K0-24) X
-    // and the x values scaled for their codes' bit positions, in LDS, and
-    // after a barrier each lane takes those of its chunk c.
+    // (lanes past the last unit fetch nothing: every workgroup reads x, so
+    // its loads are a large share of the set-up's traffic); stage turns them
+    // into the chain start -z 2^(K0-24) X and the x values scaled for their
+    // codes' bit positions, in LDS, and after a barrier each lane takes those
+    // of its chunk c.
     static __device__ __forceinline__ void load_x(const float *__restrict__ x, int cpr, int f,
                                                   float (&v)[16]) {
-        const int u = f < cpr * UPC ? f : cpr * UPC - 1;
-        const v4f *xp = reinterpret_cast<const v4f *>(x) + 4 * u;
+        if (f < cpr * UPC) {
+            const v4f *xp = reinterpret_cast<const v4f *>(x) + 4 * f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const v4f t = xp[q];
-            v[4 * q] = t.x;
-            v[4 * q + 1] = t.y;
-            v[4 * q + 2] = t.z;
-            v[4 * q + 3] = t.w;
+            for (int q = 0; q < 4; ++q) {
+                const v4f t = xp[q];
+                v[4 * q] = t.x;
+                v[4 * q + 1] = t.y;
+                v[4 * q + 2] = t.z;
+                v[4 * q + 3] = t.w;
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < 16; ++p) v[p] = 0.f;
         }
     }
     static __device__ __forceinline__ void stage(const float (&v)[16], int cpr, int f, int c,
