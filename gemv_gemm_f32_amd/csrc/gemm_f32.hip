@@ -576,27 +576,33 @@ hipError_t launch_direct(int M, int N, int K, float alpha, const float *A, int64
     return hipGetLastError();
 }
 
-// Narrow tiles: 64 x 32 when A is x-major, else 32 x 64, so the narrow side
-// falls on B in A . B and A . B^T and on A in A^T . B and A^T . B^T; two
-// waves per k-group, KS k-groups.
-template <bool AX, bool BX>
+// Narrow tiles, 64 x 32 (TALL) or 32 x 64, with two waves per k-group and
+// KS k-groups (6 fill 144 KiB of LDS).
+template <bool AX, bool BX, bool TALL>
 hipError_t launch_half(int ks, int M, int N, int K, float alpha, const float *A, int64_t lda,
                        const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
                        hipStream_t s) {
-    constexpr int BM = AX ? 64 : 32, BN = AX ? 32 : 64;
-    return ks == 4 ? launch_direct<AX, BX, BM, BN, 4, 2>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s)
-           : ks == 2 ? launch_direct<AX, BX, BM, BN, 2, 2>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s)
-                     : launch_direct<AX, BX, BM, BN, 1, 2>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    constexpr int BM = TALL ? 64 : 32, BN = TALL ? 32 : 64;
+    switch (ks) {
+    case 6: return launch_direct<AX, BX, BM, BN, 6, 2>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    case 4: return launch_direct<AX, BX, BM, BN, 4, 2>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    case 2: return launch_direct<AX, BX, BM, BN, 2, 2>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    default: return launch_direct<AX, BX, BM, BN, 1, 2>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    }
 }
 
-// Quarter tiles: 32 x 32, one wave per k-group, KS k-groups.
+// Quarter tiles: 32 x 32, one wave per k-group, KS k-groups (8 fill 128 KiB
+// of LDS).
 template <bool AX, bool BX>
 hipError_t launch_quarter(int ks, int M, int N, int K, float alpha, const float *A, int64_t lda,
                           const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
                           hipStream_t s) {
-    return ks == 4 ? launch_direct<AX, BX, 32, 32, 4, 1>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s)
-           : ks == 2 ? launch_direct<AX, BX, 32, 32, 2, 1>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s)
-                     : launch_direct<AX, BX, 32, 32, 1, 1>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    switch (ks) {
+    case 8: return launch_direct<AX, BX, 32, 32, 8, 1>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    case 4: return launch_direct<AX, BX, 32, 32, 4, 1>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    case 2: return launch_direct<AX, BX, 32, 32, 2, 1>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    default: return launch_direct<AX, BX, 32, 32, 1, 1>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    }
 }
 
 constexpr int PROD_BK = 32;
@@ -647,11 +653,15 @@ hipError_t launch_gemm(bool ax, bool bx, int M, int N, int K, float alpha, const
     // Smaller tiles where 64 x 64 balances badly over the CUs.  The largest
     // per-CU share of tiles is ceil(tiles / CUs); a narrow tile (64 x 32 or
     // 32 x 64) costs about half a 64 x 64 one, a little more than half on a
-    // busy CU.
+    // busy CU.  Of the two narrow shapes the one whose grid pads M and N
+    // less is taken, on a tie 64 x 32 when A is x-major (A . B, A . B^T)
+    // and 32 x 64 otherwise.
     //  - Small grids (64 x 64 tiles for fewer than half the CUs): 32 x 32
-    //    tiles when those still fit one per CU, else narrow tiles, with
-    //    the k-slabs split four ways where K allows.  256^3 took 6.3 -> 5.5
-    //    us and 500 x 500 x 2000 23.5 -> 18.4 us with 32 x 32 tiles.
+    //    tiles when those still fit one per CU, else narrow tiles, with the
+    //    k-slabs split over as many groups as the LDS holds: 8 for 32 x 32
+    //    (500 x 500 x 2000: 24.0 us with 64 x 32 tiles, 18.4 with 32 x 32 in
+    //    4 groups, 15.3 in 8) and 6 for narrow tiles (346 x 768 x 768: 11.8
+    //    us for 64 x 32 in 4 groups, 10.9 for 32 x 64 in 6).
     //  - More tiles than CUs: narrow tiles when the share of 64 x 64 tiles
     //    is at least 1.2 times that of narrow ones in 64 x 64 units, i.e. a
     //    last round of 64 x 64 tiles that would leave most CUs idle.  On
@@ -659,18 +669,22 @@ hipError_t launch_gemm(bool ax, bool bx, int M, int N, int K, float alpha, const
     //    1024 (304 tiles) 35.1 -> 31.2 us; 432, 700, 768 and 1024 tiles
     //    stay on 64 x 64, where narrow tiles measured 6-24% slower.
     const int64_t tiles_32 = (int64_t)((M + 31) / 32) * ((N + 31) / 32);
-    const int64_t tiles_h = ax ? (int64_t)((M + 63) / 64) * ((N + 31) / 32)
-                               : (int64_t)((M + 31) / 32) * ((N + 63) / 64);
+    const int64_t pad_tall = (int64_t)((M + 63) / 64) * ((N + 31) / 32) * 2;   // in 32 x 32 units
+    const int64_t pad_wide = (int64_t)((M + 31) / 32) * ((N + 63) / 64) * 2;
+    const bool tall = pad_tall < pad_wide || (pad_tall == pad_wide && ax);
+    const int64_t tiles_h = (tall ? pad_tall : pad_wide) / 2;
     const auto share = [num_cus](int64_t t) { return (t + num_cus - 1) / num_cus; };
     const bool small = tiles_64 * 2 < (int64_t)num_cus;
     const bool quarter = small && tiles_32 <= (int64_t)num_cus;
     const bool half = small ? !quarter
                             : tiles_64 > (int64_t)num_cus && 10 * share(tiles_64) >= 6 * share(tiles_h);
-    const int kss = slabs >= 8 ? 4 : (slabs >= 4 ? 2 : 1);
+    const int ksq = slabs >= 8 ? 8 : (slabs >= 4 ? 4 : (slabs >= 2 ? 2 : 1));
+    const int ksh = !small ? ks : (slabs >= 12 ? 6 : (slabs >= 8 ? 4 : (slabs >= 4 ? 2 : 1)));
 #define GG_ARGS M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s
 #define GG_GEMM_DIRECT(AX_, BX_)                                                     \
-    if (quarter) return launch_quarter<AX_, BX_>(kss, GG_ARGS);                    \
-    if (half) return launch_half<AX_, BX_>(small ? kss : ks, GG_ARGS);             \
+    if (quarter) return launch_quarter<AX_, BX_>(ksq, GG_ARGS);                    \
+    if (half) return tall ? launch_half<AX_, BX_, true>(ksh, GG_ARGS)              \
+                          : launch_half<AX_, BX_, false>(ksh, GG_ARGS);            \
     return ks == 4 ? launch_direct<AX_, BX_, 64, 64, 4>(GG_ARGS)                  \
            : ks == 2 ? launch_direct<AX_, BX_, 64, 64, 2>(GG_ARGS)                \
                      : launch_direct<AX_, BX_, 64, 64, 1>(GG_ARGS);

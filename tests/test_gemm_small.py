@@ -1,7 +1,7 @@
 """GPU parity of the GEMM on small grids, where a 64 x 64 tile grid would
 cover fewer than half the compute units: such products take 32 x 32 tiles
-when those fit one per CU, else narrow tiles (64 x 32 when A is x-major,
-else 32 x 64) with two waves per k-group.  All four transpose pairs against
+when those fit one per CU, else narrow tiles (64 x 32 or 32 x 64, whichever
+pads less) with two waves per k-group.  All four transpose pairs against
 the oracle on every element, at the classifier shape (346 x 768 x 768, narrow
 tiles), ragged and tiny shapes, a K tail inside a slab, K below one slab,
 K-heavy products split over four k-groups, alpha/beta, and padded leading

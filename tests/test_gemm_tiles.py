@@ -1,12 +1,14 @@
 """GPU parity of the GEMM's smaller direct-load tiles, chosen by how evenly a
 grid spreads over the compute units: 32 x 32 tiles on small grids that fit
-one per CU, narrow tiles (64 x 32 when A is x-major, else 32 x 64) on small
-grids that do not and on grids whose last round of 64 x 64 tiles would leave
-most CUs idle.  All four transpose pairs are checked against the oracle on
-every element, with ragged tile edges, K tails inside a slab, one to four
-k-groups, alpha/beta and padded leading dimensions.  The helper `regime`
-restates the launcher's choice so that each case is known to reach the
-tiles it is meant for."""
+one per CU, narrow tiles (64 x 32 or 32 x 64, whichever pads M and N less;
+on a tie 64 x 32 when A is x-major) on small grids that do not and on
+grids whose last round of 64 x 64 tiles would leave most CUs idle.  Small
+grids split the k-slabs over up to 8 groups (32 x 32) or 6 (narrow).  All
+four transpose pairs are checked against the oracle on every element, with
+ragged tile edges, K tails inside a slab, one to eight k-groups, alpha/beta
+and padded leading dimensions.  The helper `regime` restates the
+launcher's choice so that each case is known to reach the tiles it is
+meant for."""
 import numpy as np
 import pytest
 
@@ -31,7 +33,8 @@ def regime(M, N, K, ta, cus):
     cdiv = lambda a, b: -(-a // b)
     t64 = cdiv(M, 64) * cdiv(N, 64)
     t32 = cdiv(M, 32) * cdiv(N, 32)
-    th = cdiv(M, 32) * cdiv(N, 64) if ta else cdiv(M, 64) * cdiv(N, 32)
+    tall, wide = cdiv(M, 64) * cdiv(N, 32), cdiv(M, 32) * cdiv(N, 64)
+    th = tall if tall < wide or (tall == wide and not ta) else wide
     if 2 * t64 < cus:
         return "quarter" if t32 <= cus else "half"
     if t64 > cus and 10 * cdiv(t64, cus) >= 6 * cdiv(th, cus):
@@ -44,11 +47,13 @@ def _ops(ta, tb, M, N, K, gen):
 
 
 CASES = [
-    # quarter tiles: one to four k-groups, ragged edges, K tails
+    # quarter tiles: one to eight k-groups, ragged edges, K tails
     ("quarter", 100, 200, 1028), ("quarter", 33, 68, 36), ("quarter", 132, 36, 100),
     ("quarter", 500, 500, 2000), ("quarter", 256, 256, 256), ("quarter", 4, 4, 4),
-    # narrow tiles on a small grid
-    ("half", 500, 600, 100), ("half", 348, 772, 772),
+    # narrow tiles on a small grid: 64 x 32 (500 rows) and 32 x 64 (348
+    # rows) with 1, 2, 4 and 6 k-groups
+    ("half", 500, 600, 100), ("half", 348, 772, 772), ("half", 500, 600, 300),
+    ("half", 500, 600, 60),
     # narrow tiles on a grid a little larger than the CUs, K tail in a slab
     ("half", 1000, 1212, 300), ("half", 1024, 1216, 60),
 ]
