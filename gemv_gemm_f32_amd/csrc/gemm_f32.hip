@@ -345,7 +345,10 @@ struct DirectOperand {
                 const int q = 64 * blk + lane;
                 const int row = q / CPR;
                 const int c = (q % CPR + CPR - 8 * ((row >> 2) & 1) % CPR) % CPR;
-                voff[j] = (unsigned)(((int64_t)row * ld + min(x0 + 4 * c, X - 4)) * 4);
+                // chunks past the row's last one load that one (their columns
+                // are never stored); the last one may run past X into the next
+                // row, or past the operand's end, which reads zeros
+                voff[j] = (unsigned)(((int64_t)row * ld + min(x0 + 4 * c, (X - 1) & ~3)) * 4);
                 kof[j] = row;
             }
         }
@@ -367,13 +370,20 @@ struct DirectOperand {
                 rsrc, (lds_void *)(stage + (WPG * j + wave) * 1024), 16, voff[j], so, 0, 0);
 #endif
     }
-    // after this wave's loads of the slab at k0 have landed: zero what lies at k >= K
+    // after this wave's loads of the slab at k0 have landed: zero what lies at
+    // k >= K (whole chunks, and in x-major rows the part of a chunk past K
+    // when K is not a multiple of 4)
     __device__ __forceinline__ void zero_tail(char *stage, int k0, int K, int wave, int lane) const {
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
-            if (k0 + kof[j] >= K)
-                *reinterpret_cast<v4f *>(stage + (WPG * j + wave) * 1024 + lane * 16) =
-                    v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NI; ++j) {
+            float *p = reinterpret_cast<float *>(stage + (WPG * j + wave) * 1024 + lane * 16);
+            const int k = k0 + kof[j];
+            if (k >= K) {
+                *reinterpret_cast<v4f *>(p) = v4f{0.f, 0.f, 0.f, 0.f};
+            } else if (XMAJOR && k + 4 > K) {
+                for (int e = K - k; e < 4; ++e) p[e] = 0.f;
+            }
+        }
     }
     // byte offset, within a stage, of lane (l32, h)'s operand of k-group g
     // for the 32-block at x = xb
@@ -627,8 +637,9 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 hipError_t launch_gemm(bool ax, bool bx, int M, int N, int K, float alpha, const float *A,
                        int64_t lda, const float *B, int64_t ldb, float beta, float *C,
                        int64_t ldc, int num_cus, hipStream_t s) {
-    // 16-byte loads need the operand's contiguous extent, its leading
-    // dimension and its base all to be multiples of 4 floats.
+    // The staged path's 16-byte register loads need the operand's contiguous
+    // extent, its leading dimension and its base all to be multiples of 4
+    // floats; otherwise it loads floats one by one.
     const int a_contig = ax ? K : M;
     const int b_contig = bx ? K : N;
     const bool va = aligned16(A) && (lda % 4 == 0) && (a_contig % 4 == 0);
@@ -637,7 +648,10 @@ hipError_t launch_gemm(bool ax, bool bx, int M, int N, int K, float alpha, const
     auto extent = [](bool xmajor, int X, int64_t ld, int K) {
         return xmajor ? ((int64_t)(X - 1) * ld + K) * 4 : ((int64_t)(K - 1) * ld + X) * 4;
     };
-    const bool direct = va && vb && K > 0 && extent(ax, M, lda, K) < (int64_t(1) << 31) &&
+    // Its 16-byte loads need only 4-byte aligned addresses (rows of any
+    // width and leading dimension), and the buffer range check is per dword,
+    // so a chunk that runs past an operand's last element reads zeros there.
+    const bool direct = K > 0 && extent(ax, M, lda, K) < (int64_t(1) << 31) &&
                         extent(bx, N, ldb, K) < (int64_t(1) << 31);
     // Staged path: 128 x 64 tiles when that grid still gives every CU two
     // tiles to interleave; otherwise 64 x 64, which keeps small and K-heavy

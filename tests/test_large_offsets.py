@@ -59,6 +59,8 @@ GEMM_CASES = [
     ("nt", 256, 2048, 256, "B", 262140),    # direct, x-major B
     ("nn", 256, 256, 2048, "B", 262140),    # direct, k-major B
     ("nn", 256, 256, 2048, "B", 262400),    # staged
+    ("nn", 2048, 256, 256, "A", 262401),    # staged, rows not 16-byte aligned
+    ("nn", 256, 256, 2048, "B", 262401),    # staged, rows not 16-byte aligned
 ]
 
 
