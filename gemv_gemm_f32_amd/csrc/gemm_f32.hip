@@ -312,7 +312,8 @@ __device__ __forceinline__ int xswz(int r) { return (r ^ (r >> 3)) & 7; }
 // WPG*j + w of the stage.
 //   XMAJOR: element (x, k) at P[x*ld + k]; the stage holds TX rows of 128 B.
 //   else  : element (x, k) at P[k*ld + x]; the stage holds 32 rows of TX*4 B.
-template <int TX, bool XMAJOR, int WPG = 4>
+// KT: K is not a multiple of 4, so an x-major chunk can straddle K.
+template <int TX, bool XMAJOR, int WPG = 4, bool KT = false>
 struct DirectOperand {
     static constexpr int BK = 32;
     static constexpr int STAGE = TX * BK * 4;     // bytes per stage
@@ -380,7 +381,7 @@ struct DirectOperand {
             const int k = k0 + kof[j];
             if (k >= K) {
                 *reinterpret_cast<v4f *>(p) = v4f{0.f, 0.f, 0.f, 0.f};
-            } else if (XMAJOR && k + 4 > K) {
+            } else if (XMAJOR && KT && k + 4 > K) {
                 for (int e = K - k; e < 4; ++e) p[e] = 0.f;
             }
         }
@@ -409,7 +410,7 @@ struct DirectOperand {
 // WPG waves of a group lay out as 2 x 2 (WPG = 4), 1 x 2 or 2 x 1 (WPG = 2,
 // along the longer side of the tile) or 1 x 1 over the tile, each wave
 // holding 32 x 32 MFMA blocks.
-template <int BM, int BN, bool AX, bool BX, int KS, int WPG = 4>
+template <int BM, int BN, bool AX, bool BX, int KS, int WPG = 4, bool KT = false>
 __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
     int M, int N, int K, float alpha, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
@@ -420,8 +421,8 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
     constexpr int WM = BM / WR, WN = BN / WC;
     constexpr int IB = WM / 32, JB = WN / 32;
     static_assert(IB * 32 == WM && JB * 32 == WN && WR * WC == WPG, "tile must split into 32-blocks");
-    using OA = DirectOperand<BM, AX, WPG>;
-    using OB = DirectOperand<BN, BX, WPG>;
+    using OA = DirectOperand<BM, AX, WPG, KT>;
+    using OB = DirectOperand<BN, BX, WPG, KT>;
     constexpr int STAGE = OA::STAGE + OB::STAGE;
     constexpr int ACCW = IB * JB * 16;            // accumulator words per lane
     static_assert(KS == 1 || (KS - 1) * 64 * WPG * ACCW * 4 <= KS * 2 * STAGE,
@@ -575,12 +576,12 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
         }
 }
 
-template <bool AX, bool BX, int BM, int BN, int KS = 1, int WPG = 4>
+template <bool AX, bool BX, int BM, int BN, int KS = 1, int WPG = 4, bool KT = false>
 hipError_t launch_direct(int M, int N, int K, float alpha, const float *A, int64_t lda,
                          const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
                          hipStream_t s) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    hipLaunchKernelGGL((gemm_f32_direct<BM, BN, AX, BX, KS, WPG>), dim3(tiles_m * tiles_n),
+    hipLaunchKernelGGL((gemm_f32_direct<BM, BN, AX, BX, KS, WPG, KT>), dim3(tiles_m * tiles_n),
                        dim3(64 * WPG * KS), 0, s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                        tiles_m, tiles_n);
     return hipGetLastError();
@@ -588,31 +589,45 @@ hipError_t launch_direct(int M, int N, int K, float alpha, const float *A, int64
 
 // Narrow tiles, 64 x 32 (TALL) or 32 x 64, with two waves per k-group and
 // KS k-groups (6 fill 144 KiB of LDS).
-template <bool AX, bool BX, bool TALL>
+template <bool AX, bool BX, bool TALL, bool KT>
 hipError_t launch_half(int ks, int M, int N, int K, float alpha, const float *A, int64_t lda,
                        const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
                        hipStream_t s) {
     constexpr int BM = TALL ? 64 : 32, BN = TALL ? 32 : 64;
     switch (ks) {
-    case 6: return launch_direct<AX, BX, BM, BN, 6, 2>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
-    case 4: return launch_direct<AX, BX, BM, BN, 4, 2>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
-    case 2: return launch_direct<AX, BX, BM, BN, 2, 2>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
-    default: return launch_direct<AX, BX, BM, BN, 1, 2>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    case 6: return launch_direct<AX, BX, BM, BN, 6, 2, KT>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    case 4: return launch_direct<AX, BX, BM, BN, 4, 2, KT>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    case 2: return launch_direct<AX, BX, BM, BN, 2, 2, KT>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    default: return launch_direct<AX, BX, BM, BN, 1, 2, KT>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
     }
 }
 
 // Quarter tiles: 32 x 32, one wave per k-group, KS k-groups (8 fill 128 KiB
 // of LDS).
-template <bool AX, bool BX>
+template <bool AX, bool BX, bool KT>
 hipError_t launch_quarter(int ks, int M, int N, int K, float alpha, const float *A, int64_t lda,
                           const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
                           hipStream_t s) {
     switch (ks) {
-    case 8: return launch_direct<AX, BX, 32, 32, 8, 1>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
-    case 4: return launch_direct<AX, BX, 32, 32, 4, 1>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
-    case 2: return launch_direct<AX, BX, 32, 32, 2, 1>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
-    default: return launch_direct<AX, BX, 32, 32, 1, 1>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    case 8: return launch_direct<AX, BX, 32, 32, 8, 1, KT>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    case 4: return launch_direct<AX, BX, 32, 32, 4, 1, KT>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    case 2: return launch_direct<AX, BX, 32, 32, 2, 1, KT>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    default: return launch_direct<AX, BX, 32, 32, 1, 1, KT>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
     }
+}
+
+// The direct kernel for a tile choice made by launch_gemm.
+template <bool AX, bool BX, bool KT>
+hipError_t launch_pick(bool quarter, bool half, bool tall, int ksq, int ksh, int ks, int M, int N,
+                       int K, float alpha, const float *A, int64_t lda, const float *B,
+                       int64_t ldb, float beta, float *C, int64_t ldc, hipStream_t s) {
+    if (quarter) return launch_quarter<AX, BX, KT>(ksq, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    if (half)
+        return tall ? launch_half<AX, BX, true, KT>(ksh, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s)
+                    : launch_half<AX, BX, false, KT>(ksh, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    return ks == 4 ? launch_direct<AX, BX, 64, 64, 4, 4, KT>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s)
+           : ks == 2 ? launch_direct<AX, BX, 64, 64, 2, 4, KT>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s)
+                     : launch_direct<AX, BX, 64, 64, 1, 4, KT>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
 }
 
 constexpr int PROD_BK = 32;
@@ -696,12 +711,9 @@ hipError_t launch_gemm(bool ax, bool bx, int M, int N, int K, float alpha, const
     const int ksh = !small ? ks : (slabs >= 12 ? 6 : (slabs >= 8 ? 4 : (slabs >= 4 ? 2 : 1)));
 #define GG_ARGS M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s
 #define GG_GEMM_DIRECT(AX_, BX_)                                                     \
-    if (quarter) return launch_quarter<AX_, BX_>(ksq, GG_ARGS);                    \
-    if (half) return tall ? launch_half<AX_, BX_, true>(ksh, GG_ARGS)              \
-                          : launch_half<AX_, BX_, false>(ksh, GG_ARGS);            \
-    return ks == 4 ? launch_direct<AX_, BX_, 64, 64, 4>(GG_ARGS)                  \
-           : ks == 2 ? launch_direct<AX_, BX_, 64, 64, 2>(GG_ARGS)                \
-                     : launch_direct<AX_, BX_, 64, 64, 1>(GG_ARGS);
+    if (K % 4 != 0 && (AX_ || BX_))                                                  \
+        return launch_pick<AX_, BX_, true>(quarter, half, tall, ksq, ksh, ks, GG_ARGS); \
+    return launch_pick<AX_, BX_, false>(quarter, half, tall, ksq, ksh, ks, GG_ARGS);
 #define GG_GEMM_SHAPE(AX_, BX_, VA_, VB_)                                     \
     return big ? launch_t<AX_, BX_, VA_, VB_, 128, 64>(GG_ARGS)            \
                : launch_t<AX_, BX_, VA_, VB_, 64, 64>(GG_ARGS);
