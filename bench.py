@@ -404,7 +404,7 @@ def write_traffic(fetch_db, write_db):
             (lambda n: n.startswith("gemv_packed_flat<2, 8, 64,"),
              "traffic_gemv_q2_batched_12288x1536.json", q2_srcs,
              CALLS_PER_TOKEN * Q2_ALG_BYTES),
-            (lambda n: n.startswith("gemv_packed_flat<4, 4, 1,"),
+            (lambda n: n.startswith("gemv_packed_flat<4, 2, 1,"),
              "traffic_gemv_q4_12288x1536.json", q2_srcs, Q4_ALG_BYTES),
             (lambda n: n.startswith("gemv_packed_flat<4, 8, 64,"),
              "traffic_gemv_q4_batched_12288x1536.json", q2_srcs,

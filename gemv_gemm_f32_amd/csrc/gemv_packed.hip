@@ -609,14 +609,14 @@ int flat_cpr(int count, int M, int K, const uint8_t *const *Q, int64_t ldq, int6
 }
 
 // Steps per workgroup.  A single product needs many workgroups to fill the
-// chip: one step (2-bit) or four (4-bit, whose rows are twice as long).  A
+// chip: one step (2-bit) or two (4-bit, whose rows are twice as long).  A
 // batch has workgroups to spare: eight steps.  (A sweep of 1, 2 and 4 steps
 // for single products and 4 to 16 for batches of 40 at 12,288 x 1,536 put
 // the best there.)
-// The code loads go out before the x set-up's arithmetic except in single
-// 4-bit products (2% faster for the others, 1% slower there, same box).
-template <int BITS, int NB, int T = (NB == 1 ? (BITS == 2 ? 1 : 4) : 8),
-          bool EARLY = (NB != 1 || BITS == 2)>
+// The code loads go out before the x set-up's arithmetic (EARLY): 2% faster
+// for single 2-bit products and for batches, and, since x is loaded once per
+// unit, for single 4-bit products too (4.57 -> 4.45 us with two steps).
+template <int BITS, int NB, int T = (NB == 1 ? (BITS == 2 ? 1 : 2) : 8), bool EARLY = true>
 hipError_t launch_flat(int count, int M, int cpr, const uint8_t *const *Q, int64_t ldq,
                        const uint16_t *const *S, int64_t lds, const float *const *x,
                        float *const *y, hipStream_t s) {
