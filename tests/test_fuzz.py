@@ -1,6 +1,7 @@
-"""Seeded random cases through the C ABI against the CPU oracle: shapes,
-transpose pairs, alignment offsets, leading-dimension padding and alpha/beta
-for the matrix product; widths, shapes, padding, offsets and batch sizes for
+"""Seeded random cases through the C ABI against the CPU oracle: shapes on
+both sides of the tile, slab and tile-count boundaries, transpose pairs,
+alignment offsets, leading-dimension padding and alpha/beta for the matrix
+product; widths, shapes, padding, offsets and batch sizes for
 the packed matrix-vector products.  Each case is named by its seed."""
 import numpy as np
 import pytest
@@ -25,12 +26,13 @@ def _placed(a, offset, pad):
     return view
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(120))
 def test_gemm_random_cases(seed):
     rng = np.random.default_rng(1000 + seed)
-    M, N = (int(v) for v in rng.integers(1, 300, 2))
-    K = int(rng.integers(0, 400))
-    if rng.random() < 0.5:                       # the aligned (direct) path
+    hi = 1100 if seed % 4 == 3 else 300          # one case in four past the CU count
+    M, N = (int(v) for v in rng.integers(1, hi, 2))
+    K = int(rng.integers(0, 400 if hi > 300 else 1200))
+    if rng.random() < 0.5:                       # rows of whole 16-byte chunks
         M, N, K = (v + (-v) % 4 for v in (M, N, K))
     ta, tb = (bool(v) for v in rng.integers(0, 2, 2))
     alpha, beta = (float(v) for v in rng.choice([0.0, 1.0, -1.5, 0.5], 2))
