@@ -51,10 +51,23 @@ struct Span {
     uintptr_t lo, hi;
 };
 
+// Bytes from p to the end of the matrix's last element (sizes below 2^31,
+// so the product fits in 128 bits).
+unsigned __int128 extent_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t elem) {
+    if (rows <= 0 || cols <= 0) return 0;
+    return ((unsigned __int128)(rows - 1) * (uint64_t)ld + (uint64_t)cols) * (uint64_t)elem;
+}
+
+// A matrix whose bytes would run past the end of the address space.
+bool wraps(const void *p, int64_t rows, int64_t cols, int64_t ld, int64_t elem) {
+    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+    return extent_bytes(rows, cols, ld, elem) > (unsigned __int128)(UINTPTR_MAX - b);
+}
+
+// Only for matrices that do not wrap.
 Span span(const void *p, int64_t rows, int64_t cols, int64_t ld, int64_t elem) {
     const uintptr_t b = reinterpret_cast<uintptr_t>(p);
-    if (rows <= 0 || cols <= 0) return {b, b};
-    return {b, b + (uintptr_t)(((rows - 1) * ld + cols) * elem)};
+    return {b, b + (uintptr_t)extent_bytes(rows, cols, ld, elem)};
 }
 
 bool overlaps(Span a, Span b) {
@@ -82,6 +95,9 @@ int gemm_common(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha, 
     if (use_ab && (bad_ptr(A, 4) || bad_ptr(B, 4))) return GG_ERR_INVALID_ARG;
     if (ldc < N || ldc > kMaxDim) return GG_ERR_INVALID_ARG;
     if (use_ab && (lda < a_cols || ldb < b_cols || lda > kMaxDim || ldb > kMaxDim))
+        return GG_ERR_INVALID_ARG;
+    if (wraps(C, M, N, ldc, 4) ||
+        (use_ab && (wraps(A, a_rows, a_cols, lda, 4) || wraps(B, b_rows, b_cols, ldb, 4))))
         return GG_ERR_INVALID_ARG;
     const Span c = span(C, M, N, ldc, 4);
     if (use_ab && (overlaps(c, span(A, a_rows, a_cols, lda, 4)) ||
@@ -130,6 +146,8 @@ int gemv_f32(int64_t M, int64_t K, const float *W, int64_t ldw, const float *x, 
     if (bad_ptr(y, 4)) return GG_ERR_INVALID_ARG;
     if (K > 0 && (bad_ptr(W, 4) || bad_ptr(x, 4))) return GG_ERR_INVALID_ARG;
     if (K > 0 && (ldw < K || ldw > kMaxDim)) return GG_ERR_INVALID_ARG;
+    if (wraps(y, 1, M, M, 4) || (K > 0 && (wraps(W, M, K, ldw, 4) || wraps(x, 1, K, K, 4))))
+        return GG_ERR_INVALID_ARG;
     const Span ys = span(y, 1, M, M, 4);
     if (K > 0 && (overlaps(ys, span(W, M, K, ldw, 4)) || overlaps(ys, span(x, 1, K, K, 4))))
         return GG_ERR_ALIAS;
@@ -157,8 +175,10 @@ int packed_batched(int bits, int64_t count, int64_t M, int64_t K, const uint8_t 
     if (K > 0 && (ldq < qcols || lds < scols || ldq > kMaxDim || lds > kMaxDim))
         return GG_ERR_INVALID_ARG;
     for (int64_t b = 0; b < count; ++b) {
-        if (bad_ptr(y[b], 4)) return GG_ERR_INVALID_ARG;
-        if (K > 0 && (bad_ptr(Q[b], 1) || bad_ptr(S[b], 2) || bad_ptr(x[b], 4)))
+        if (bad_ptr(y[b], 4) || wraps(y[b], 1, M, M, 4)) return GG_ERR_INVALID_ARG;
+        if (K > 0 && (bad_ptr(Q[b], 1) || bad_ptr(S[b], 2) || bad_ptr(x[b], 4) ||
+                      wraps(Q[b], M, qcols, ldq, 1) || wraps(S[b], M, scols, lds, 2) ||
+                      wraps(x[b], 1, K, K, 4)))
             return GG_ERR_INVALID_ARG;
     }
     // Every output must be disjoint from every input and from every other

@@ -671,6 +671,9 @@ hipError_t launch_gemm(bool ax, bool bx, int M, int N, int K, float alpha, const
     // Staged path: 128 x 64 tiles when that grid still gives every CU two
     // tiles to interleave; otherwise 64 x 64, which keeps small and K-heavy
     // products (few output tiles) spread over the CUs.
+    // Grids are at most 2^31 - 1 workgroups of the smallest tile (32 x 32);
+    // no product that fits in memory comes near that.
+    if ((int64_t)((M + 31) / 32) * ((N + 31) / 32) > INT32_MAX) return hipErrorInvalidValue;
     const int64_t tiles_128x64 = (int64_t)((M + 127) / 128) * ((N + 63) / 64);
     const bool big = tiles_128x64 >= 2 * (int64_t)num_cus;
     // Direct path: 64 x 64 tiles with the k-slabs split over KS groups of 4

@@ -21,7 +21,8 @@
  *    launched.  Checks, in order: sizes non-negative and below 2^31; an empty
  *    output returns GG_OK at once; non-null pointers, aligned to their element
  *    size, for every operand of non-zero extent; leading dimensions at least
- *    the row width; the output's byte range disjoint from every input's; the
+ *    the row width; no operand's byte range running past the end of the
+ *    address space; the output's byte range disjoint from every input's; the
  *    current device is a gfx950.  No exception or abort crosses this
  *    interface.
  *  - Results are reproducible bit for bit from run to run on the same shapes

@@ -54,6 +54,23 @@ def test_gemm_rejects_bad_sizes(name):
 
 
 @pytest.mark.parametrize("name", GEMMS)
+def test_gemm_rejects_ranges_past_the_address_space(name):
+    """Sizes below 2^31 whose byte range would wrap: invalid, not an alias."""
+    f = getattr(lib, name)
+    big = (1 << 31) - 1
+    high = (1 << 64) - (1 << 20)          # 1 MiB below the top of the address space
+    assert f(big, big, 1, PA, big, PB, big, high, big, None) == bd.GG_ERR_INVALID_ARG
+    assert f(4, 4, big, high, big, PB, big, PC, 4, None) == bd.GG_ERR_INVALID_ARG
+
+
+def test_packed_and_gemv_reject_ranges_past_the_address_space():
+    big = (1 << 31) - 1
+    high = (1 << 64) - (1 << 20)
+    assert lib.gemv_f32(big, big, high, big, PB, PC, None) == bd.GG_ERR_INVALID_ARG
+    assert lib.gemv_q2(big, 64, high, 16, PB, 1, PA, PC, None) == bd.GG_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", GEMMS)
 def test_gemm_empty_output_is_ok_without_pointers(name):
     f = getattr(lib, name)
     assert f(0, 5, 7, None, 0, None, 0, None, 0, None) == bd.GG_OK
