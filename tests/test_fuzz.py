@@ -95,3 +95,51 @@ def test_packed_random_cases(seed):
         ref, bound = ref_fn(Q, S, xs[b], K=K)
         assert_close(host(ys[b]), ref, bound, "seed %d: %d-bit %dx%d, %d products, offset %d"
                      % (seed, bits, M, K, count, off))
+
+
+K_FLAT = {2: [512, 768, 1024, 1536, 2048, 3072], 4: [256, 384, 512, 768, 1024, 1536]}
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_packed_flat_random_cases(seed):
+    """Shapes the flat split takes: K with 8 to 48 chunks per row, rows on
+    both sides of a workgroup's block, batches of 1 to 65 products (two
+    launches past 64) with one shared x or one x each, padded leading
+    dimensions and code bases offset by whole chunks; sampled products
+    against the oracle, and the last one bit for bit against a single call."""
+    rng = np.random.default_rng(3000 + seed)
+    bits = int(rng.choice([2, 4]))
+    K = int(rng.choice(K_FLAT[bits]))
+    M = int(rng.integers(1, 3000)) if rng.random() < 0.7 else int(rng.integers(1, 64))
+    count = int(rng.choice([1, 2, 5, 40, 65]))
+    shared = bool(rng.random() < 0.5)
+    pad_q, pad_s = int(rng.choice([0, 16, 48, 5])), int(rng.choice([0, 3]))
+    off = int(rng.choice([0, 16, 32]))
+    t = torch()
+    nb = K * bits // 8
+    mats, dQ, dS = [], [], []
+    for _ in range(count):
+        Q = rng.integers(0, 256, (M, nb + pad_q), dtype=np.uint8)
+        S = rng.uniform(0.01, 0.05, (M, K // 64 + pad_s)).astype(np.float16).view(np.uint16)
+        mats.append((Q, S))
+        buf = t.zeros(off + Q.size, dtype=t.uint8, device="cuda")
+        q = buf[off:].view(Q.shape)
+        q.copy_(t.from_numpy(Q).to("cuda"))
+        dQ.append(q[:, :nb])
+        dS.append(dev(S.view(np.int16))[:, :K // 64])
+    xs = [inputs.normal(rng, (K,))] * count if shared else [inputs.normal(rng, (K,))
+                                                             for _ in range(count)]
+    dxs = [dev(xs[0])] * count if shared else [dev(x) for x in xs]
+    f1 = bd.gemv_q2 if bits == 2 else bd.gemv_q4
+    fb = bd.gemv_q2_batched if bits == 2 else bd.gemv_q4_batched
+    ref_fn = oracle.gemv_q2 if bits == 2 else oracle.gemv_q4
+    ys = [f1(dQ[0], dS[0], dxs[0])] if count == 1 else fb(dQ, dS, dxs)
+    t.cuda.synchronize()
+    for b in sorted({0, count // 2, count - 1}):
+        Q, S = mats[b]
+        ref, bound = ref_fn(Q, S, xs[b], K=K)
+        assert_close(host(ys[b]), ref, bound, "seed %d: %d-bit %dx%d, product %d of %d"
+                     % (seed, bits, M, K, b, count))
+    if count > 1:
+        b = count - 1
+        assert np.array_equal(host(f1(dQ[b], dS[b], dxs[b])), host(ys[b]))
