@@ -71,7 +71,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int THREADS = 256;
-constexpr int GROUP_M = 4;         // tile rows per ordering group
+constexpr int GROUP_M = 8;         // tile rows per ordering group
 
 // ---------------------------------------------------------------------------
 // Staged path.
