@@ -340,9 +340,10 @@ __global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int6
 }
 
 // ---------------------------------------------------------------------------
-// Flat split.  A workgroup of three waves (192 lanes) reads a block of RPS
-// consecutive rows per step, lane f taking 16-byte chunk f of the block.
-// When a row holds CPR chunks and CPR divides 192 (RPS = 192 / CPR), lane f
+// Flat split.  A workgroup of TH lanes (192 in a batch, 576 for a single
+// product) reads a block of RPS consecutive rows per step, lane f taking
+// 16-byte chunk f of the block.  When a row holds CPR chunks and CPR divides
+// 192 (RPS = TH / CPR), lane f
 // always lands on chunk f mod CPR of row f / CPR: its columns -- and the x
 // values, position scales and unit sums that go with them -- are the same at
 // every step, so they are set up once per workgroup.  Each load instruction
@@ -351,9 +352,15 @@ __global__ __launch_bounds__(THREADS) void gemv_packed_kernel(int M, int K, int6
 // group of 2-bit codes or half a group of 4-bit codes, so a lane needs one
 // scale per chunk.  Per chunk the lane forms the UPC unit chains of the
 // unpack above, adds them in unit order and applies the scale; the CPR
-// partial sums of a row meet in LDS, where one lane adds them in chunk order.
-// The order is fixed for a given shape, so results repeat bit for bit.
+// partial sums of a row meet in LDS, where one lane adds them in a fixed
+// pairwise tree.  The order is fixed for a given shape, so results repeat bit
+// for bit, and single and batched products agree bit for bit.
 constexpr int FLAT_THREADS = 192;
+// A single product takes nine-wave workgroups: a third as many workgroups
+// read x and dispatch (2-bit 12,288 x 1,536: 3.94 -> 3.76 us; 4-bit 4.47 ->
+// 4.28 us, same box; 384 lanes gave 3.91 and 4.29 us, 768 lanes 4.00 and
+// 4.46 us).
+constexpr int FLAT_SINGLE_THREADS = 576;
 constexpr int FLAT_MIN_CPR = 8, FLAT_MAX_CPR = 48;
 constexpr int FLAT_MAX_RPS = FLAT_THREADS / FLAT_MIN_CPR;
 
@@ -482,8 +489,9 @@ struct Flat {
     // Rows [0, nrows) of a block of partial sums (ps floats per row, cpr
     // used), one lane per row; row r goes to y[r] when r < rows_valid.
     static __device__ __forceinline__ void rows(const float *part, int ps, int cpr, int nrows,
-                                                int rows_valid, float *__restrict__ y, int f) {
-        for (int r = f; r < nrows; r += FLAT_THREADS) {
+                                                int rows_valid, float *__restrict__ y, int f,
+                                                int threads) {
+        for (int r = f; r < nrows; r += threads) {
             if (r >= rows_valid) break;
             const float *pr = part + r * ps;
             float sum;
@@ -555,16 +563,16 @@ struct FlatLoads {
 // the code loads are issued between the x loads and the set-up arithmetic,
 // so that their latency runs under the set-up (vector-memory loads retire
 // in issue order, so the set-up's wait for x does not wait for them).
-template <int BITS, int T, int NB, bool EARLY>
-__global__ __launch_bounds__(FLAT_THREADS) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 1 : 4)))
+template <int BITS, int T, int NB, bool EARLY, int TH = FLAT_THREADS>
+__global__ __launch_bounds__(TH) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 1 : 4)))
 void gemv_packed_flat(int M, int cpr, int rdiv, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
     using F = Flat<BITS>;
     __shared__ __attribute__((aligned(16))) typename F::Smem sm;
-    __shared__ __attribute__((aligned(16))) float part[T * (FLAT_THREADS + 4 * FLAT_MAX_RPS)];
+    __shared__ __attribute__((aligned(16))) float part[T * (TH + 4 * (TH / FLAT_MIN_CPR))];
 
     const int b = NB == 1 ? 0 : (int)blockIdx.y;
     const int f = threadIdx.x;
-    const int rps = FLAT_THREADS / cpr;       // rows per step
+    const int rps = TH / cpr;                 // rows per step
     const int rin = (f * rdiv) >> 16, c = f - rin * cpr;   // f / cpr (rdiv = ceil(2^16 / cpr))
     const int row0 = (int)blockIdx.x * rps * T;
     const int ps = cpr + 4;                   // LDS floats per row of partial sums
@@ -586,7 +594,7 @@ void gemv_packed_flat(int M, int cpr, int rdiv, int64_t ldq, int64_t lds, Packed
         if (NB == 1) __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
-    F::rows(part, ps, cpr, rps * T, M - row0, ptrs.y[b] + row0, f);
+    F::rows(part, ps, cpr, rps * T, M - row0, ptrs.y[b] + row0, f, TH);
 }
 
 // Chunks per row for the flat split, or 0 where it does not apply: every row
@@ -616,11 +624,12 @@ int flat_cpr(int count, int M, int K, const uint8_t *const *Q, int64_t ldq, int6
 // The code loads go out before the x set-up's arithmetic (EARLY): 2% faster
 // for single 2-bit products and for batches, and, since x is loaded once per
 // unit, for single 4-bit products too (4.57 -> 4.45 us with two steps).
-template <int BITS, int NB, int T = (NB == 1 ? (BITS == 2 ? 1 : 2) : 8), bool EARLY = true>
+template <int BITS, int NB, int T = (NB == 1 ? (BITS == 2 ? 1 : 2) : 8), bool EARLY = true,
+          int TH = (NB == 1 ? FLAT_SINGLE_THREADS : FLAT_THREADS)>
 hipError_t launch_flat(int count, int M, int cpr, const uint8_t *const *Q, int64_t ldq,
                        const uint16_t *const *S, int64_t lds, const float *const *x,
                        float *const *y, hipStream_t s) {
-    const int rows_per_wg = FLAT_THREADS / cpr * T;
+    const int rows_per_wg = TH / cpr * T;
     const dim3 grid((M + rows_per_wg - 1) / rows_per_wg, count);
     PackedPtrs<NB> p;
     for (int b = 0; b < NB; ++b) {
@@ -630,10 +639,10 @@ hipError_t launch_flat(int count, int M, int cpr, const uint8_t *const *Q, int64
         p.x[b] = x[i];
         p.y[b] = y[i];
     }
-    // f / cpr as (f * rdiv) >> 16 is exact for f < 192 and cpr <= 48: the
+    // f / cpr as (f * rdiv) >> 16 is exact for f < 768 and cpr <= 48: the
     // rounding excess f * (rdiv - 2^16 / cpr) / 2^16 stays below 1 / cpr.
     const int rdiv = (65536 + cpr - 1) / cpr;
-    hipLaunchKernelGGL((gemv_packed_flat<BITS, T, NB, EARLY>), grid, dim3(FLAT_THREADS), 0, s, M,
+    hipLaunchKernelGGL((gemv_packed_flat<BITS, T, NB, EARLY, TH>), grid, dim3(TH), 0, s, M,
                        cpr, rdiv, ldq, lds, p);
     return hipGetLastError();
 }

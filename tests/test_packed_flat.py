@@ -2,8 +2,8 @@
 split: K a multiple of 64 whose rows hold 8 to 48 chunks of 16 bytes that
 divide a 192-lane workgroup (2-bit K in {512, 768, 1024, 1536, 2048, 3072},
 4-bit K in {256, 384, 512, 768, 1024, 1536}), with 16-byte aligned code rows
-and x.  Row counts fall on both sides of a workgroup's rows (8 rows per step
-at 24 chunks; 1 to 4 steps per workgroup for one product, 8 in a batch),
+and x.  Row counts fall on both sides of a workgroup's rows (24 rows per
+workgroup for one product at 24 chunks, 64 in a batch),
 leading dimensions are padded with garbage, and results are checked against
 the oracle element by element, bit for bit where every partial sum is an
 integer."""
