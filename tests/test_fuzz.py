@@ -2,7 +2,12 @@
 both sides of the tile, slab and tile-count boundaries, transpose pairs,
 alignment offsets, leading-dimension padding and alpha/beta for the matrix
 product; widths, shapes, padding, offsets and batch sizes for
-the packed matrix-vector products.  Each case is named by its seed."""
+the packed matrix-vector products.  Each case is named by its seed.
+
+GG_FUZZ_SCALE=n (default 1) multiplies every test's number of seeds by n for
+longer runs; the first seeds stay the same."""
+import os
+
 import numpy as np
 import pytest
 
@@ -12,6 +17,8 @@ from gemv_gemm_f32_amd import inputs
 from gpu_util import assert_close, dev, host, torch
 
 pytestmark = pytest.mark.gpu
+
+SCALE = max(1, int(os.environ.get("GG_FUZZ_SCALE", "1")))
 
 
 def _placed(a, offset, pad):
@@ -26,7 +33,7 @@ def _placed(a, offset, pad):
     return view
 
 
-@pytest.mark.parametrize("seed", range(120))
+@pytest.mark.parametrize("seed", range(120 * SCALE))
 def test_gemm_random_cases(seed):
     rng = np.random.default_rng(1000 + seed)
     hi = 1100 if seed % 4 == 3 else 300          # one case in four past the CU count
@@ -58,7 +65,7 @@ def _packed_case(rng, bits, M, K, pad_q, pad_s):
     return Q, S
 
 
-@pytest.mark.parametrize("seed", range(36))
+@pytest.mark.parametrize("seed", range(36 * SCALE))
 def test_packed_random_cases(seed):
     rng = np.random.default_rng(2000 + seed)
     bits = int(rng.choice([2, 4]))
@@ -100,7 +107,7 @@ def test_packed_random_cases(seed):
 K_FLAT = {2: [512, 768, 1024, 1536, 2048, 3072], 4: [256, 384, 512, 768, 1024, 1536]}
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(40 * SCALE))
 def test_packed_flat_random_cases(seed):
     """Shapes the flat split takes: K with 8 to 48 chunks per row, rows on
     both sides of a workgroup's block, batches of 1 to 65 products (two
