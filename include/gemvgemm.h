@@ -28,8 +28,14 @@
  *  - Results are reproducible bit for bit from run to run on the same shapes
  *    (fixed reduction trees, no floating-point atomics).  They agree with the
  *    exact sum to |c - c_exact| <= 1e-4 * sum_k |a_ik * b_kj| per element on
- *    the supported workloads; fp32 operands are used as IEEE fp32 (no reduced
- *    precision inputs).
+ *    the supported workloads with finite inputs; fp32 operands are used as
+ *    IEEE fp32 (no reduced precision inputs).
+ *  - Non-finite inputs: the fp32 products follow IEEE arithmetic, so a NaN
+ *    operand makes exactly the outputs whose sums contain it NaN, and an
+ *    infinity gives +-inf there (NaN where it meets a zero or an opposite
+ *    infinity).  The packed products apply the zero point through the sum of
+ *    x, so a NaN or an infinity anywhere in x makes every output NaN, and a
+ *    NaN scale makes its own row NaN.
  *  - Thread safety: the only global state is a per-device property cache
  *    filled once; every entry point may be called from several threads.
  */
