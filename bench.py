@@ -767,9 +767,9 @@ def main():
     q2_hot_us = 1e3 * hot_ms / n_hot
     del hot_graph
     copy_bytes = 1 << 30
-    csrc = torch.empty(copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
-    cdst = torch.empty_like(csrc)
     with torch.cuda.stream(stream):
+        csrc = torch.empty(copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        cdst = torch.empty_like(csrc)
         cdst.copy_(csrc)
         stream.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
