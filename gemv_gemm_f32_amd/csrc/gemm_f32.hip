@@ -55,7 +55,7 @@
 //    accumulator itself.
 //  * Tile order: workgroups are handed to the 8 XCDs round-robin, so the grid
 //    index is remapped to give each XCD a contiguous run of tiles, ordered in
-//    groups of 4 tile rows so that a run shares A row panels and B column
+//    groups of 8 tile rows so that a run shares A row panels and B column
 //    panels in that XCD's L2.
 //  * Every output cell is one fixed sequence of MFMA accumulations over k,
 //    independent of timing and of the path taken, so results are
