@@ -105,7 +105,6 @@ int gemm_common(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha, 
         return GG_ERR_ALIAS;
     int cus = 0;
     if (int st = check_device(&cus)) return st;
-    (void)hipGetLastError();   // clear a stale error so the check below is ours
     return launch_status(gg::launch_gemm(!ta, tb, (int)M, (int)N, use_ab ? (int)K : 0, alpha,
                                          A, lda, B, ldb, beta, C, ldc, cus,
                                          reinterpret_cast<hipStream_t>(stream)));
@@ -153,7 +152,6 @@ int gemv_f32(int64_t M, int64_t K, const float *W, int64_t ldw, const float *x, 
         return GG_ERR_ALIAS;
     int cus = 0;
     if (int st = check_device(&cus)) return st;
-    (void)hipGetLastError();
     return launch_status(gg::launch_gemv_f32((int)M, (int)K, W, ldw, x, y,
                                              reinterpret_cast<hipStream_t>(stream)));
 }
@@ -208,7 +206,6 @@ int packed_batched(int bits, int64_t count, int64_t M, int64_t K, const uint8_t 
     }
     int cus = 0;
     if (int st = check_device(&cus)) return st;
-    (void)hipGetLastError();
     const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     return launch_status(bits == 2 ? gg::launch_gemv_q2((int)count, (int)M, (int)K, Q, ldq, S,
                                                         lds, x, y, hs)

@@ -581,10 +581,9 @@ hipError_t launch_direct(int M, int N, int K, float alpha, const float *A, int64
                          const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
                          hipStream_t s) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    hipLaunchKernelGGL((gemm_f32_direct<BM, BN, AX, BX, KS, WPG, KT>), dim3(tiles_m * tiles_n),
-                       dim3(64 * WPG * KS), 0, s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
-                       tiles_m, tiles_n);
-    return hipGetLastError();
+    return launch(gemm_f32_direct<BM, BN, AX, BX, KS, WPG, KT>, dim3(tiles_m * tiles_n),
+                  dim3(64 * WPG * KS), s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tiles_m,
+                  tiles_n);
 }
 
 // Narrow tiles, 64 x 32 (TALL) or 32 x 64, with two waves per k-group and
@@ -639,10 +638,8 @@ hipError_t launch_t(int M, int N, int K, float alpha, const float *A, int64_t ld
                     hipStream_t s) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const int nwg = tiles_m * tiles_n;
-    hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, BK, AX, BX, VA, VB, FENCE>), dim3(nwg),
-                       dim3(THREADS), 0, s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
-                       tiles_m, tiles_n);
-    return hipGetLastError();
+    return launch(gemm_f32_kernel<BM, BN, BK, AX, BX, VA, VB, FENCE>, dim3(nwg), dim3(THREADS),
+                  s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tiles_m, tiles_n);
 }
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }

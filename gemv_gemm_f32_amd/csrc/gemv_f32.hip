@@ -133,13 +133,8 @@ hipError_t launch_gemv_f32(int M, int K, const float *W, int64_t ldw, const floa
     const bool vec = (reinterpret_cast<uintptr_t>(W) % 16 == 0) &&
                      (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (ldw % 4 == 0) &&
                      (K % 4 == 0);
-    if (vec)
-        hipLaunchKernelGGL((gemv_f32_kernel<R, 6, true>), dim3(nwg), dim3(THREADS), 0, s,
-                           M, K, W, ldw, x, y);
-    else
-        hipLaunchKernelGGL((gemv_f32_kernel<R, 8, false>), dim3(nwg), dim3(THREADS), 0, s,
-                           M, K, W, ldw, x, y);
-    return hipGetLastError();
+    if (vec) return launch(gemv_f32_kernel<R, 6, true>, dim3(nwg), dim3(THREADS), s, M, K, W, ldw, x, y);
+    return launch(gemv_f32_kernel<R, 8, false>, dim3(nwg), dim3(THREADS), s, M, K, W, ldw, x, y);
 }
 
 }  // namespace gg

@@ -642,9 +642,8 @@ hipError_t launch_flat(int count, int M, int cpr, const uint8_t *const *Q, int64
     // f / cpr as (f * rdiv) >> 16 is exact for f < 768 and cpr <= 48: the
     // rounding excess f * (rdiv - 2^16 / cpr) / 2^16 stays below 1 / cpr.
     const int rdiv = (65536 + cpr - 1) / cpr;
-    hipLaunchKernelGGL((gemv_packed_flat<BITS, T, NB, EARLY, TH>), grid, dim3(TH), 0, s, M,
-                       cpr, rdiv, ldq, lds, p);
-    return hipGetLastError();
+    return launch(gemv_packed_flat<BITS, T, NB, EARLY, TH>, grid, dim3(TH), s, M, cpr, rdiv, ldq,
+                  lds, p);
 }
 
 // A single product needs every SIMD busy: 6 rows per group of lanes gives
@@ -679,15 +678,13 @@ hipError_t launch_chunk(int count, int M, int K, const uint8_t *const *Q, int64_
     const bool full = fast && (K % (16 * SPLIT * UPL) == 0) &&
                       (M % (SPLIT == 32 ? 2 * RPL : RPL) == 0);
     if (full)
-        hipLaunchKernelGGL((gemv_packed_kernel<BITS, SPLIT, RPL, true, true, NB>), grid,
-                           dim3(THREADS), 0, s, M, K, ldq, lds, p);
-    else if (fast)
-        hipLaunchKernelGGL((gemv_packed_kernel<BITS, SPLIT, RPL, true, false, NB>), grid,
-                           dim3(THREADS), 0, s, M, K, ldq, lds, p);
-    else
-        hipLaunchKernelGGL((gemv_packed_kernel<BITS, SPLIT, RPL, false, false, NB>), grid,
-                           dim3(THREADS), 0, s, M, K, ldq, lds, p);
-    return hipGetLastError();
+        return launch(gemv_packed_kernel<BITS, SPLIT, RPL, true, true, NB>, grid, dim3(THREADS),
+                      s, M, K, ldq, lds, p);
+    if (fast)
+        return launch(gemv_packed_kernel<BITS, SPLIT, RPL, true, false, NB>, grid, dim3(THREADS),
+                      s, M, K, ldq, lds, p);
+    return launch(gemv_packed_kernel<BITS, SPLIT, RPL, false, false, NB>, grid, dim3(THREADS), s,
+                  M, K, ldq, lds, p);
 }
 
 // Rows split 32 ways unless the rows are long and few: at K >= 6,144 (each

@@ -9,7 +9,28 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 namespace gg {
+
+// Launches kernel<<<grid, block, 0, s>>>(args...) and returns that launch's
+// own status from hipLaunchKernel, so an error left pending by an earlier,
+// unrelated HIP call is neither reported as ours nor cleared.  The arguments
+// are converted to the kernel's parameter types first.
+template <typename... P, size_t... I>
+hipError_t launch_args(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t s,
+                       std::tuple<P...> &args, std::index_sequence<I...>) {
+    void *ptrs[sizeof...(P) + 1] = {static_cast<void *>(&std::get<I>(args))..., nullptr};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, 0, s);
+}
+
+template <typename... P, typename... A>
+hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t s, A &&...a) {
+    static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+    std::tuple<P...> args(std::forward<A>(a)...);
+    return launch_args(kernel, grid, block, s, args, std::index_sequence_for<P...>{});
+}
 
 // C = alpha * op(A).op(B) + beta * C (C not read when beta == 0).
 // ax: A stored M x K (else K x M, i.e. op(A) = A^T); bx: B stored N x K
@@ -25,7 +46,9 @@ hipError_t launch_gemv_f32(int M, int K, const float *W, int64_t ldw,
 
 // y_b = W_b.x_b for b < count, W_b as 2-bit (q2) or 4-bit (q4) codes with
 // one binary16 scale per 64 columns; the pointer arrays are host arrays of
-// device pointers.
+// device pointers.  More than PACKED_MAX_BATCH products take several
+// launches in order; if one of them is rejected the earlier ones stay
+// queued.
 constexpr int PACKED_MAX_BATCH = 64;
 hipError_t launch_gemv_q2(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
                           const uint16_t *const *S, int64_t lds, const float *const *x,

@@ -24,7 +24,11 @@
  *    the row width; no operand's byte range running past the end of the
  *    address space; the output's byte range disjoint from every input's; the
  *    current device is a gfx950.  No exception or abort crosses this
- *    interface.
+ *    interface.  GG_ERR_LAUNCH reports the status of this call's own
+ *    launch; an error left pending by an earlier HIP call is neither
+ *    reported nor cleared.  (The one exception to "nothing was launched":
+ *    a batch of more than 64 products takes several launches, and if a
+ *    later one is rejected the earlier ones stay queued.)
  *  - Results are reproducible bit for bit from run to run on the same shapes
  *    (fixed reduction trees, no floating-point atomics).  They agree with the
  *    exact sum to |c - c_exact| <= 1e-4 * sum_k |a_ik * b_kj| per element on
@@ -166,6 +170,8 @@ int gemv_q2(int64_t M, int64_t K, const uint8_t *Q, int64_t ldq,
  *   as in gemv_q2).  The arrays are read during the call and not kept.
  *   Every y[b] must be disjoint from every input and from every other y[c]
  *   (else GG_ERR_ALIAS); inputs may be shared (for example one x for all).
+ *   Products 64 at a time share a launch, in order; GG_ERR_LAUNCH from a
+ *   batch of more than 64 may leave the products of earlier launches queued.
  * A batch runs the same arithmetic per product as gemv_q2, with more rows
  * per thread; results meet the same tolerance and are reproducible run to
  * run, but a batch may sum in a different order from a gemv_q2 call and so
