@@ -8,33 +8,36 @@ A step is one pass of the whole path over one batch of synthetic input:
   * one gemm_f32 of two 2048 x 2048 fp32 matrices (uniform [-1, 1), seed 3),
     the largest size of the kernel sweep in "I built a GPT-2 in the browser,
     then made it 2.6x-12.1x faster" (section "The kernel sweep");
-  * one token of 2-bit GEMVs: 40 consecutive gemv_q2 calls ("Kernel 0112",
-    section "What is being measured": the kernel runs 40 times per token),
-    call n using weight matrix n mod 128 of a 128-matrix set (648 MiB of codes
-    and scales, far above the 256 MB Infinity Cache, as the page's "cold"
+  * one token of 2-bit GEMVs: the 40 products a token runs ("Kernel 0112",
+    section "What is being measured") in one gemv_q2_batched launch, product n
+    using weight matrix n mod 128 of a 128-matrix set (648 MiB of codes and
+    scales, far above the 256 MB Infinity Cache, as the page's "cold"
     rotation keeps reuse between runs unlikely).
-Every input is generated, hashed and copied to HBM before timing.  Launches
-are captured into HIP graphs (through torch.cuda.CUDAGraph) so that timed
-regions replay kernels back to back, without host launch gaps.  HIP events on
-the replay stream time K whole steps (ms_per_step), and, for each kernel's
-average launch duration, runs of back-to-back launches of that kernel alone
-(K GEMMs; K tokens of 40 q2 calls).
+Every input is generated, hashed and copied to HBM before timing, and every
+product is checked against the CPU oracle first -- on every matrix of each
+rotation set -- so that a failing kernel reports no speed.  Launches are
+captured into HIP graphs (torch.cuda.CUDAGraph) so timed regions replay
+kernels back to back, without host launch gaps.
+
+Timing.  `ms_per_step` is K whole steps (after W warm-up steps) between two
+HIP events on the replay stream.  Each kernel's launch duration comes from a
+fixed window that does not depend on K: one graph of L back-to-back launches
+of that kernel alone (inputs rotating as above), replayed for at least
+0.1 s of warm-up and then R times with a HIP event after each replay; `mean_us`
+is the window's time over its R * L launches and `median_us` the median of the
+per-replay means.  The rooflines use `mean_us`.
 
 Output: one JSON line.  `value` is the GEMM's TFLOP/s (2 * 2048^3 flops per
-launch over its average launch duration); the 2-bit GEMV's weight GB/s
-(codes + scales per call over its average duration) is in `q2_gemv`.  Both
-carry a roofline object.  `q2_gemv_batched` times the same tokens with each
-token's 40 products in one gemv_q2_batched launch; `q4_gemv` times the 4-bit
-product the same two ways, `q2_gemv_transposed` the 2-bit product at the
-transposed 1,536 x 12,288 shape, and `gemv_f32` the fp32 product.  Before any number is
-printed the outputs are checked against the CPU oracle on sampled cells; a
-failing kernel reports no speed.  `cpu_baseline` times the oracle itself on a bounded sample.
-After the main timing, `spread` gives each kernel's per-launch median, p10,
-p90 and minimum over 16 single replays, and `context` the 2-bit GEMV on one
-cache-resident matrix (its launch-and-compute floor) and the rate of a plain
-device-to-device copy.  `gemm_configs` checks and times the other GEMM
-configurations: the nine products of a GPT-2-small block at 1,024 tokens
-(alone and as one graph), the 346 x 768 x 768 classifier layer and 256^3.
+launch over its mean launch duration).  `q2_gemv` and `q2_gemv_batched` give
+the 2-bit GEMV's weight GB/s (codes + scales per product over its duration)
+for one product per launch and for a token's 40 products per launch, each
+with a roofline object; `q4_gemv`, `q2_gemv_transposed` and `gemv_f32` do the
+same for the 4-bit product, the transposed 1,536 x 12,288 shape and the fp32
+product.  `gemm_configs` checks and times the other GEMM configurations (the
+nine products of a GPT-2-small block, the 346 x 768 x 768 classifier layer,
+256^3).  `cpu_baseline` times the oracle on the host, on one core and on every
+usable core.  `context` holds reference points measured in the same run.  The
+last key, `summary`, repeats the headline figures in a few fields.
 """
 from __future__ import annotations
 
@@ -45,6 +48,7 @@ import os
 import platform
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -60,6 +64,7 @@ Q2_WEIGHT_BYTES = Q2_CODE_BYTES + Q2_SCALE_BYTES   # 5,308,416
 Q2_ALG_BYTES = Q2_WEIGHT_BYTES + Q2_K * 4 + Q2_M * 4   # + x + y = 5,363,712
 Q2_ROTATION = 128
 CALLS_PER_TOKEN = 40
+N_TOK = 16                                         # 16 tokens x 40 = 640 = 5 x 128
 Q4_CODE_BYTES = Q2_M * Q2_K // 2                   # 9,437,184
 Q4_WEIGHT_BYTES = Q4_CODE_BYTES + Q2_SCALE_BYTES   # 10,027,008
 Q4_ALG_BYTES = Q4_WEIGHT_BYTES + Q2_K * 4 + Q2_M * 4   # + x + y = 10,082,304
@@ -72,8 +77,16 @@ QT_ALG_BYTES = Q2_WEIGHT_BYTES + QT_K * 4 + QT_M * 4   # 5,363,712
 PEAK_FP32_MFMA_TFLOPS = 157.3      # MI355X dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
 # "I built a GPT-2 in the browser...", table of section "The kernel sweep":
-# blocked4 at 2048^3 took 9.12 ms on an Apple M-series laptop (WebGPU).
+# blocked4 at 2048^3 took 9.12 ms on an Apple M-series laptop (WebGPU): the
+# pages' own figure for this metric and workload, on other hardware.
 PAGE_GEMM_2048_TFLOPS = GEMM_FLOPS / 9.12e-3 / 1e12
+
+# Fixed timing windows: (launches per graph, timed replays).
+WIN_GEMM = (25, 8)                 # 200 launches of 2048^3
+WIN_SINGLE = (N_TOK * CALLS_PER_TOKEN, 4)   # 2,560 single-product launches
+WIN_BATCHED = (N_TOK, 8)           # 128 launches of 40 products
+WIN_CONFIG = (8, 25)               # 200 launches per GEMM configuration
+WARM_S = 0.1                       # time-based warm-up before each window
 
 PROFILES = os.path.join(ROOT, "profiles")
 CALIBRATION_BYTES = 256 << 20      # the copy used to scale byte counters
@@ -105,104 +118,92 @@ def traffic_from_profile(name, sha):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(A, B, Q, S, x, budget_s=12.0):
-    """The oracle, single-threaded as written, on a bounded sample of the
-    same workload: leading rows of the 2048^3 product, sized to about
-    `budget_s` seconds, and whole 2-bit GEMVs on one rotation matrix."""
+def usable_cores():
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(A, B, Q, S, x):
+    """The oracle as it stands, timed on the host: the whole 2048^3 product
+    (about 3.5 s on one core) and 2-bit GEMVs on one rotation matrix, first
+    on one core, then with its output rows split into blocks over every
+    usable core (threads calling the C oracle, which runs without the GIL)."""
     import oracle
     oracle.build(force=False)
-    # calibrate on 4 rows, then fill the budget (at most all 2048 rows)
+    cores = usable_cores()
     t0 = time.perf_counter()
-    oracle.gemm_nn(A[:4], B)
-    t4 = time.perf_counter() - t0
-    rows = int(max(4, min(GEMM_N, 4 * (0.75 * budget_s) / max(t4, 1e-6))))
-    t0 = time.perf_counter()
-    oracle.gemm_nn(A[:rows], B)
-    tg = time.perf_counter() - t0
-    gemm_tflops = 2.0 * rows * GEMM_N * GEMM_N / tg / 1e12
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.gemv_q2(Q, S, x)
-        reps += 1
-        if time.perf_counter() - t0 > 0.25 * budget_s or reps >= 50:
-            break
-    tq = (time.perf_counter() - t0) / reps
+    oracle.gemm_nn(A, B)
+    t1 = time.perf_counter() - t0
+    blocks = np.array_split(np.arange(GEMM_N), cores)
+    with ThreadPoolExecutor(max_workers=cores) as pool:
+        t0 = time.perf_counter()
+        list(pool.map(lambda r: oracle.gemm_nn(A[r[0]:r[-1] + 1], B), blocks))
+        tn = time.perf_counter() - t0
+        reps = 8
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.gemv_q2(Q, S, x)
+        tq1 = (time.perf_counter() - t0) / reps
+        t0 = time.perf_counter()
+        list(pool.map(lambda _: oracle.gemv_q2(Q, S, x), range(cores * 2)))
+        tqn = (time.perf_counter() - t0) / (cores * 2)
     return {
-        "value": gemm_tflops,
+        "value": GEMM_FLOPS / tn / 1e12,
         "unit": "TFLOP/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": ("fp64 triple-loop oracle: rows 0..%d of the 2048^3 product "
-                   "(%.1f s); 2-bit unpack-then-dot oracle on one 12288x1536 "
-                   "matrix, %d calls" % (rows - 1, tg, reps)),
-        "q2_gemv_weight_gbs": Q2_WEIGHT_BYTES / tq / 1e9,
-        "cpu": platform.processor() or platform.machine(),
+        "sample": ("fp64 triple-loop oracle on the whole 2048^3 product (%.2f s on %d cores, "
+                   "%.2f s on 1); 2-bit unpack-then-dot oracle on one 12288x1536 matrix "
+                   "(%d calls on 1 core, %d spread over %d cores)"
+                   % (tn, cores, t1, reps, cores * 2, cores)),
+        "value_1core": GEMM_FLOPS / t1 / 1e12,
+        "q2_gemv_weight_gbs": Q2_WEIGHT_BYTES / tqn / 1e9,
+        "q2_gemv_weight_gbs_1core": Q2_WEIGHT_BYTES / tq1 / 1e9,
+        "cpu": host_cpu() or platform.processor() or platform.machine(),
     }
 
 
-def vendor_context(torch, stream, capture, timed, token_runner, n_tok, per_replay, dA, dB, Wf,
-                   dx, A, B, args):
+def vendor_context(torch, stream, capture, window, dA, dB, Wf, dx):
     """The vendor library on the same inputs, for context only (never part of
-    the library's path): torch.matmul in fp32 with TF32 off (hipBLASLt or
-    rocBLAS) at 2048^3, and torch.mv over the fp32 GEMV rotation set, timed
-    like the library's kernels (back-to-back launches in graph replays)."""
+    the library's path): torch.matmul in fp32 with TF32 off at 2048^3 and
+    torch.mv over the fp32 GEMV rotation set, in the same fixed windows."""
     out = {"note": ("torch.matmul / torch.mv in fp32 with TF32 off on the same operands, "
-                    "graph-replayed back to back like the library's kernels: context, "
-                    "not part of the library")}
+                    "timed like the library's kernels: context, not part of the library")}
     try:
         torch.backends.cuda.matmul.allow_tf32 = False
         C = torch.empty_like(dA)
         with torch.cuda.stream(stream):
             torch.matmul(dA, dB, out=C)
             stream.synchronize()
-        ref = (A[:4].astype(np.float64) @ B.astype(np.float64))
-        err = float(np.max(np.abs(C[:4].cpu().numpy() - ref)))
-        g = capture(lambda: [torch.matmul(dA, dB, out=C) for _ in range(per_replay)])
-        reps = max(1, (args.steps + per_replay - 1) // per_replay)
-
-        def run(i):
-            if i is not None:
-                g.replay()
-                return 1
-            for _ in range(reps):
-                g.replay()
-            return reps * per_replay
-        ms, n, _ = timed(run, 2)
-        us = 1e3 * ms / n
-        out["matmul_2048_us"] = us
-        out["matmul_2048_tflops"] = GEMM_FLOPS / us / 1e6
-        out["matmul_2048_max_abs_err_first_rows"] = err
+        g = capture(lambda: [torch.matmul(dA, dB, out=C) for _ in range(8)])
+        w = window([g], 8, 25)
+        out["matmul_2048_us"] = w["mean_us"]
+        out["matmul_2048_tflops"] = GEMM_FLOPS / w["mean_us"] / 1e6
         y = torch.empty(Q2_M, dtype=torch.float32, device=dA.device)
-
-        def tok(t):
-            for c in range(CALLS_PER_TOKEN):
-                torch.mv(Wf[(t * CALLS_PER_TOKEN + c) % F32_ROTATION], dx, out=y)
         with torch.cuda.stream(stream):
-            tok(0)
+            torch.mv(Wf[0], dx, out=y)
             stream.synchronize()
-        graphs = [capture(lambda t=t: tok(t)) for t in range(n_tok)]
-        ms, n, _ = timed(token_runner(graphs), 2)
-        us = 1e3 * ms / n
-        out["mv_12288x1536_us"] = us
-        out["mv_12288x1536_gbs"] = F32_ALG_BYTES / us / 1e3
+        # six graphs of 40 products: 240 calls, five turns of the 48-matrix set
+        gs = [capture(lambda t=t: [torch.mv(Wf[(40 * t + c) % F32_ROTATION], dx, out=y)
+                                   for c in range(40)]) for t in range(6)]
+        w = window(gs, 240, 4)
+        out["mv_12288x1536_us"] = w["mean_us"]
+        out["mv_12288x1536_gbs"] = F32_ALG_BYTES / w["mean_us"] / 1e3
     except Exception as e:   # context only: report, never fail the bench
         out["error"] = "%s: %s" % (type(e).__name__, e)
+        log("vendor context skipped: %s" % out["error"])
     return out
 
 
-def gemm_configs(torch, bd, inputs, oracle, dev, stream, capture, timed, steps, per_replay=8):
+def gemm_configs(torch, bd, inputs, oracle, dev, capture, window):
     """The GEMM configurations besides 2048^3, each checked against the oracle
     on sampled cells before it is timed: the nine products of a GPT-2-small
     block at 1,024 tokens (three forward, six backward; "I built a GPT-2 in
     the browser...", section "The kernel sweep", where matmul is most of
     training time), the 346 x 768 x 768 classifier layer (the 346-token
-    prompt of the polyomino classifier page) and 256^3.  Each product is
-    timed over back-to-back launches in graph replays (the median of three
-    interleaved rounds), the block's nine products also as one graph;
-    torch.matmul (fp32, TF32 off) on the same operands is context only.  A
-    product that fails parity reports no time."""
-    torch.backends.cuda.matmul.allow_tf32 = False
+    prompt of the polyomino classifier page) and 256^3.  Each product gets a
+    fixed window of back-to-back launches (the median of three interleaved
+    rounds), and the block's nine products also run as one graph.  A product
+    that fails parity reports no time."""
     entry = {"nn": bd.gemm_f32, "tn": bd.gemm_f32_tn, "nt": bd.gemm_f32_nt}
     rng = np.random.default_rng(77)
     t = inputs.gpt2_tensors(2)
@@ -211,9 +212,7 @@ def gemm_configs(torch, bd, inputs, oracle, dev, stream, capture, timed, steps, 
     A256, B256 = inputs.small_square(0)
     ops += [("classifier_346x768x768", "nn", 346, 768, 768, A346, B346),
             ("square_256", "nn", 256, 256, 256, A256, B256)]
-    reps = max(1, (steps + per_replay - 1) // per_replay)
-    out, launches, all_ok = {}, [], True
-    timing = []                # (name, our graph, vendor graph or error, flops)
+    out, launches, all_ok, timing = {}, [], True, []
     for name, lay, M, N, K, A, B in ops:
         dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
         dC = torch.empty((M, N), dtype=torch.float32, device=dev)
@@ -230,72 +229,31 @@ def gemm_configs(torch, bd, inputs, oracle, dev, stream, capture, timed, steps, 
         flops = 2.0 * M * N * K
         if name in {o[0] for o in inputs.GPT2_OPS}:
             launches.append((f, dA, dB, dC, flops))
-        if not ok:
-            continue
-        g = capture(lambda f=f, dA=dA, dB=dB, dC=dC: [f(dA, dB, C=dC) for _ in range(per_replay)])
-        try:
-            oa = dA.t() if lay == "tn" else dA
-            ob = dB.t() if lay == "nt" else dB
-            gv = capture(lambda oa=oa, ob=ob, dC=dC: [torch.matmul(oa, ob, out=dC)
-                                                      for _ in range(per_replay)])
-        except Exception as e:   # context only
-            gv = "%s: %s" % (type(e).__name__, e)
-        timing.append((name, g, gv, flops))
-
-    def runner(graph):
-        def run(i):
-            if i is not None:
-                graph.replay()
-                return 1
-            for _ in range(reps):
-                graph.replay()
-            return reps * per_replay
-        return run
-
-    def one_us(graph):
-        stream.synchronize()
-        ms, n, _ = timed(runner(graph), 4)
-        return 1e3 * ms / n
-
-    # Three rounds over every product (ours, then the vendor's), the median
-    # per product: a product timed right after the parity checks, or after a
-    # long burst of these launches, has read up to 1.8x slow on some boxes,
-    # and interleaving spreads such spells over all of them.
-    ours, vend = {n: [] for n, *_ in timing}, {n: [] for n, *_ in timing}
+        if ok:
+            g = capture(lambda f=f, dA=dA, dB=dB, dC=dC: [f(dA, dB, C=dC)
+                                                          for _ in range(WIN_CONFIG[0])])
+            timing.append((name, g, flops))
+    # Three rounds over every product, the median per product: interleaving
+    # spreads slow spells of a box over all of them.
+    rounds = {n: [] for n, *_ in timing}
     for _ in range(3):
-        for name, g, gv, _ in timing:
-            ours[name].append(one_us(g))
-            if not isinstance(gv, str):
-                vend[name].append(one_us(gv))
-    for name, g, gv, flops in timing:
+        for name, g, _ in timing:
+            rounds[name].append(window(g, *WIN_CONFIG, warm_s=0.02)["mean_us"])
+    for name, g, flops in timing:
         d = out[name]
-        d["us"] = float(np.median(ours[name]))
-        d["us_rounds"] = ours[name]
+        d["us"] = float(np.median(rounds[name]))
+        d["us_rounds"] = rounds[name]
+        d["launches_per_round"] = WIN_CONFIG[0] * WIN_CONFIG[1]
         d["tflops"] = flops / d["us"] / 1e6
         d["frac_of_fp32_mfma_peak"] = d["tflops"] / PEAK_FP32_MFMA_TFLOPS
-        if isinstance(gv, str):
-            d["vendor_error"] = gv
-        else:
-            d["vendor_torch_matmul_us"] = float(np.median(vend[name]))
     if all_ok:
-        g = capture(lambda: [f(dA, dB, C=dC) for f, dA, dB, dC, _ in launches])
-
-        def runb(i):
-            if i is not None:
-                g.replay()
-                return 1
-            for _ in range(steps):
-                g.replay()
-            return steps
-        stream.synchronize()
-        ms, n, _ = timed(runb, 4)
-        us = 1e3 * ms / n
+        g = capture(lambda: [f(dA, dB, C=dC) for _ in range(2)
+                             for f, dA, dB, dC, _ in launches])
+        w = window(g, 2, 25)          # 25 replays of two blocks
         total = sum(fl for *_, fl in launches)
         out["gpt2_block_9_products"] = {
-            "us": us, "tflops": total / us / 1e6,
-            "frac_of_fp32_mfma_peak": total / us / 1e6 / PEAK_FP32_MFMA_TFLOPS,
-            "vendor_torch_matmul_us_sum": sum(out[o[0]].get("vendor_torch_matmul_us", float("nan"))
-                                              for o in inputs.GPT2_OPS),
+            "us": w["mean_us"], "tflops": total / w["mean_us"] / 1e6,
+            "frac_of_fp32_mfma_peak": total / w["mean_us"] / 1e6 / PEAK_FP32_MFMA_TFLOPS,
             "note": "F1..B3w back to back in one graph, 39,862,665,216 flop per block"}
     return out, all_ok
 
@@ -401,7 +359,7 @@ def write_traffic(fetch_db, write_db):
              "traffic_gemm_f32_2048.json", ("gemm_f32.hip",), 3 * 4 * GEMM_N * GEMM_N),
             (lambda n: n.startswith("gemv_packed_flat<2, 1, 1,"),
              "traffic_gemv_q2_12288x1536.json", q2_srcs, Q2_ALG_BYTES),
-            (lambda n: n.startswith("gemv_packed_flat<2, 8, 64,"),
+            (lambda n: n.startswith("gemv_q2_idot<3, 8, 64>"),
              "traffic_gemv_q2_batched_12288x1536.json", q2_srcs,
              CALLS_PER_TOKEN * Q2_ALG_BYTES),
             (lambda n: n.startswith("gemv_packed_flat<4, 2, 1,"),
@@ -434,6 +392,15 @@ def write_traffic(fetch_db, write_db):
         out.append(d)
         print(json.dumps(d))
     return 0
+
+
+def roofline(kernel, alg_bytes, us, traffic=None, note=None):
+    achieved = alg_bytes / us / 1e3
+    d = {"kernel": kernel, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+         "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic}
+    if note:
+        d["traffic_note"] = note
+    return d
 
 
 def main():
@@ -484,99 +451,135 @@ def main():
     dC = torch.empty((GEMM_N, GEMM_N), dtype=torch.float32, device=dev)
     x = inputs.q2_x()
     dx = torch.from_numpy(x).to(dev)
-    Qd, Sd, hq = [], [], hashlib.sha256()
-    Q0 = S0 = None
-    for r in range(Q2_ROTATION):
-        Q, S = inputs.q2_weight(r)
-        if r == 0:
-            Q0, S0 = Q, S
-        hq.update(Q.tobytes())
-        hq.update(S.tobytes())
-        Qd.append(torch.from_numpy(Q).to(dev))
-        Sd.append(torch.from_numpy(S.view(np.int16)).to(dev))
-    dy = torch.empty(Q2_M, dtype=torch.float32, device=dev)
-    Q4d, S4d, h4 = [], [], hashlib.sha256()
-    Q40 = S40 = None
-    for r in range(Q4_ROTATION):
-        Q, S = inputs.q4_weight(r)
-        if r == 0:
-            Q40, S40 = Q, S
-        h4.update(Q.tobytes())
-        h4.update(S.tobytes())
-        Q4d.append(torch.from_numpy(Q).to(dev))
-        S4d.append(torch.from_numpy(S.view(np.int16)).to(dev))
-    # fp32 GEMV: 48 matrices of 12,288 x 1,536 (3.375 GiB), the same x
-    # length; drawn on a few host threads, uploaded one by one
-    from concurrent.futures import ThreadPoolExecutor
-    with ThreadPoolExecutor(max_workers=min(8, len(os.sched_getaffinity(0)))) as pool:
-        Wf = [torch.from_numpy(W).to(dev)
-              for W in pool.map(inputs.gemv_f32_weight, range(F32_ROTATION))]
-    W0 = Wf[0].cpu().numpy()
-    xf = inputs.gemv_f32_x()
-    dxf = torch.from_numpy(xf).to(dev)
-    # the transposed shape: 1,536 rows of 12,288 columns, same bytes per matrix
+
+    def packed_set(gen, n, M=Q2_M, K=Q2_K):
+        Qd, Sd, h = [], [], hashlib.sha256()
+        for r in range(n):
+            Q, S = gen(r, M, K)
+            h.update(Q.tobytes())
+            h.update(S.tobytes())
+            Qd.append(torch.from_numpy(Q).to(dev))
+            Sd.append(torch.from_numpy(S.view(np.int16)).to(dev))
+        return Qd, Sd, h.hexdigest()[:16]
+
+    Qd, Sd, hq = packed_set(inputs.q2_weight, Q2_ROTATION)
+    Q4d, S4d, h4 = packed_set(inputs.q4_weight, Q4_ROTATION)
+    QTd, STd, ht = packed_set(inputs.q2_weight, Q2_ROTATION, QT_M, QT_K)
     xt = inputs.q2_x(QT_K)
     dxt = torch.from_numpy(xt).to(dev)
-    QTd, STd, ht = [], [], hashlib.sha256()
-    QT0 = ST0 = None
-    for r in range(Q2_ROTATION):
-        Q, S = inputs.q2_weight(r, QT_M, QT_K)
-        if r == 0:
-            QT0, ST0 = Q, S
-        ht.update(Q.tobytes())
-        ht.update(S.tobytes())
-        QTd.append(torch.from_numpy(Q).to(dev))
-        STd.append(torch.from_numpy(S.view(np.int16)).to(dev))
+    # fp32 GEMV: 48 matrices of 12,288 x 1,536 (3.375 GiB), drawn on a few
+    # host threads, uploaded one by one
+    with ThreadPoolExecutor(max_workers=min(8, usable_cores())) as pool:
+        Wf = [torch.from_numpy(W).to(dev)
+              for W in pool.map(inputs.gemv_f32_weight, range(F32_ROTATION))]
+    xf = inputs.gemv_f32_x()
+    dxf = torch.from_numpy(xf).to(dev)
+    dy = torch.empty(Q2_M, dtype=torch.float32, device=dev)
     dyt = torch.empty(QT_M, dtype=torch.float32, device=dev)
+    dys = [torch.empty(Q2_M, dtype=torch.float32, device=dev) for _ in range(CALLS_PER_TOKEN)]
     dyts = [torch.empty(QT_M, dtype=torch.float32, device=dev) for _ in range(CALLS_PER_TOKEN)]
     torch.cuda.synchronize()
     hashes = {"gemm_A_B": inputs.sha256(A, B)[:16], "q2_x": inputs.sha256(x)[:16],
-              "q2_set": hq.hexdigest()[:16], "q4_set": h4.hexdigest()[:16],
-              "q2_transposed_set": ht.hexdigest()[:16], "q2_transposed_x": inputs.sha256(xt)[:16]}
+              "q2_set": hq, "q4_set": h4, "q2_transposed_set": ht,
+              "q2_transposed_x": inputs.sha256(xt)[:16], "gemv_f32_x": inputs.sha256(xf)[:16]}
     log("inputs ready in %.1f s" % (time.perf_counter() - t0))
 
-    # ---- parity first: a wrong kernel reports no speed
+    # ---- parity first, on every matrix of every rotation set: a wrong
+    #      kernel reports no speed
     import oracle
+    t0 = time.perf_counter()
     bd.gemm_f32(dA, dB, C=dC)
-    bd.gemv_q2(Qd[0], Sd[0], dx, y=dy)
     C = dC.cpu().numpy()
-    y = dy.cpu().numpy()
     rng = np.random.default_rng(2024)
     rows, cols = rng.integers(0, GEMM_N, 512), rng.integers(0, GEMM_N, 512)
     ref, bound = oracle.gemm_cells(A, B, rows, cols)
     gemm_ok, gemm_worst, _ = oracle.check(C[rows, cols], ref, bound)
-    yref, ybound = oracle.gemv_q2(Q0, S0, x)
-    q2_ok, q2_worst, _ = oracle.check(y, yref, ybound)
-    # the batched entry point on token 0's 40 products, checked on 3 of them
-    dys = [torch.empty(Q2_M, dtype=torch.float32, device=dev) for _ in range(CALLS_PER_TOKEN)]
-    bd.gemv_q2_batched(Qd[:CALLS_PER_TOKEN], Sd[:CALLS_PER_TOKEN], [dx] * CALLS_PER_TOKEN, ys=dys)
-    qb_ok, qb_worst = True, 0.0
-    for b in (0, 17, CALLS_PER_TOKEN - 1):
-        Qb, Sb = inputs.q2_weight(b)
-        rb, bb = oracle.gemv_q2(Qb, Sb, x)
-        ok, worst, _ = oracle.check(dys[b].cpu().numpy(), rb, bb)
-        qb_ok, qb_worst = qb_ok and ok, max(qb_worst, worst)
-    bd.gemv_q4(Q4d[0], S4d[0], dx, y=dy)
-    y4ref, y4bound = oracle.gemv_q4(Q40, S40, x)
-    q4_ok, q4_worst, _ = oracle.check(dy.cpu().numpy(), y4ref, y4bound)
-    bd.gemv_q4_batched(Q4d[:CALLS_PER_TOKEN], S4d[:CALLS_PER_TOKEN], [dx] * CALLS_PER_TOKEN,
-                       ys=dys)
-    q4b_ok, q4b_worst = True, 0.0
-    for b in (0, CALLS_PER_TOKEN - 1):
-        Qb, Sb = inputs.q4_weight(b)
-        rb, bb = oracle.gemv_q4(Qb, Sb, x)
-        ok, worst, _ = oracle.check(dys[b].cpu().numpy(), rb, bb)
-        q4b_ok, q4b_worst = q4b_ok and ok, max(q4b_worst, worst)
-    bd.gemv_f32(Wf[0], dxf, y=dy)
-    yfref, yfbound = oracle.gemv(W0, xf)
-    gf_ok, gf_worst, _ = oracle.check(dy.cpu().numpy(), yfref, yfbound)
-    bd.gemv_q2(QTd[0], STd[0], dxt, y=dyt)
-    ytref, ytbound = oracle.gemv_q2(QT0, ST0, xt)
-    qt_ok, qt_worst, _ = oracle.check(dyt.cpu().numpy(), ytref, ytbound)
-    log("parity: gemm worst %.3g, q2 worst %.3g, q2 batched worst %.3g, q4 worst %.3g, "
-        "q4 batched worst %.3g, q2 transposed worst %.3g, gemv_f32 worst %.3g (x 1e-4 bound)" %
-        (gemm_worst / 1e-4, q2_worst / 1e-4, qb_worst / 1e-4, q4_worst / 1e-4,
-         q4b_worst / 1e-4, qt_worst / 1e-4, gf_worst / 1e-4))
+
+    def packed_outputs(single, batched, Qs, Ss, xv, M):
+        """Each matrix of a set through the single-product entry point and
+        through batched launches of 64; both results on the host."""
+        n = len(Qs)
+        out_s = torch.empty((n, M), dtype=torch.float32, device=dev)
+        out_b = torch.empty((n, M), dtype=torch.float32, device=dev)
+        for r in range(n):
+            single(Qs[r], Ss[r], xv, y=out_s[r])
+        for b0 in range(0, n, 64):
+            idx = range(b0, min(n, b0 + 64))
+            batched([Qs[r] for r in idx], [Ss[r] for r in idx], [xv] * len(idx),
+                    ys=[out_b[r] for r in idx])
+        return out_s.cpu().numpy(), out_b.cpu().numpy()
+
+    q2s, q2b = packed_outputs(bd.gemv_q2, bd.gemv_q2_batched, Qd, Sd, dx, Q2_M)
+
+    def q2_ref(r):
+        Q, S = inputs.q2_weight(r)
+        return oracle.gemv_q2(Q, S, x)
+    with ThreadPoolExecutor(max_workers=usable_cores()) as pool:
+        q2_refs = list(pool.map(q2_ref, range(Q2_ROTATION)))
+
+    def check_set(outs, refs, what):
+        ok, worst = True, 0.0
+        for r, (ref_r, bound_r) in enumerate(refs):
+            good, w, idx = oracle.check(outs[r], ref_r, bound_r)
+            if not good:
+                log("parity FAIL: %s matrix %d at %s" % (what, r, idx))
+            ok, worst = ok and good, max(worst, w)
+        return ok, worst
+    q2_ok, q2_worst = check_set(q2s, q2_refs, "gemv_q2")
+    qb_ok, qb_worst = check_set(q2b, q2_refs, "gemv_q2_batched")
+    del q2_refs
+
+    q4s, q4b = packed_outputs(bd.gemv_q4, bd.gemv_q4_batched, Q4d, S4d, dx, Q2_M)
+
+    def q4_ref(r):
+        Q, S = inputs.q4_weight(r)
+        return oracle.gemv_q4(Q, S, x)
+    with ThreadPoolExecutor(max_workers=usable_cores()) as pool:
+        q4_refs = list(pool.map(q4_ref, range(Q4_ROTATION)))
+    q4_ok, q4_worst = check_set(q4s, q4_refs, "gemv_q4")
+    q4b_ok, q4b_worst = check_set(q4b, q4_refs, "gemv_q4_batched")
+    del q4_refs
+
+    qts, qtb = packed_outputs(bd.gemv_q2, bd.gemv_q2_batched, QTd, STd, dxt, QT_M)
+
+    def qt_ref(r):
+        Q, S = inputs.q2_weight(r, QT_M, QT_K)
+        return oracle.gemv_q2(Q, S, xt)
+    with ThreadPoolExecutor(max_workers=usable_cores()) as pool:
+        qt_refs = list(pool.map(qt_ref, range(Q2_ROTATION)))
+    qt_ok, qt_worst = check_set(qts, qt_refs, "gemv_q2 1536x12288")
+    qtb_ok, qtb_worst = check_set(qtb, qt_refs, "gemv_q2_batched 1536x12288")
+    del qt_refs
+
+    gf = torch.empty((F32_ROTATION, Q2_M), dtype=torch.float32, device=dev)
+    for r in range(F32_ROTATION):
+        bd.gemv_f32(Wf[r], dxf, y=gf[r])
+    gf = gf.cpu().numpy()
+    with ThreadPoolExecutor(max_workers=usable_cores()) as pool:
+        gf_refs = list(pool.map(lambda r: oracle.gemv(inputs.gemv_f32_weight(r), xf),
+                                range(F32_ROTATION)))
+    gf_ok, gf_worst = check_set(gf, gf_refs, "gemv_f32")
+    del gf_refs
+    parity = {
+        "gemm_f32_2048": "pass" if gemm_ok else "FAIL", "gemm_worst_err_over_bound": gemm_worst,
+        "gemv_q2": "pass" if q2_ok else "FAIL", "gemv_q2_worst": q2_worst,
+        "gemv_q2_batched": "pass" if qb_ok else "FAIL", "gemv_q2_batched_worst": qb_worst,
+        "gemv_q4": "pass" if q4_ok else "FAIL", "gemv_q4_worst": q4_worst,
+        "gemv_q4_batched": "pass" if q4b_ok else "FAIL", "gemv_q4_batched_worst": q4b_worst,
+        "gemv_q2_transposed": "pass" if qt_ok else "FAIL", "gemv_q2_transposed_worst": qt_worst,
+        "gemv_q2_transposed_batched": "pass" if qtb_ok else "FAIL",
+        "gemv_q2_transposed_batched_worst": qtb_worst,
+        "gemv_f32": "pass" if gf_ok else "FAIL", "gemv_f32_worst": gf_worst,
+        "note": ("worst |gpu - oracle| / sum|a*b| per element (bound 1e-4); the packed and "
+                 "fp32 GEMVs on every matrix of their rotation sets, through the single and "
+                 "the batched entry points; the 2048^3 GEMM on 512 sampled cells"),
+    }
+    log("parity in %.1f s: gemm %.3g, q2 %.3g, q2 batched %.3g, q4 %.3g, q4 batched %.3g, "
+        "q2 transposed %.3g / %.3g, gemv_f32 %.3g (x 1e-4 bound)" %
+        (time.perf_counter() - t0, gemm_worst / 1e-4, q2_worst / 1e-4, qb_worst / 1e-4,
+         q4_worst / 1e-4, q4b_worst / 1e-4, qt_worst / 1e-4, qtb_worst / 1e-4,
+         gf_worst / 1e-4))
+    del q2s, q2b, q4s, q4b, qts, qtb, gf
 
     if args.copy_calibration > 0:
         n = args.copy_calibration // 4
@@ -588,26 +591,8 @@ def main():
         log("calibration copy: %d bytes" % (4 * n))
         del src, dst
 
-    # ---- graphs.  A token is 40 q2 calls; 16 tokens cover the 128-matrix
-    #      rotation (lcm(40, 128) = 640 calls), so call n uses matrix n mod 128.
-    #      step_graphs[t]: one whole step (the GEMM, then token t).
-    #      gemm_graph: GEMMS_PER_REPLAY back-to-back GEMMs; tok_graphs[t]:
-    #      token t alone.  Those two time each kernel over runs of
-    #      back-to-back launches, so a kernel's average launch duration
-    #      carries no per-replay overhead.
+    # ---- graphs
     stream = torch.cuda.Stream(device=dev)
-    n_tok = 16
-    gemms_per_replay = 8
-    with torch.cuda.stream(stream):
-        for _ in range(3):
-            bd.gemm_f32(dA, dB, C=dC)
-            bd.gemv_q2(Qd[0], Sd[0], dx, y=dy)
-    stream.synchronize()
-
-    def token(t):
-        for c in range(CALLS_PER_TOKEN):
-            n = t * CALLS_PER_TOKEN + c
-            bd.gemv_q2(Qd[n % Q2_ROTATION], Sd[n % Q2_ROTATION], dx, y=dy)
 
     def capture(fn):
         g = torch.cuda.CUDAGraph()
@@ -615,157 +600,116 @@ def main():
             fn()
         return g
 
-    def token_batched(t):
-        idx = [(t * CALLS_PER_TOKEN + c) % Q2_ROTATION for c in range(CALLS_PER_TOKEN)]
-        bd.gemv_q2_batched([Qd[i] for i in idx], [Sd[i] for i in idx],
-                           [dx] * CALLS_PER_TOKEN, ys=dys)
+    def window(graph, launches, replays, warm_s=WARM_S):
+        """A fixed window: `replays` replays of `graph` (a graph, or a list of
+        graphs replayed in turn, holding `launches` back-to-back launches in
+        all) after `warm_s` seconds of warm-up replays, a HIP event on the
+        replay stream after each replay."""
+        graphs = graph if isinstance(graph, list) else [graph]
 
-    step_graphs = [capture(lambda t=t: (bd.gemm_f32(dA, dB, C=dC), token(t)))
-                   for t in range(n_tok)]
-    btok_graphs = [capture(lambda t=t: token_batched(t)) for t in range(n_tok)]
-
-    def token4(t):
-        for c in range(CALLS_PER_TOKEN):
-            n = (t * CALLS_PER_TOKEN + c) % Q4_ROTATION
-            bd.gemv_q4(Q4d[n], S4d[n], dx, y=dy)
-
-    def token4_batched(t):
-        idx = [(t * CALLS_PER_TOKEN + c) % Q4_ROTATION for c in range(CALLS_PER_TOKEN)]
-        bd.gemv_q4_batched([Q4d[i] for i in idx], [S4d[i] for i in idx],
-                           [dx] * CALLS_PER_TOKEN, ys=dys)
-
-    def tokent(t):
-        for c in range(CALLS_PER_TOKEN):
-            n = (t * CALLS_PER_TOKEN + c) % Q2_ROTATION
-            bd.gemv_q2(QTd[n], STd[n], dxt, y=dyt)
-
-    def tokent_batched(t):
-        idx = [(t * CALLS_PER_TOKEN + c) % Q2_ROTATION for c in range(CALLS_PER_TOKEN)]
-        bd.gemv_q2_batched([QTd[i] for i in idx], [STd[i] for i in idx],
-                           [dxt] * CALLS_PER_TOKEN, ys=dyts)
-
-    def tokenf(t):
-        for c in range(CALLS_PER_TOKEN):
-            bd.gemv_f32(Wf[(t * CALLS_PER_TOKEN + c) % F32_ROTATION], dxf, y=dy)
-
-    tokf_graphs = [capture(lambda t=t: tokenf(t)) for t in range(n_tok)]
-    tokt_graphs = [capture(lambda t=t: tokent(t)) for t in range(n_tok)]
-    btokt_graphs = [capture(lambda t=t: tokent_batched(t)) for t in range(n_tok)]
-    tok4_graphs = [capture(lambda t=t: token4(t)) for t in range(n_tok)]
-    btok4_graphs = [capture(lambda t=t: token4_batched(t)) for t in range(n_tok)]
-    tok_graphs = [capture(lambda t=t: token(t)) for t in range(n_tok)]
-    gemm_graph = capture(lambda: [bd.gemm_f32(dA, dB, C=dC)
-                                  for _ in range(gemms_per_replay)])
-    torch.cuda.synchronize()
-
-    def timed(replays, warm):
-        """HIP events on the replay stream around back-to-back replays."""
+        def replay():
+            for g in graphs:
+                g.replay()
         with torch.cuda.stream(stream):
-            for i in range(warm):
-                replays(i)
-            stream.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            t = time.perf_counter()
-            n = replays(None)
-            e1.record(stream)
-            stream.synchronize()
-            t = time.perf_counter() - t
-        return e0.elapsed_time(e1), n, t
-
-    def spread(graphs, launches, n=16):
-        """Per-launch durations over n single replays of graphs (run after the
-        main timing, one event pair per replay): median, p10, p90, min in us."""
-        with torch.cuda.stream(stream):
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+            t0 = time.perf_counter()
+            while True:
+                for _ in range(2):
+                    replay()
+                stream.synchronize()
+                if time.perf_counter() - t0 >= warm_s:
+                    break
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(replays + 1)]
             ev[0].record(stream)
-            for k in range(n):
-                graphs[k % len(graphs)].replay()
+            for k in range(replays):
+                replay()
                 ev[k + 1].record(stream)
             stream.synchronize()
-        us = sorted(1e3 * ev[k].elapsed_time(ev[k + 1]) / launches for k in range(n))
-        q = lambda f: us[min(n - 1, int(round(f * (n - 1))))]
-        return {"median_us": q(0.5), "p10_us": q(0.1), "p90_us": q(0.9), "min_us": us[0],
-                "replays": n, "launches_per_replay": launches,
-                "note": ("an event pair per replay: medians run a few percent above "
-                         "the uninterrupted back-to-back averages")}
+        per = sorted(1e3 * ev[k].elapsed_time(ev[k + 1]) / launches for k in range(replays))
+        total_us = 1e3 * ev[0].elapsed_time(ev[-1])
+        return {"mean_us": total_us / (launches * replays),
+                "median_us": per[len(per) // 2] if replays % 2 else
+                0.5 * (per[replays // 2 - 1] + per[replays // 2]),
+                "min_us": per[0], "max_us": per[-1], "launches": launches * replays,
+                "launches_per_replay": launches, "replays": replays, "warmup_s": warm_s}
 
-    def run_steps(i):
-        if i is not None:
-            step_graphs[i % n_tok].replay()
-            return 1
-        for s in range(args.steps):
-            step_graphs[(args.warmup + s) % n_tok].replay()
-        return args.steps
+    def tok_idx(t, rot):
+        return [(t * CALLS_PER_TOKEN + c) % rot for c in range(CALLS_PER_TOKEN)]
 
-    n_gemm_replays = max(1, (args.steps + gemms_per_replay - 1) // gemms_per_replay)
+    def singles(fn, Qs, Ss, xv, y, rot):
+        return lambda: [fn(Qs[n % rot], Ss[n % rot], xv, y=y) for n in range(WIN_SINGLE[0])]
 
-    def run_gemms(i):
-        if i is not None:
-            gemm_graph.replay()
-            return 1
-        for _ in range(n_gemm_replays):
-            gemm_graph.replay()
-        return n_gemm_replays * gemms_per_replay
-
-    def run_tokens(i):
-        if i is not None:
-            tok_graphs[i % n_tok].replay()
-            return 1
-        for s in range(args.steps):
-            tok_graphs[s % n_tok].replay()
-        return args.steps * CALLS_PER_TOKEN
-
-    def token_runner(graphs):
-        def run(i):
-            if i is not None:
-                graphs[i % n_tok].replay()
-                return 1
-            for s in range(args.steps):
-                graphs[s % n_tok].replay()
-            return args.steps * CALLS_PER_TOKEN
+    def batches(fn, Qs, Ss, xv, ys, rot):
+        def run():
+            for t in range(N_TOK):
+                idx = tok_idx(t, rot)
+                fn([Qs[i] for i in idx], [Ss[i] for i in idx], [xv] * CALLS_PER_TOKEN, ys=ys)
         return run
 
-    run_btokens = token_runner(btok_graphs)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            bd.gemm_f32(dA, dB, C=dC)
+            batches(bd.gemv_q2_batched, Qd, Sd, dx, dys, Q2_ROTATION)()
+    stream.synchronize()
 
-    total_ms, _, t_wall = timed(run_steps, args.warmup)
-    gemm_ms, n_gemm, _ = timed(run_gemms, max(1, args.warmup // gemms_per_replay))
-    tok_ms, n_q2, _ = timed(run_tokens, args.warmup)
-    btok_ms, n_qb, _ = timed(run_btokens, args.warmup)
-    qb_us = 1e3 * btok_ms / n_qb
-    qb_alg_gbs = Q2_ALG_BYTES / qb_us / 1e3
-    tok4_ms, n_q4, _ = timed(token_runner(tok4_graphs), args.warmup)
-    btok4_ms, n_q4b, _ = timed(token_runner(btok4_graphs), args.warmup)
-    q4_us = 1e3 * tok4_ms / n_q4
-    q4b_us = 1e3 * btok4_ms / n_q4b
-    tokt_ms, n_qt, _ = timed(token_runner(tokt_graphs), args.warmup)
-    btokt_ms, n_qtb, _ = timed(token_runner(btokt_graphs), args.warmup)
-    qt_us = 1e3 * tokt_ms / n_qt
-    tokf_ms, n_gf, _ = timed(token_runner(tokf_graphs), args.warmup)
-    gf_us = 1e3 * tokf_ms / n_gf
-    qtb_us = 1e3 * btokt_ms / n_qtb
-    gemm_us = 1e3 * gemm_ms / n_gemm
-    q2_us = 1e3 * tok_ms / n_q2
+    # whole steps: the GEMM, then token t's 40 products in one launch
+    step_graphs = []
+    for t in range(N_TOK):
+        idx = tok_idx(t, Q2_ROTATION)
+        step_graphs.append(capture(lambda idx=idx: (
+            bd.gemm_f32(dA, dB, C=dC),
+            bd.gemv_q2_batched([Qd[i] for i in idx], [Sd[i] for i in idx],
+                               [dx] * CALLS_PER_TOKEN, ys=dys))))
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step_graphs[i % N_TOK].replay()
+        stream.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        t_wall = time.perf_counter()
+        for s in range(args.steps):
+            step_graphs[(args.warmup + s) % N_TOK].replay()
+        e1.record(stream)
+        stream.synchronize()
+        t_wall = time.perf_counter() - t_wall
+    total_ms = e0.elapsed_time(e1)
+    del step_graphs
 
-    # ---- context, after the main timing: the spread of per-launch times,
-    #      the 2-bit GEMV with one cache-resident matrix ("hot"), and what a
-    #      plain device-to-device copy streams on this GPU.
-    spreads = {
-        "gemm_f32": spread([gemm_graph], gemms_per_replay),
-        "gemv_q2": spread(tok_graphs, CALLS_PER_TOKEN),
-        "gemv_q2_batched": spread(btok_graphs, CALLS_PER_TOKEN),
-        "gemv_q4": spread(tok4_graphs, CALLS_PER_TOKEN),
-        "gemv_q4_batched": spread(btok4_graphs, CALLS_PER_TOKEN),
-        "gemv_q2_transposed": spread(tokt_graphs, CALLS_PER_TOKEN),
-        "gemv_q2_transposed_batched": spread(btokt_graphs, CALLS_PER_TOKEN),
-        "gemv_f32": spread(tokf_graphs, CALLS_PER_TOKEN),
-    }
-    hot_graph = capture(lambda: [bd.gemv_q2(Qd[0], Sd[0], dx, y=dy)
-                                 for _ in range(CALLS_PER_TOKEN)])
-    hot_ms, n_hot, _ = timed(token_runner([hot_graph] * n_tok), args.warmup)
-    q2_hot_us = 1e3 * hot_ms / n_hot
-    del hot_graph
+    # per-kernel windows
+    win = {}
+    g = capture(lambda: [bd.gemm_f32(dA, dB, C=dC) for _ in range(WIN_GEMM[0])])
+    win["gemm_f32"] = window(g, *WIN_GEMM)
+    del g
+    for name, mk, gw in (
+            ("gemv_q2_batched", batches(bd.gemv_q2_batched, Qd, Sd, dx, dys, Q2_ROTATION),
+             WIN_BATCHED),
+            ("gemv_q2", singles(bd.gemv_q2, Qd, Sd, dx, dy, Q2_ROTATION), WIN_SINGLE),
+            ("gemv_q4_batched", batches(bd.gemv_q4_batched, Q4d, S4d, dx, dys, Q4_ROTATION),
+             WIN_BATCHED),
+            ("gemv_q4", singles(bd.gemv_q4, Q4d, S4d, dx, dy, Q4_ROTATION), WIN_SINGLE),
+            ("gemv_q2_transposed_batched",
+             batches(bd.gemv_q2_batched, QTd, STd, dxt, dyts, Q2_ROTATION), WIN_BATCHED),
+            ("gemv_q2_transposed", singles(bd.gemv_q2, QTd, STd, dxt, dyt, Q2_ROTATION),
+             WIN_SINGLE),
+            ("gemv_f32", lambda: [bd.gemv_f32(Wf[n % F32_ROTATION], dxf, y=dy)
+                                  for n in range(WIN_SINGLE[0])], WIN_SINGLE)):
+        g = capture(mk)
+        win[name] = window(g, *gw)
+        del g
+        log("%-28s mean %.3f us, median %.3f us per launch" %
+            (name, win[name]["mean_us"], win[name]["median_us"]))
+    per_product = {k: (win[k]["mean_us"] / CALLS_PER_TOKEN if k.endswith("_batched")
+                       else win[k]["mean_us"]) for k in win}
+
+    # ---- context, after the main timing
+    #  * the 2-bit GEMV on one cache-resident matrix ("hot");
+    #  * a near-empty kernel back to back: the per-launch floor of the queue;
+    #  * what a plain device-to-device copy streams.
+    g = capture(lambda: [bd.gemv_q2(Qd[0], Sd[0], dx, y=dy) for _ in range(WIN_SINGLE[0])])
+    q2_hot_us = window(g, WIN_SINGLE[0], 2)["mean_us"]
+    small = torch.zeros(256 * 256, dtype=torch.float32, device=dev)
+    g = capture(lambda: [small.fill_(1.0) for _ in range(WIN_SINGLE[0])])
+    floor_us = window(g, WIN_SINGLE[0], 2)["mean_us"]
+    del g, small
     copy_bytes = 1 << 30
     with torch.cuda.stream(stream):
         csrc = torch.empty(copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -780,18 +724,14 @@ def main():
         stream.synchronize()
     copy_gbs = 2 * copy_bytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del csrc, cdst
-    vendor = vendor_context(torch, stream, capture, timed, token_runner, n_tok, gemms_per_replay,
-                            dA, dB, Wf, dxf, A, B, args)
-    configs, configs_ok = gemm_configs(torch, bd, inputs, oracle, dev, stream, capture, timed,
-                                       args.steps)
+    vendor = vendor_context(torch, stream, capture, window, dA, dB, Wf, dxf)
+    torch.cuda.synchronize()
+    configs, configs_ok = gemm_configs(torch, bd, inputs, oracle, dev, capture, window)
 
+    gemm_us = win["gemm_f32"]["mean_us"]
     gemm_tflops = GEMM_FLOPS / gemm_us / 1e6
-    q2_gbs = Q2_WEIGHT_BYTES / q2_us / 1e3
-    q2_alg_gbs = Q2_ALG_BYTES / q2_us / 1e3
-
-    gemm_traffic = traffic_from_profile("traffic_gemm_f32_2048.json",
-                                        src_sha("gemm_f32.hip"))
     psha = src_sha("gemv_packed.hip", "wave.hpp")
+    gemm_traffic = traffic_from_profile("traffic_gemm_f32_2048.json", src_sha("gemm_f32.hip"))
     q2_traffic = traffic_from_profile("traffic_gemv_q2_12288x1536.json", psha)
     qb_traffic = traffic_from_profile("traffic_gemv_q2_batched_12288x1536.json", psha)
     q4_traffic = traffic_from_profile("traffic_gemv_q4_12288x1536.json", psha)
@@ -799,11 +739,19 @@ def main():
     qt_traffic = traffic_from_profile("traffic_gemv_q2_1536x12288.json", psha)
     gf_traffic = traffic_from_profile("traffic_gemv_f32_12288x1536.json",
                                       src_sha("gemv_f32.hip", "wave.hpp"))
+    per_prod_note = "HBM bytes per product (launch total / 40)"
 
     cpu = None
     if not args.no_cpu_baseline:
+        Q0, S0 = inputs.q2_weight(0)
         cpu = cpu_baseline(A, B, Q0, S0, x)
 
+    all_ok = (gemm_ok and q2_ok and qb_ok and q4_ok and q4b_ok and qt_ok and qtb_ok and gf_ok
+              and configs_ok)
+    qb_us, q2_us = per_product["gemv_q2_batched"], per_product["gemv_q2"]
+    q4b_us, q4_us = per_product["gemv_q4_batched"], per_product["gemv_q4"]
+    qtb_us, qt_us = per_product["gemv_q2_transposed_batched"], per_product["gemv_q2_transposed"]
+    gf_us = per_product["gemv_f32"]
     out = {
         "metric": "fp32 GEMM TFLOP/s at 2048^3; 2-bit GEMV weight GB/s at 12288x1536",
         "value": gemm_tflops if gemm_ok else None,
@@ -815,22 +763,24 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": (gemm_tflops / PAGE_GEMM_2048_TFLOPS) if gemm_ok else None,
-        "vs_baseline_note": ("against the page's blocked4 WebGPU kernel at 2048^3 "
-                             "(9.12 ms = 1.88 TFLOP/s) on an Apple M-series laptop: "
-                             "context from other hardware, not a target"),
+        "vs_baseline_note": ("the pages' own figure for this metric and workload: the blocked4 "
+                             "WebGPU kernel at 2048^3 (9.12 ms = 1.88 TFLOP/s) on an Apple "
+                             "M-series laptop -- other hardware, context and not a target; "
+                             "vs_cpu_baseline is the ratio to the oracle timed here"),
+        "vs_cpu_baseline": (gemm_tflops / cpu["value"]) if (gemm_ok and cpu) else None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {
             "workload": ("per step: gemm_f32 2048x2048x2048 (A, B uniform[-1,1), seed 3) "
-                         "+ one token of 40 gemv_q2 12288x1536 calls rotating over 128 "
-                         "seeded matrices (648 MiB of codes+scales)"),
+                         "+ one token of 40 2-bit 12288x1536 products in one gemv_q2_batched "
+                         "launch, rotating over 128 seeded matrices (648 MiB of codes+scales)"),
             "gemm": "2048x2048x2048 NN",
             "q2_gemv": "12288x1536, 2-bit codes + fp16 scale per 64 columns",
             "rotation": Q2_ROTATION,
             "calls_per_token": CALLS_PER_TOKEN,
-            "timing": ("HIP graph replay; HIP events on the replay stream around "
-                       "K whole steps, and around runs of back-to-back GEMM and "
-                       "q2 launches for each kernel's average launch duration"),
+            "timing": ("HIP graph replay; ms_per_step: HIP events around K whole steps; each "
+                       "kernel: a fixed window of back-to-back launches (launches per graph x "
+                       "replays, after %.1f s of warm-up), mean over the window" % WARM_S),
         },
         "roofline": {
             "kernel": "gemm_f32 (NN, 2048^3)",
@@ -841,40 +791,28 @@ def main():
             "frac": gemm_tflops / PEAK_FP32_MFMA_TFLOPS,
             "traffic": gemm_traffic,
             "avg_launch_us": gemm_us,
-        },
-        "q2_gemv": {
-            "metric": "2-bit GEMV effective weight-streaming GB/s at 12288x1536 (cold rotation)",
-            "value": q2_gbs if q2_ok else None,
-            "unit": "GB/s",
-            "codes_only_gbs": Q2_CODE_BYTES / q2_us / 1e3 if q2_ok else None,
-            "avg_launch_us": q2_us,
-            "roofline": {
-                "kernel": "gemv_q2 (12288x1536)",
-                "bound": "hbm",
-                "achieved": q2_alg_gbs,
-                "peak": PEAK_HBM_GBS,
-                "unit": "GB/s",
-                "frac": q2_alg_gbs / PEAK_HBM_GBS,
-                "traffic": q2_traffic,
-            },
+            "median_launch_us": win["gemm_f32"]["median_us"],
+            "launches": win["gemm_f32"]["launches"],
         },
         "q2_gemv_batched": {
             "metric": ("2-bit GEMV effective weight-streaming GB/s at 12288x1536, one "
                        "token's 40 products in one gemv_q2_batched launch (cold rotation)"),
             "value": Q2_WEIGHT_BYTES / qb_us / 1e3 if qb_ok else None,
             "unit": "GB/s",
+            "codes_only_gbs": Q2_CODE_BYTES / qb_us / 1e3,
             "us_per_gemv": qb_us,
-            "us_per_token": qb_us * CALLS_PER_TOKEN,
-            "roofline": {
-                "kernel": "gemv_q2_batched (40 x 12288x1536 per launch)",
-                "bound": "hbm",
-                "achieved": qb_alg_gbs,
-                "peak": PEAK_HBM_GBS,
-                "unit": "GB/s",
-                "frac": qb_alg_gbs / PEAK_HBM_GBS,
-                "traffic": (qb_traffic / CALLS_PER_TOKEN) if qb_traffic else None,
-                "traffic_note": "HBM bytes per product (launch total / 40)",
-            },
+            "us_per_token": win["gemv_q2_batched"]["mean_us"],
+            "roofline": roofline("gemv_q2_batched (40 x 12288x1536 per launch)", Q2_ALG_BYTES,
+                                 qb_us, qb_traffic / CALLS_PER_TOKEN if qb_traffic else None,
+                                 per_prod_note),
+        },
+        "q2_gemv": {
+            "metric": "2-bit GEMV effective weight-streaming GB/s at 12288x1536 (cold rotation)",
+            "value": Q2_WEIGHT_BYTES / q2_us / 1e3 if q2_ok else None,
+            "unit": "GB/s",
+            "codes_only_gbs": Q2_CODE_BYTES / q2_us / 1e3,
+            "avg_launch_us": q2_us,
+            "roofline": roofline("gemv_q2 (12288x1536)", Q2_ALG_BYTES, q2_us, q2_traffic),
         },
         "q4_gemv": {
             "metric": ("4-bit GEMV effective weight-streaming GB/s at 12288x1536 "
@@ -882,29 +820,15 @@ def main():
             "value": Q4_WEIGHT_BYTES / q4_us / 1e3 if q4_ok else None,
             "unit": "GB/s",
             "avg_launch_us": q4_us,
-            "roofline": {
-                "kernel": "gemv_q4 (12288x1536)",
-                "bound": "hbm",
-                "achieved": Q4_ALG_BYTES / q4_us / 1e3,
-                "peak": PEAK_HBM_GBS,
-                "unit": "GB/s",
-                "frac": Q4_ALG_BYTES / q4_us / 1e3 / PEAK_HBM_GBS,
-                "traffic": q4_traffic,
-            },
+            "roofline": roofline("gemv_q4 (12288x1536)", Q4_ALG_BYTES, q4_us, q4_traffic),
             "batched": {
                 "value": Q4_WEIGHT_BYTES / q4b_us / 1e3 if q4b_ok else None,
                 "unit": "GB/s",
                 "us_per_gemv": q4b_us,
-                "roofline": {
-                    "kernel": "gemv_q4_batched (40 x 12288x1536 per launch)",
-                    "bound": "hbm",
-                    "achieved": Q4_ALG_BYTES / q4b_us / 1e3,
-                    "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s",
-                    "frac": Q4_ALG_BYTES / q4b_us / 1e3 / PEAK_HBM_GBS,
-                    "traffic": (q4b_traffic / CALLS_PER_TOKEN) if q4b_traffic else None,
-                    "traffic_note": "HBM bytes per product (launch total / 40)",
-                },
+                "roofline": roofline("gemv_q4_batched (40 x 12288x1536 per launch)",
+                                     Q4_ALG_BYTES, q4b_us,
+                                     q4b_traffic / CALLS_PER_TOKEN if q4b_traffic else None,
+                                     per_prod_note),
             },
         },
         "q2_gemv_transposed": {
@@ -914,17 +838,9 @@ def main():
             "value": Q2_WEIGHT_BYTES / qt_us / 1e3 if qt_ok else None,
             "unit": "GB/s",
             "avg_launch_us": qt_us,
-            "roofline": {
-                "kernel": "gemv_q2 (1536x12288)",
-                "bound": "hbm",
-                "achieved": QT_ALG_BYTES / qt_us / 1e3,
-                "peak": PEAK_HBM_GBS,
-                "unit": "GB/s",
-                "frac": QT_ALG_BYTES / qt_us / 1e3 / PEAK_HBM_GBS,
-                "traffic": qt_traffic,
-            },
+            "roofline": roofline("gemv_q2 (1536x12288)", QT_ALG_BYTES, qt_us, qt_traffic),
             "batched": {
-                "value": Q2_WEIGHT_BYTES / qtb_us / 1e3 if qt_ok else None,
+                "value": Q2_WEIGHT_BYTES / qtb_us / 1e3 if qtb_ok else None,
                 "unit": "GB/s",
                 "us_per_gemv": qtb_us,
                 "frac": QT_ALG_BYTES / qtb_us / 1e3 / PEAK_HBM_GBS,
@@ -935,53 +851,54 @@ def main():
             "value": F32_ALG_BYTES / gf_us / 1e3 if gf_ok else None,
             "unit": "GB/s",
             "avg_launch_us": gf_us,
-            "roofline": {
-                "kernel": "gemv_f32 (12288x1536)",
-                "bound": "hbm",
-                "achieved": F32_ALG_BYTES / gf_us / 1e3,
-                "peak": PEAK_HBM_GBS,
-                "unit": "GB/s",
-                "frac": F32_ALG_BYTES / gf_us / 1e3 / PEAK_HBM_GBS,
-                "traffic": gf_traffic,
-            },
+            "roofline": roofline("gemv_f32 (12288x1536)", F32_ALG_BYTES, gf_us, gf_traffic),
         },
+        "windows": win,
         "gemm_configs": configs,
-        "spread": spreads,
         "context": {
             "q2_gemv_hot_us": q2_hot_us,
-            "q2_gemv_hot_note": ("gemv_q2 12288x1536 on one matrix, 40 back-to-back calls: "
-                                 "weights resident in cache, the launch-and-compute floor"),
+            "q2_gemv_hot_note": ("gemv_q2 12288x1536 on one matrix, back to back: weights "
+                                 "resident in cache, the launch-and-compute floor"),
+            "launch_floor_us": floor_us,
+            "launch_floor_note": ("a fill of 256 KiB (a near-empty kernel) back to back in "
+                                  "one graph: the queue's per-launch floor"),
             "hbm_copy_gbs": copy_gbs,
             "hbm_copy_note": ("torch device-to-device copy of 1 GiB, 10 times, "
                               "read + write bytes / time: what plain streaming reaches"),
             "vendor_library": vendor,
         },
-        "parity": {"gemm_f32_2048": "pass" if gemm_ok else "FAIL",
-                   "gemm_configs": "pass" if configs_ok else "FAIL",
-                   "gemv_f32": "pass" if gf_ok else "FAIL",
-                   "gemv_f32_worst_err_over_bound": gf_worst,
-                   "gemv_q2_transposed": "pass" if qt_ok else "FAIL",
-                   "q2_transposed_worst_err_over_bound": qt_worst,
-                   "gemv_q4": "pass" if q4_ok else "FAIL",
-                   "gemv_q4_batched": "pass" if q4b_ok else "FAIL",
-                   "q4_worst_err_over_bound": q4_worst,
-                   "q4_batched_worst_err_over_bound": q4b_worst,
-                   "gemv_q2": "pass" if q2_ok else "FAIL",
-                   "gemv_q2_batched": "pass" if qb_ok else "FAIL",
-                   "q2_batched_worst_err_over_bound": qb_worst,
-                   "gemm_worst_err_over_bound": gemm_worst,
-                   "q2_worst_err_over_bound": q2_worst},
+        "parity": parity,
         "cpu_baseline": cpu,
         "inputs_sha256": hashes,
         "device": {"name": prop.name, "arch": getattr(prop, "gcnArchName", None),
                    "cus": prop.multi_processor_count, "torch": torch.__version__,
                    "hip": getattr(torch.version, "hip", None), "host_cpu": host_cpu(),
-                   "host_cores_usable": len(os.sched_getaffinity(0))},
+                   "host_cores_usable": usable_cores()},
         "wall_s_timed": t_wall,
     }
+    ok_s = lambda b: "pass" if b else "FAIL"
+    out["summary"] = {
+        "gemm_2048": {"us": round(gemm_us, 2), "tflops": round(gemm_tflops, 1),
+                      "frac": round(gemm_tflops / PEAK_FP32_MFMA_TFLOPS, 3),
+                      "parity": ok_s(gemm_ok)},
+        "q2_batched": {"us_per_product": round(qb_us, 3),
+                       "weight_gbs": round(Q2_WEIGHT_BYTES / qb_us / 1e3, 0),
+                       "frac": round(Q2_ALG_BYTES / qb_us / 1e3 / PEAK_HBM_GBS, 3),
+                       "parity": ok_s(qb_ok)},
+        "q2_single": {"us": round(q2_us, 3),
+                      "weight_gbs": round(Q2_WEIGHT_BYTES / q2_us / 1e3, 0),
+                      "frac": round(Q2_ALG_BYTES / q2_us / 1e3 / PEAK_HBM_GBS, 3),
+                      "parity": ok_s(q2_ok)},
+        "q4_batched_frac": round(Q4_ALG_BYTES / q4b_us / 1e3 / PEAK_HBM_GBS, 3),
+        "gemv_f32_frac": round(F32_ALG_BYTES / gf_us / 1e3 / PEAK_HBM_GBS, 3),
+        "gpt2_block_frac": round(configs.get("gpt2_block_9_products", {})
+                                 .get("frac_of_fp32_mfma_peak", float("nan")), 3),
+        "parity_all": ok_s(all_ok),
+        "cpu_oracle_tflops": round(cpu["value"], 5) if cpu else None,
+        "cpu_cores": cpu["cores"] if cpu else None,
+    }
     print(json.dumps(out), flush=True)
-    return 0 if (gemm_ok and q2_ok and qb_ok and q4_ok and q4b_ok and qt_ok and gf_ok
-                 and configs_ok) else 1
+    return 0 if all_ok else 1
 
 
 if __name__ == "__main__":

@@ -687,6 +687,314 @@ hipError_t launch_chunk(int count, int M, int K, const uint8_t *const *Q, int64_
                   M, K, ldq, lds, p);
 }
 
+// ---------------------------------------------------------------------------
+// 2-bit codes with integer dot products.  The multiply-add unpack above costs
+// 16 v_fma_mix_f32 and 9 bit operations per 16 weights; a batch of 2-bit
+// products is bound by that work, not by HBM.  v_dot8_i32_i4 multiplies 8
+// pairs of signed nibbles and adds them to an int32, so with x held as
+// integers the codes need no conversion at all:
+//
+//  * x as integers.  Per 64-column chunk (one scale group) let E be the
+//    exponent of the chunk's largest |x| (max |x| < 2^E) and
+//    q_k = rint(x_k 2^(22-E)), so |q_k| <= 2^22 and |x_k - q_k 2^(E-22)| <=
+//    2^(E-23).  q + 0x888888 has six nibbles d_i + 8 with
+//    q = sum_i d_i 16^i and d_i in [-8, 7]; flipping bit 3 of each nibble
+//    gives d_i as a signed nibble.  The rounding to an integer is done by the
+//    fp32 add of 1.5 * 2^23, whose bit pattern then holds q + 2^22.
+//  * Lanes.  A wave reads 8 chunks of 8 rows per step: lane l takes chunk
+//    8 * wave + (l & 7) of row l >> 3, so each load instruction covers eight
+//    128-byte segments, and the 8 lanes that share a chunk sit in one wave.
+//    Those 8 lanes split the chunk's set-up, lane j taking the even (j even)
+//    or odd columns of unit j >> 1 (a unit is 16 columns, one code word):
+//    they quantise their 8 columns and transpose the 8 x 6 nibbles into six
+//    digit words (word i holds digit i of the 8 columns), and swap them
+//    through LDS inside the wave, so every lane holds the 48 digit words of
+//    its chunk.  The chunk's maximum and sum of q meet by lane shuffles.
+//  * Steps.  For a code word w, w & 0x33333333 holds the codes of its even
+//    columns in nibbles 0..7 and (w >> 2) & 0x33333333 those of its odd
+//    columns.  Twelve v_dot8_i32_i4 per word (one chain per digit) give
+//    acc_i = sum c d_i over the chunk, exactly; then
+//        T = sum_i acc_i 16^i = sum_k c_k q_k            (|T| < 2^30),
+//        Z = 2 T - 3 sum_k q_k = 2 sum_k (c_k - 3/2) q_k   (|Z| < 2^31),
+//    both exact in int32, and the chunk's share of the row is
+//    s 2^(E-23) Z.  That is 15 instructions per 16 weights and 9 per chunk.
+//  * Rounding.  Only x is rounded.  Over a chunk that moves the sum by at
+//    most 64 * (3/2) s 2^(E-23), while the chunk's share of the bound is
+//    sum |w x| >= (s/2) max |x| >= s 2^(E-2): at most 48 * 2^-20 = 4.6e-5 of
+//    it.  Converting Z to fp32, the scale product and the row's sum over
+//    chunks add at most (3 + chunks) * 3 * 2^-24 of it: below 1e-5 for up to
+//    48 chunks.  This holds for every finite x and s for which no partial
+//    sum overflows or falls below the normal range (s 2^(E-23) |Z| above
+//    2^-126 wherever it is not zero).
+//  * Non-finite x.  A NaN or an infinity in x makes every output NaN (its
+//    chunk's quantised values leave the 24-bit range, which the set-up
+//    detects); a non-finite scale makes its own row non-finite.
+//  * Scales.  Lane l of a wave loads the 8 scales of its wave's chunks in
+//    row l of the workgroup with one 16-byte load and the lanes trade them
+//    through LDS, instead of one 2-byte load per lane and step.
+//  * Reduction.  The row's partial sums meet in LDS after one barrier and one
+//    lane per row adds them in a fixed pairwise tree: deterministic.
+constexpr int IDOT_MAX_WAVES = FLAT_MAX_CPR / 8;
+
+template <int WAVES, int T>
+struct IdotSmem {
+    static constexpr int CPR = 8 * WAVES, ROWS = 8 * T, PS = CPR + 4;
+    unsigned dig[WAVES][8 * 48];          // per wave: 8 chunks x 8 lanes x 6 digit words
+    uint16_t scl[WAVES][ROWS * 8];        // per wave: row x its 8 chunks' scales
+    float part[ROWS * PS];                // row x chunk partial sums
+    int bad[WAVES];
+};
+
+// a * b over 8 signed nibble pairs, as the first product of a chain (the
+// VOP3P form with an inline zero addend: no move of a zero into the
+// accumulator first, as the accumulating VOP2 form needs)
+__device__ __forceinline__ int dot8_first(int a, int b) {
+    int r;
+    asm("v_dot8_i32_i4 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// binary16 h (the low half of hb) times fp32 f, in one mixed-precision
+// multiply-add with a zero addend
+__device__ __forceinline__ float mul_half(unsigned hb, float f) {
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hb), "v"(f));
+    return r;
+}
+
+__device__ __forceinline__ unsigned nib_swap(unsigned a, unsigned b, bool hi) {
+    // one output of the 4-bit stage of the transpose
+    return hi ? (((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u))
+              : ((a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u));
+}
+
+// WAVES waves per workgroup (the row has 8 * WAVES chunks), T steps of 8
+// rows, NB products per pointer block.
+template <int WAVES, int T, int NB>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 1 : 4)))
+void gemv_q2_idot(int M, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
+    using Sm = IdotSmem<WAVES, T>;
+    constexpr int CPR = Sm::CPR, ROWS = Sm::ROWS, PS = Sm::PS;
+    __shared__ __attribute__((aligned(16))) Sm sm;
+
+    const int b = NB == 1 ? 0 : (int)blockIdx.y;
+    const int w = (int)threadIdx.x >> 6, l = (int)threadIdx.x & 63;
+    const int cl = l & 7, j = l >> 3, c = 8 * w + cl, u = j >> 1;
+    const unsigned odd = 0u - (unsigned)(j & 1);   // all ones for the odd-column lanes
+    const int row0 = (int)blockIdx.x * ROWS;
+
+    // ---- Loads, in the order they are needed (vector-memory loads retire in
+    // issue order): the unit's 16 x values, the 16-byte scale block, then
+    // every code chunk of the T steps.
+    v4f xr[4];
+    {
+        const v4f *xp = reinterpret_cast<const v4f *>(ptrs.x[b] + 64 * c + 16 * u);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xr[q] = xp[q];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    u4 sraw;
+    unsigned craw[T][4];
+#if defined(__HIP_DEVICE_COMPILE__)
+    {
+        const int rows_left = M - row0;       // >= 1
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(ptrs.Q[b] + (int64_t)row0 * ldq), (short)0,
+            (int)((int64_t)(rows_left - 1) * ldq + 16 * CPR), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(ptrs.S[b] + (int64_t)row0 * lds), (short)0,
+            (int)(((int64_t)(rows_left - 1) * lds + CPR) * 2), 0x00020000);
+        // lanes past the workgroup's rows load from past the resource: zeros
+        const int soff = l < ROWS ? (int)((unsigned)l * (unsigned)lds * 2u + 16u * (unsigned)w)
+                                  : 0x7FFFFFF0;
+        sraw = __builtin_amdgcn_raw_buffer_load_b128(rs, soff, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        const unsigned vq = (unsigned)j * (unsigned)ldq + 16u * (unsigned)c;
+        const unsigned sq = 8u * (unsigned)ldq;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const u4 v = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(vq + t * sq), 0, NT);
+            craw[t][0] = v.x;
+            craw[t][1] = v.y;
+            craw[t][2] = v.z;
+            craw[t][3] = v.w;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#else
+    sraw = u4{0u, 0u, 0u, 0u};
+    for (int t = 0; t < T; ++t) craw[t][0] = craw[t][1] = craw[t][2] = craw[t][3] = 0u;
+#endif
+
+    // ---- Set-up: this lane's 8 columns of the chunk as digit words.
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        v[4 * q] = xr[q].x;
+        v[4 * q + 1] = xr[q].y;
+        v[4 * q + 2] = xr[q].z;
+        v[4 * q + 3] = xr[q].w;
+    }
+    float mx = 0.f;   // largest |x| of the unit (a NaN is skipped here, caught below)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) mx = __builtin_fmaxf(mx, __builtin_fabsf(v[q]));
+    // ... and of the chunk: the other units' lanes are l ^ 16 and l ^ 32
+    mx = __builtin_fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(mx), 0x401F)));
+    mx = __builtin_fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute((l ^ 32) << 2,
+                                                                          __float_as_int(mx))));
+    const int E = __builtin_amdgcn_frexp_expf(mx);   // max |x| < 2^E; 0 for 0 and non-finite
+    unsigned uq[8];
+    int qs = 0;
+    unsigned orr = 0;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        // the odd or even column, by a bit select (not an indexed load)
+        const float xv = __uint_as_float((__float_as_uint(v[2 * m + 1]) & odd) |
+                                         (__float_as_uint(v[2 * m]) & ~odd));
+        const float t = __builtin_amdgcn_ldexpf(xv, 22 - E) + 12582912.f;   // + 1.5 * 2^23
+        uq[m] = __float_as_uint(t) - 0x4AB77778u;      // q + 0x888888
+        orr |= uq[m];
+        qs += (int)uq[m];
+    }
+    qs -= 8 * 0x888888;
+    const bool bad = (orr >> 24) != 0u;                // a NaN or an infinity in x
+    // the chunk's sum of q over its 8 lanes: l ^ 8, l ^ 16, l ^ 32
+    qs += __builtin_amdgcn_update_dpp(0, qs, 0x128, 0xF, 0xF, false);   // row_ror:8
+    qs += __builtin_amdgcn_ds_swizzle(qs, 0x401F);
+    qs += __builtin_amdgcn_ds_bpermute((l ^ 32) << 2, qs);
+    const unsigned neg3q = (unsigned)(-3 * qs);
+    const int kz = E - 23;
+    // transpose the 8 x 8 nibbles (digits 6, 7 are zero and dropped): halves,
+    // then bytes, then nibbles
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const unsigned A = uq[r], B = uq[r + 4];
+        uq[r] = __builtin_amdgcn_perm(B, A, 0x05040100u);
+        uq[r + 4] = __builtin_amdgcn_perm(B, A, 0x07060302u);
+    }
+#pragma unroll
+    for (int r = 0; r < 8; r += 4)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const unsigned A = uq[r + h], B = uq[r + h + 2];
+            uq[r + h] = __builtin_amdgcn_perm(B, A, 0x06020400u);
+            uq[r + h + 2] = __builtin_amdgcn_perm(B, A, 0x07030501u);
+        }
+    unsigned dg[6];
+#pragma unroll
+    for (int r = 0; r < 6; r += 2) {
+        dg[r] = nib_swap(uq[r], uq[r + 1], false) ^ 0x88888888u;
+        dg[r + 1] = nib_swap(uq[r], uq[r + 1], true) ^ 0x88888888u;
+    }
+    // ---- Swap digit words and scales inside the wave through LDS.
+    {
+        u2 *dst = reinterpret_cast<u2 *>(&sm.dig[w][cl * 48 + j * 6]);
+        dst[0] = u2{dg[0], dg[1]};
+        dst[1] = u2{dg[2], dg[3]};
+        dst[2] = u2{dg[4], dg[5]};
+        if (l < ROWS) *reinterpret_cast<u4 *>(&sm.scl[w][l * 8]) = sraw;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    unsigned D[48];
+#pragma unroll
+    for (int q = 0; q < 12; ++q) {
+        const u4 t = *reinterpret_cast<const u4 *>(&sm.dig[w][cl * 48 + 4 * q]);
+        D[4 * q] = t.x;
+        D[4 * q + 1] = t.y;
+        D[4 * q + 2] = t.z;
+        D[4 * q + 3] = t.w;
+    }
+
+    // ---- Steps: the chunk of row 8t + j.  Two chains, over the even and the
+    // odd columns, each walking the digits from the top one down and shifting
+    // by one digit in between (Horner's rule inside the chain):
+    //     a = ((acc_5 16 + acc_4) 16 + ...) 16 + acc_0.
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const unsigned sb = sm.scl[w][(8 * t + j) * 8 + cl];
+        int ev[4], od[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const unsigned wd = craw[t][q];
+            ev[q] = (int)(wd & 0x33333333u);
+            od[q] = (int)((wd >> 2) & 0x33333333u);
+        }
+        int ae = dot8_first(ev[0], (int)D[5]), ao = dot8_first(od[0], (int)D[6 + 5]);
+#pragma unroll
+        for (int d = 5; d >= 0; --d) {
+            if (d < 5) {
+                ae = (int)((unsigned)ae << 4);
+                ao = (int)((unsigned)ao << 4);
+            }
+#pragma unroll
+            for (int q = (d == 5 ? 1 : 0); q < 4; ++q) {
+                ae = __builtin_amdgcn_sdot8(ev[q], (int)D[12 * q + d], ae, false);
+                ao = __builtin_amdgcn_sdot8(od[q], (int)D[12 * q + 6 + d], ao, false);
+            }
+        }
+        const int z = (int)(((unsigned)(ae + ao) << 1) + neg3q);
+        sm.part[(8 * t + j) * PS + c] = __builtin_amdgcn_ldexpf(mul_half(sb, (float)z), kz);
+        if (NB == 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    const unsigned long long anybad = __builtin_amdgcn_ballot_w64(bad);
+    if (l == 0) sm.bad[w] = anybad != 0ull;
+    __syncthreads();
+    bool nan_out = false;
+#pragma unroll
+    for (int q = 0; q < WAVES; ++q) nan_out = nan_out || sm.bad[q] != 0;
+    float *__restrict__ y = ptrs.y[b] + row0;
+    for (int r = (int)threadIdx.x; r < ROWS; r += 64 * WAVES) {
+        if (row0 + r >= M) break;
+        const float sum = Flat<2>::template row_sum<CPR / 4>(sm.part + r * PS);
+        y[r] = nan_out ? __builtin_nanf("") : sum;
+    }
+}
+
+// The integer-dot kernel serves 2-bit rows of 8 to 48 chunks, a multiple of
+// 8 (K = 512, 1024, 1536, 2048, 3072), with 16-byte aligned code rows, scale
+// rows (lds a multiple of 8) and x, and byte offsets within 31 bits; 0 where
+// it does not apply, else the number of waves per workgroup.
+inline int idot_waves(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
+                      const uint16_t *const *S, int64_t lds, const float *const *x) {
+    if (K % 512 != 0 || K / 64 > FLAT_MAX_CPR || ldq % 16 != 0 || lds % 8 != 0) return 0;
+    if ((int64_t)M * ldq >= (int64_t(1) << 31) || (int64_t)M * lds * 2 >= (int64_t(1) << 31))
+        return 0;
+    for (int i = 0; i < count; ++i)
+        if (reinterpret_cast<uintptr_t>(Q[i]) % 16 != 0 ||
+            reinterpret_cast<uintptr_t>(S[i]) % 16 != 0 ||
+            reinterpret_cast<uintptr_t>(x[i]) % 16 != 0)
+            return 0;
+    return K / 512;
+}
+
+// Steps per workgroup: 8 in a batch (64 rows), IDOT_SINGLE_T for a single
+// product, which needs many workgroups to fill the chip.
+constexpr int IDOT_SINGLE_T = 1;
+
+template <int NB, int T = (NB == 1 ? IDOT_SINGLE_T : 8)>
+hipError_t launch_idot(int waves, int count, int M, const uint8_t *const *Q, int64_t ldq,
+                       const uint16_t *const *S, int64_t lds, const float *const *x,
+                       float *const *y, hipStream_t s) {
+    const dim3 grid((M + 8 * T - 1) / (8 * T), count);
+    PackedPtrs<NB> p;
+    for (int b = 0; b < NB; ++b) {
+        const int i = b < count ? b : 0;
+        p.Q[b] = Q[i];
+        p.S[b] = S[i];
+        p.x[b] = x[i];
+        p.y[b] = y[i];
+    }
+    switch (waves) {
+    case 1: return launch(gemv_q2_idot<1, T, NB>, grid, dim3(64), s, M, ldq, lds, p);
+    case 2: return launch(gemv_q2_idot<2, T, NB>, grid, dim3(128), s, M, ldq, lds, p);
+    case 3: return launch(gemv_q2_idot<3, T, NB>, grid, dim3(192), s, M, ldq, lds, p);
+    case 4: return launch(gemv_q2_idot<4, T, NB>, grid, dim3(256), s, M, ldq, lds, p);
+    default: return launch(gemv_q2_idot<6, T, NB>, grid, dim3(384), s, M, ldq, lds, p);
+    }
+}
+
 // Rows split 32 ways unless the rows are long and few: at K >= 6,144 (each
 // of 256 lanes then holds at least one live unit per pass in two of its
 // three slots) with fewer rows than 32-way groups of one product would need
@@ -697,6 +1005,10 @@ template <int BITS, int NB>
 hipError_t launch_split(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
                         const uint16_t *const *S, int64_t lds, const float *const *x,
                         float *const *y, hipStream_t s) {
+    if (BITS == 2 && NB > 1) {
+        const int waves = idot_waves(count, M, K, Q, ldq, S, lds, x);
+        if (waves) return launch_idot<NB>(waves, count, M, Q, ldq, S, lds, x, y, s);
+    }
     const int cpr = flat_cpr<BITS>(count, M, K, Q, ldq, lds, x);
     if (cpr) return launch_flat<BITS, NB>(count, M, cpr, Q, ldq, S, lds, x, y, s);
     return deep_split(M, K)

@@ -95,8 +95,16 @@ def test_single_and_batched(bits, M, K):
     for (Qb, Sb, xb), yb in (((Q1, S1, x1), ys[0]), ((Q2, S2, x2), ys[2])):
         rb, bb = _oracle(bits, Qb, Sb, xb)
         assert_close(yb, rb, bb, "%d-bit batched neighbour %dx%d" % (bits, M, K))
-    # the same arithmetic per row in both launches
-    assert np.array_equal(y, ys[1])
+    # 4-bit batches run the single call's arithmetic per row; 2-bit batches
+    # of these shapes may take the integer-dot kernel, so they are held to
+    # the tolerance above and to repeating their own bits
+    if bits == 4:
+        assert np.array_equal(y, ys[1])
+    else:
+        again = _batched(bits, [dev(Q1), dev(Q), dev(Q2)],
+                         [dev(S1.view(np.int16)), dev(S.view(np.int16)), dev(S2.view(np.int16))],
+                         [dev(x1), dev(x), dev(x2)])
+        assert np.array_equal(again[1], ys[1])
 
 
 @pytest.mark.parametrize("bits,K", [(2, 1536), (2, 512), (2, 3072), (4, 1536), (4, 256)])
@@ -173,7 +181,8 @@ def test_full_size_batch_of_forty(bits):
 def test_large_batches(bits, M, count):
     """Batches of 7 to 64 products, with a partial last workgroup at 5,000,
     777 and 3,001 rows: sampled products against the oracle, and the same
-    bits as single calls."""
+    bits as single calls (4-bit) or as a second launch of the batch (2-bit,
+    whose batches may take the integer-dot kernel)."""
     K = 1536
     rng = np.random.default_rng(7 * M + count)
     x = inputs.normal(rng, (K,))
@@ -182,10 +191,12 @@ def test_large_batches(bits, M, count):
     dQ = [dev(Q) for Q, _ in mats]
     dS = [dev(S.view(np.int16)) for _, S in mats]
     ys = _batched(bits, dQ, dS, [dx] * count)
+    again = _batched(bits, dQ, dS, [dx] * count) if bits == 2 else None
     for r in (0, count // 2, count - 1):
         ref, bound = _oracle(bits, *mats[r], x)
         assert_close(ys[r], ref, bound, "%d-bit batch product %d of %d, M=%d" % (bits, r, count, M))
-        assert np.array_equal(ys[r], _single(bits, dQ[r], dS[r], dx))
+        other = _single(bits, dQ[r], dS[r], dx) if bits == 4 else again[r]
+        assert np.array_equal(ys[r], other)
 
 
 @pytest.mark.parametrize("bits,K", [(2, 12288), (4, 6144)])

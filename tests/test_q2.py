@@ -143,18 +143,22 @@ def _rotation(n, M=12288, K=1536, start=0):
     return out
 
 
-def test_batched_equals_single_calls_bitwise():
+def test_batched_and_single_calls_agree():
+    """A batch and single calls on the same products both meet the tolerance
+    (they may run different kernels, so the header promises no more), and a
+    repeated batch gives the same bits."""
     mats = _rotation(5, 3000, 1536)
     x = inputs.q2_x()
     dQ = [dev(Q) for Q, _ in mats]
     dS = [dev(S.view(np.int16)) for _, S in mats]
     dx = dev(x)
     ys = bd.gemv_q2_batched(dQ, dS, [dx] * 5)
+    again = bd.gemv_q2_batched(dQ, dS, [dx] * 5)
     for b, (Q, S) in enumerate(mats):
-        single = host(bd.gemv_q2(dQ[b], dS[b], dx))
-        assert np.array_equal(host(ys[b]), single), b
         ref, bound = oracle.gemv_q2(Q, S, x)
+        assert_close(host(bd.gemv_q2(dQ[b], dS[b], dx)), ref, bound, "single %d" % b)
         assert_close(host(ys[b]), ref, bound, "batched %d" % b)
+        assert np.array_equal(host(ys[b]), host(again[b])), b
 
 
 def test_batched_more_than_one_launch_and_own_x():
