@@ -331,6 +331,73 @@ def _median_per_kernel(per):
     return {k: float(np.median(list(v.values()))) for k, v in per.items()}
 
 
+# Weights per dispatch of the GEMV kernels at the bench's shapes, for counts
+# per weight: (kernel-name prefix, whole name suffix, weights per dispatch).
+WEIGHTS_PER_DISPATCH = (
+    ("gemv_q2_idot<3,", ", 64>", CALLS_PER_TOKEN * Q2_M * Q2_K),
+    ("gemv_packed_flat<2, 1, 1,", "", Q2_M * Q2_K),
+    ("gemv_packed_flat<4, 2, 1,", "", Q2_M * Q2_K),
+    ("gemv_packed_flat<4, 8, 64,", "", CALLS_PER_TOKEN * Q2_M * Q2_K),
+    ("gemv_f32_kernel<1, 6, true>", "", Q2_M * Q2_K),
+)
+N_SIMD = 1024                      # 256 CUs x 4 SIMDs
+N_XCD = 8                          # GRBM_GUI_ACTIVE is summed over the 8 XCDs
+
+
+def summarize_counters(db_paths):
+    """Per kernel (and launch shape): the median per dispatch of every counter
+    found in the rocprofv3 --pmc databases, then derived figures: VALU
+    instructions per lane per weight (SQ_INSTS_VALU * 64 / weights), VALU
+    issue share 4 * SQ_ACTIVE_INST_VALU / (SIMDs * GRBM_GUI_ACTIVE / XCDs),
+    MFMA utilisation SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs * GRBM_GUI_ACTIVE /
+    XCDs), LDS bank-conflict cycles per LDS instruction and the L2 hit rate."""
+    import sqlite3
+    med = {}
+    for path in db_paths:
+        db = sqlite3.connect(path)
+        names = [r[0] for r in db.execute(
+            "select distinct counter_name from counters_collection").fetchall()]
+        db.close()
+        for c in names:
+            for k, v in _median_per_kernel(_counter_dispatches(path, c)).items():
+                med.setdefault(k, {})[c] = v
+    lines = []
+    counters = sorted({c for d in med.values() for c in d})
+    lines.append("| kernel | " + " | ".join(counters) + " |")
+    lines.append("|---" * (len(counters) + 1) + "|")
+    for k in sorted(med):
+        lines.append("| %s | " % k + " | ".join(
+            "%.0f" % med[k][c] if c in med[k] else "" for c in counters) + " |")
+    lines.append("")
+    lines.append("| kernel | VALU instr per lane per weight | VALU issue share | MFMA util | "
+                 "LDS conflict cycles per LDS instr | L2 hit rate |")
+    lines.append("|---|---|---|---|---|---|")
+    for k in sorted(med):
+        d = med[k]
+        base = k.split(" @")[0]
+        wts = [w for pre, suf, w in WEIGHTS_PER_DISPATCH
+               if base.startswith(pre) and base.endswith(suf)]
+        cyc = d.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD
+
+        def f(v, fmt):
+            return fmt % v if v is not None else ""
+        vpw = d["SQ_INSTS_VALU"] * 64.0 / wts[0] if wts and "SQ_INSTS_VALU" in d else None
+        busy = (4.0 * d["SQ_ACTIVE_INST_VALU"] / (N_SIMD * cyc)
+                if cyc and "SQ_ACTIVE_INST_VALU" in d else None)
+        mfma = (d["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * cyc)
+                if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in d else None)
+        lds = (d["SQ_LDS_BANK_CONFLICT"] / d["SQ_INSTS_LDS"]
+               if d.get("SQ_INSTS_LDS") and "SQ_LDS_BANK_CONFLICT" in d else None)
+        hits = (d["TCC_HIT_sum"] / (d["TCC_HIT_sum"] + d["TCC_MISS_sum"])
+                if "TCC_HIT_sum" in d and d.get("TCC_HIT_sum", 0) + d.get("TCC_MISS_sum", 0)
+                else None)
+        if any(v is not None for v in (vpw, busy, mfma, lds, hits)):
+            lines.append("| %s | %s | %s | %s | %s | %s |" % (
+                k, f(vpw, "%.3f"), f(busy, "%.2f"), f(mfma, "%.2f"), f(lds, "%.2f"),
+                f(hits, "%.3f")))
+    return "\n".join(lines)
+
+
 def write_traffic(fetch_db, write_db):
     """HBM bytes per launch of the GEMM and the 2-bit GEMV: FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch, median over dispatches), each scaled by
@@ -359,7 +426,7 @@ def write_traffic(fetch_db, write_db):
              "traffic_gemm_f32_2048.json", ("gemm_f32.hip",), 3 * 4 * GEMM_N * GEMM_N),
             (lambda n: n.startswith("gemv_packed_flat<2, 1, 1,"),
              "traffic_gemv_q2_12288x1536.json", q2_srcs, Q2_ALG_BYTES),
-            (lambda n: n.startswith("gemv_q2_idot<3, 8, 64>"),
+            (lambda n: n.startswith("gemv_q2_idot<3,") and n.split(" @")[0].endswith(", 64>"),
              "traffic_gemv_q2_batched_12288x1536.json", q2_srcs,
              CALLS_PER_TOKEN * Q2_ALG_BYTES),
             (lambda n: n.startswith("gemv_packed_flat<4, 2, 1,"),
@@ -403,6 +470,52 @@ def roofline(kernel, alg_bytes, us, traffic=None, note=None):
     return d
 
 
+def counters_run(torch, bd, inputs):
+    """Each kernel of the path on the bench's inputs, a few launches each,
+    eagerly, after one device-to-device copy of CALIBRATION_BYTES (the
+    reference that scales rocprofv3's byte counters): 5 GEMMs at 2048^3, 128
+    single 2-bit products and 4 batches of 40 over the 128-matrix set, the
+    same for 4-bit over its 64 matrices, and 48 fp32 GEMVs."""
+    dev = torch.device("cuda:0")
+    A, B = inputs.large_square(3)
+    dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+    dC = torch.empty((GEMM_N, GEMM_N), dtype=torch.float32, device=dev)
+    dx = torch.from_numpy(inputs.q2_x()).to(dev)
+
+    def packed_set(gen, n):
+        out = []
+        for r in range(n):
+            Q, S = gen(r)
+            out.append((torch.from_numpy(Q).to(dev), torch.from_numpy(S.view(np.int16)).to(dev)))
+        return out
+    q2, q4 = packed_set(inputs.q2_weight, Q2_ROTATION), packed_set(inputs.q4_weight, Q4_ROTATION)
+    Wf = [torch.from_numpy(inputs.gemv_f32_weight(r)).to(dev) for r in range(F32_ROTATION)]
+    dxf = torch.from_numpy(inputs.gemv_f32_x()).to(dev)
+    dy = torch.empty(Q2_M, dtype=torch.float32, device=dev)
+    dys = [torch.empty(Q2_M, dtype=torch.float32, device=dev) for _ in range(CALLS_PER_TOKEN)]
+    src = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    for _ in range(5):
+        bd.gemm_f32(dA, dB, C=dC)
+    for pset, rot, single, batched in ((q2, Q2_ROTATION, bd.gemv_q2, bd.gemv_q2_batched),
+                                       (q4, Q4_ROTATION, bd.gemv_q4, bd.gemv_q4_batched)):
+        for Q, S in pset:
+            single(Q, S, dx, y=dy)
+        for t in range(4):
+            idx = [(t * CALLS_PER_TOKEN + c) % rot for c in range(CALLS_PER_TOKEN)]
+            batched([pset[i][0] for i in idx], [pset[i][1] for i in idx],
+                    [dx] * CALLS_PER_TOKEN, ys=dys)
+    for W in Wf:
+        bd.gemv_f32(W, dxf, y=dy)
+    torch.cuda.synchronize()
+    log("counters run done")
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -412,9 +525,16 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="also run one device-to-device copy of BYTES before "
                          "timing, the reference for rocprofv3 byte counters")
+    ap.add_argument("--counters-run", action="store_true",
+                    help="only launch each kernel of the path a few times on the bench's "
+                         "inputs (for rocprofv3 --pmc passes, which serialise dispatches), "
+                         "with the calibration copy, and exit")
     ap.add_argument("--summarize-trace", metavar="RESULTS_DB",
                     help="print the per-kernel summary of a rocprofv3 "
                          "--kernel-trace --stats database and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DB",
+                    help="print per-kernel medians of the counters in rocprofv3 --pmc "
+                         "databases, with derived figures, and exit")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="turn two rocprofv3 --pmc databases (FETCH_SIZE, "
                          "WRITE_SIZE) of a run made with --copy-calibration "
@@ -422,6 +542,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
+        return 0
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters))
         return 0
     if args.traffic:
         return write_traffic(*args.traffic)
@@ -438,6 +561,8 @@ def main():
     from gemv_gemm_f32_amd import inputs
 
     bd.load()
+    if args.counters_run:
+        return counters_run(torch, bd, inputs)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     prop = torch.cuda.get_device_properties(dev)

@@ -10,7 +10,11 @@
 // a packed 4-bit path; the 4-bit product here uses the same kernel with
 // wider codes.  That page's kernel unpacked the fields with floating-point
 // floor arithmetic and reduced through shared memory with barriers (section
-// "The kernel"); this one is shaped for CDNA4:
+// "The kernel"); these are shaped for CDNA4.  Three kernels live here: the
+// row-split kernel described first (any shape), the flat split (rows of 8 to
+// 48 chunks of 16 bytes; single products and 4-bit batches), which share the
+// multiply-add unpack below, and the integer-dot kernel for batches of 2-bit
+// products on the configurations' shapes, described at its definition.
 //
 //  * Units: a row is read in units of 16 codes -- 4 bytes of 2-bit codes or
 //    8 bytes of 4-bit codes -- and 4 units make one 64-column scale group.
@@ -768,13 +772,72 @@ __device__ __forceinline__ unsigned nib_swap(unsigned a, unsigned b, bool hi) {
               : ((a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u));
 }
 
+// Code chunks in flight per lane: the first IDOT_NBUF steps' chunks are
+// issued up front, the rest one by one as steps finish with their slots.
+constexpr int IDOT_NBUF = 8;
+
+// The integer-dot kernel's buffer loads: resources that start at the
+// workgroup's first row and end at the matrix's last byte, so rows past M
+// read zeros (they are never stored).
+struct IdotLoads {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __amdgpu_buffer_rsrc_t rq, rs;
+#endif
+    unsigned vq, sq, vs, ss;
+
+    __device__ __forceinline__ void init(const uint8_t *Q, const uint16_t *S, int M, int row0,
+                                         int cpr, int64_t ldq, int64_t lds, int w, int l, int j,
+                                         int c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        const int rows_left = M - row0;       // >= 1
+        rq = __builtin_amdgcn_make_buffer_rsrc((void *)(Q + (int64_t)row0 * ldq), (short)0,
+                                               (int)((int64_t)(rows_left - 1) * ldq + 16 * cpr),
+                                               0x00020000);
+        rs = __builtin_amdgcn_make_buffer_rsrc((void *)(S + (int64_t)row0 * lds), (short)0,
+                                               (int)(((int64_t)(rows_left - 1) * lds + cpr) * 2),
+                                               0x00020000);
+#endif
+        vq = (unsigned)j * (unsigned)ldq + 16u * (unsigned)c;   // row j of step 0, chunk c
+        sq = 8u * (unsigned)ldq;                                // 8 rows per step
+        vs = (unsigned)l * (unsigned)lds * 2u + 16u * (unsigned)w;  // row l, this wave's 8 scales
+        ss = 64u * (unsigned)lds * 2u;                          // 64 rows per scale load
+    }
+    // Step t's 16-byte code chunk (non-temporal: each byte is read once).
+    __device__ __forceinline__ void codes(int t, unsigned (&cw)[4]) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+        const u4 v = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(vq + (unsigned)t * sq), 0, NT);
+        cw[0] = v.x;
+        cw[1] = v.y;
+        cw[2] = v.z;
+        cw[3] = v.w;
+#else
+        cw[0] = cw[1] = cw[2] = cw[3] = (unsigned)t * 0u;
+#endif
+    }
+    // The 8 scales of this wave's chunks in row r of the workgroup (16 bytes);
+    // r < 0 reads from past the resource, which gives zeros.
+    __device__ __forceinline__ u4 scales(int r) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+        const int off = r < 0 ? 0x7FFFFFF0 : (int)(vs + (unsigned)(r >> 6) * ss);
+        return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+#else
+        return u4{0u, 0u, 0u, (unsigned)r * 0u};
+#endif
+    }
+};
+
 // WAVES waves per workgroup (the row has 8 * WAVES chunks), T steps of 8
 // rows, NB products per pointer block.
+constexpr int IDOT_WAVES_PER_SIMD = 4;   // occupancy asked for in a batch
+
 template <int WAVES, int T, int NB>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 1 : 4)))
+__global__ __launch_bounds__(64 * WAVES)
+__attribute__((amdgpu_waves_per_eu(NB == 1 ? 1 : IDOT_WAVES_PER_SIMD)))
 void gemv_q2_idot(int M, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
     using Sm = IdotSmem<WAVES, T>;
     constexpr int CPR = Sm::CPR, ROWS = Sm::ROWS, PS = Sm::PS;
+    constexpr int NBUF = T < IDOT_NBUF ? T : IDOT_NBUF;   // code chunks in flight per lane
+    constexpr int SL = (ROWS + 63) / 64;                   // 16-byte scale loads per lane
     __shared__ __attribute__((aligned(16))) Sm sm;
 
     const int b = NB == 1 ? 0 : (int)blockIdx.y;
@@ -784,8 +847,9 @@ void gemv_q2_idot(int M, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
     const int row0 = (int)blockIdx.x * ROWS;
 
     // ---- Loads, in the order they are needed (vector-memory loads retire in
-    // issue order): the unit's 16 x values, the 16-byte scale block, then
-    // every code chunk of the T steps.
+    // issue order): the unit's 16 x values, the 16-byte scale blocks, then
+    // the code chunks of the first NBUF steps; each later step's chunk is
+    // issued as soon as a slot frees up.
     v4f xr[4];
     {
         const v4f *xp = reinterpret_cast<const v4f *>(ptrs.x[b] + 64 * c + 16 * u);
@@ -793,38 +857,16 @@ void gemv_q2_idot(int M, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
         for (int q = 0; q < 4; ++q) xr[q] = xp[q];
     }
     __builtin_amdgcn_sched_barrier(0);
-    u4 sraw;
-    unsigned craw[T][4];
-#if defined(__HIP_DEVICE_COMPILE__)
-    {
-        const int rows_left = M - row0;       // >= 1
-        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(ptrs.Q[b] + (int64_t)row0 * ldq), (short)0,
-            (int)((int64_t)(rows_left - 1) * ldq + 16 * CPR), 0x00020000);
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(ptrs.S[b] + (int64_t)row0 * lds), (short)0,
-            (int)(((int64_t)(rows_left - 1) * lds + CPR) * 2), 0x00020000);
-        // lanes past the workgroup's rows load from past the resource: zeros
-        const int soff = l < ROWS ? (int)((unsigned)l * (unsigned)lds * 2u + 16u * (unsigned)w)
-                                  : 0x7FFFFFF0;
-        sraw = __builtin_amdgcn_raw_buffer_load_b128(rs, soff, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        const unsigned vq = (unsigned)j * (unsigned)ldq + 16u * (unsigned)c;
-        const unsigned sq = 8u * (unsigned)ldq;
+    IdotLoads ld;
+    ld.init(ptrs.Q[b], ptrs.S[b], M, row0, CPR, ldq, lds, w, l, j, c);
+    u4 sraw[SL];
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const u4 v = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(vq + t * sq), 0, NT);
-            craw[t][0] = v.x;
-            craw[t][1] = v.y;
-            craw[t][2] = v.z;
-            craw[t][3] = v.w;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-#else
-    sraw = u4{0u, 0u, 0u, 0u};
-    for (int t = 0; t < T; ++t) craw[t][0] = craw[t][1] = craw[t][2] = craw[t][3] = 0u;
-#endif
+    for (int q = 0; q < SL; ++q) sraw[q] = ld.scales(64 * q + l < ROWS ? 64 * q + l : -1);
+    __builtin_amdgcn_sched_barrier(0);
+    unsigned craw[NBUF][4];
+#pragma unroll
+    for (int t = 0; t < NBUF; ++t) ld.codes(t, craw[t]);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- Set-up: this lane's 8 columns of the chunk as digit words.
     float v[16];
@@ -843,15 +885,29 @@ void gemv_q2_idot(int M, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
     mx = __builtin_fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute((l ^ 32) << 2,
                                                                           __float_as_int(mx))));
     const int E = __builtin_amdgcn_frexp_expf(mx);   // max |x| < 2^E; 0 for 0 and non-finite
+    float xv[8];
+    float ax = 0.f;   // sum of |x| over this lane's 8 columns, then over the chunk
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        // the odd or even column, by a bit select (not an indexed load)
+        xv[m] = __uint_as_float((__float_as_uint(v[2 * m + 1]) & odd) |
+                                (__float_as_uint(v[2 * m]) & ~odd));
+        ax += __builtin_fabsf(xv[m]);
+    }
+    ax += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ax), 0x128, 0xF, 0xF,
+                                                     false));   // row_ror:8, lane l ^ 8
+    ax += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(ax), 0x401F));
+    ax += __int_as_float(__builtin_amdgcn_ds_bpermute((l ^ 32) << 2, __float_as_int(ax)));
+    // Five digits (|q| <= 2^18) suffice for a chunk with sum |x| >= 2^(E+3);
+    // the wave takes six if any of its 8 chunks needs them.
+    const bool six = __builtin_amdgcn_ballot_w64(!(ax >= __builtin_amdgcn_ldexpf(1.f, E + 3))) != 0ull;
+    const int k = (six ? 22 : 18) - E;
     unsigned uq[8];
     int qs = 0;
     unsigned orr = 0;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-        // the odd or even column, by a bit select (not an indexed load)
-        const float xv = __uint_as_float((__float_as_uint(v[2 * m + 1]) & odd) |
-                                         (__float_as_uint(v[2 * m]) & ~odd));
-        const float t = __builtin_amdgcn_ldexpf(xv, 22 - E) + 12582912.f;   // + 1.5 * 2^23
+        const float t = __builtin_amdgcn_ldexpf(xv[m], k) + 12582912.f;   // + 1.5 * 2^23
         uq[m] = __float_as_uint(t) - 0x4AB77778u;      // q + 0x888888
         orr |= uq[m];
         qs += (int)uq[m];
@@ -863,7 +919,7 @@ void gemv_q2_idot(int M, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
     qs += __builtin_amdgcn_ds_swizzle(qs, 0x401F);
     qs += __builtin_amdgcn_ds_bpermute((l ^ 32) << 2, qs);
     const unsigned neg3q = (unsigned)(-3 * qs);
-    const int kz = E - 23;
+    const int kz = -k - 1;                             // Z counts halves of 2^-k
     // transpose the 8 x 8 nibbles (digits 6, 7 are zero and dropped): halves,
     // then bytes, then nibbles
 #pragma unroll
@@ -892,7 +948,9 @@ void gemv_q2_idot(int M, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
         dst[0] = u2{dg[0], dg[1]};
         dst[1] = u2{dg[2], dg[3]};
         dst[2] = u2{dg[4], dg[5]};
-        if (l < ROWS) *reinterpret_cast<u4 *>(&sm.scl[w][l * 8]) = sraw;
+#pragma unroll
+        for (int q = 0; q < SL; ++q)
+            if (64 * q + l < ROWS) *reinterpret_cast<u4 *>(&sm.scl[w][(64 * q + l) * 8]) = sraw[q];
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -910,26 +968,51 @@ void gemv_q2_idot(int M, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
     // ---- Steps: the chunk of row 8t + j.  Two chains, over the even and the
     // odd columns, each walking the digits from the top one down and shifting
     // by one digit in between (Horner's rule inside the chain):
-    //     a = ((acc_5 16 + acc_4) 16 + ...) 16 + acc_0.
+    //     a = ((acc_top 16 + ...) 16 + acc_1) 16 + acc_0,
+    // from digit 5 when the wave takes six digits, else from digit 4 (the
+    // branch is uniform over the wave).
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const unsigned sb = sm.scl[w][(8 * t + j) * 8 + cl];
         int ev[4], od[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const unsigned wd = craw[t][q];
+            const unsigned wd = craw[t % NBUF][q];
             ev[q] = (int)(wd & 0x33333333u);
             od[q] = (int)((wd >> 2) & 0x33333333u);
         }
-        int ae = dot8_first(ev[0], (int)D[5]), ao = dot8_first(od[0], (int)D[6 + 5]);
+        if (t + NBUF < T) ld.codes(t + NBUF, craw[t % NBUF]);
+        int ae, ao;
+        if (six) {
+            ae = dot8_first(ev[0], (int)D[5]);
+            ao = dot8_first(od[0], (int)D[6 + 5]);
 #pragma unroll
-        for (int d = 5; d >= 0; --d) {
-            if (d < 5) {
-                ae = (int)((unsigned)ae << 4);
-                ao = (int)((unsigned)ao << 4);
+            for (int q = 1; q < 4; ++q) {
+                ae = __builtin_amdgcn_sdot8(ev[q], (int)D[12 * q + 5], ae, false);
+                ao = __builtin_amdgcn_sdot8(od[q], (int)D[12 * q + 6 + 5], ao, false);
             }
+            ae = (int)((unsigned)ae << 4);
+            ao = (int)((unsigned)ao << 4);
 #pragma unroll
-            for (int q = (d == 5 ? 1 : 0); q < 4; ++q) {
+            for (int q = 0; q < 4; ++q) {
+                ae = __builtin_amdgcn_sdot8(ev[q], (int)D[12 * q + 4], ae, false);
+                ao = __builtin_amdgcn_sdot8(od[q], (int)D[12 * q + 6 + 4], ao, false);
+            }
+        } else {
+            ae = dot8_first(ev[0], (int)D[4]);
+            ao = dot8_first(od[0], (int)D[6 + 4]);
+#pragma unroll
+            for (int q = 1; q < 4; ++q) {
+                ae = __builtin_amdgcn_sdot8(ev[q], (int)D[12 * q + 4], ae, false);
+                ao = __builtin_amdgcn_sdot8(od[q], (int)D[12 * q + 6 + 4], ao, false);
+            }
+        }
+#pragma unroll
+        for (int d = 3; d >= 0; --d) {
+            ae = (int)((unsigned)ae << 4);
+            ao = (int)((unsigned)ao << 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
                 ae = __builtin_amdgcn_sdot8(ev[q], (int)D[12 * q + d], ae, false);
                 ao = __builtin_amdgcn_sdot8(od[q], (int)D[12 * q + 6 + d], ao, false);
             }
@@ -969,11 +1052,12 @@ inline int idot_waves(int count, int M, int K, const uint8_t *const *Q, int64_t 
     return K / 512;
 }
 
-// Steps per workgroup: 8 in a batch (64 rows), IDOT_SINGLE_T for a single
+// Steps per workgroup: IDOT_BATCH_T in a batch, IDOT_SINGLE_T for a single
 // product, which needs many workgroups to fill the chip.
 constexpr int IDOT_SINGLE_T = 1;
+constexpr int IDOT_BATCH_T = 16;
 
-template <int NB, int T = (NB == 1 ? IDOT_SINGLE_T : 8)>
+template <int NB, int T = (NB == 1 ? IDOT_SINGLE_T : IDOT_BATCH_T)>
 hipError_t launch_idot(int waves, int count, int M, const uint8_t *const *Q, int64_t ldq,
                        const uint16_t *const *S, int64_t lds, const float *const *x,
                        float *const *y, hipStream_t s) {
@@ -1005,7 +1089,7 @@ template <int BITS, int NB>
 hipError_t launch_split(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
                         const uint16_t *const *S, int64_t lds, const float *const *x,
                         float *const *y, hipStream_t s) {
-    if (BITS == 2 && NB > 1) {
+    if constexpr (BITS == 2 && NB > 1) {
         const int waves = idot_waves(count, M, K, Q, ldq, S, lds, x);
         if (waves) return launch_idot<NB>(waves, count, M, Q, ldq, S, lds, x, y, s);
     }

@@ -31,15 +31,17 @@
  *    later one is rejected the earlier ones stay queued.)
  *  - Results are reproducible bit for bit from run to run on the same shapes
  *    (fixed reduction trees, no floating-point atomics).  They agree with the
- *    exact sum to |c - c_exact| <= 1e-4 * sum_k |a_ik * b_kj| per element on
- *    the supported workloads with finite inputs; fp32 operands are used as
- *    IEEE fp32 (no reduced precision inputs).
+ *    exact sum to |c - c_exact| <= 1e-4 * sum_k |a_ik * b_kj| per element for
+ *    finite inputs whose partial sums stay in the normal fp32 range (for the
+ *    packed products: the largest |x_k| in [2^-100, 2^100]; see there); fp32
+ *    operands are used as IEEE fp32 (no reduced-precision inputs).
  *  - Non-finite inputs: the fp32 products follow IEEE arithmetic, so a NaN
  *    operand makes exactly the outputs whose sums contain it NaN, and an
  *    infinity gives +-inf there (NaN where it meets a zero or an opposite
- *    infinity).  The packed products apply the zero point through the sum of
- *    x, so a NaN or an infinity anywhere in x makes every output NaN, and a
- *    NaN scale makes its own row NaN.
+ *    infinity).  The packed products do not: they apply the zero point
+ *    through sums of x (or round x to integers), so a NaN or an infinity
+ *    anywhere in x makes EVERY output NaN, where the exact sum would give
+ *    +-inf in rows that meet an infinity; a NaN scale makes its own row NaN.
  *  - Thread safety: the only global state is a per-device property cache
  *    filled once; every entry point may be called from several threads.
  */
@@ -154,6 +156,11 @@ int gemv_f32(int64_t M, int64_t K, const float *W, int64_t ldw,
  *   Q: ldq >= ceil(K/4) bytes per row;  S: lds >= ceil(K/64) halves per row,
  *   holding IEEE binary16 bit patterns;  x (fp32) and y (fp32) contiguous.
  * Bits of Q for columns k >= K and scales past ceil(K/64) are never used.
+ * Accuracy: |y_i - exact| <= 1e-4 * sum_k |w(i,k) x_k| for finite x whose
+ * largest |x_k| lies in [2^-100, 2^100] and finite scales whose products
+ * with x keep y finite; entries of x far below the largest may underflow in
+ * partial products, which moves y by far less than the bound.  Any NaN or
+ * infinity in x makes every y NaN; a NaN scale makes its own row NaN.
  */
 int gemv_q2(int64_t M, int64_t K, const uint8_t *Q, int64_t ldq,
             const uint16_t *S, int64_t lds,
@@ -172,10 +179,11 @@ int gemv_q2(int64_t M, int64_t K, const uint8_t *Q, int64_t ldq,
  *   (else GG_ERR_ALIAS); inputs may be shared (for example one x for all).
  *   Products 64 at a time share a launch, in order; GG_ERR_LAUNCH from a
  *   batch of more than 64 may leave the products of earlier launches queued.
- * A batch runs the same arithmetic per product as gemv_q2, with more rows
- * per thread; results meet the same tolerance and are reproducible run to
- * run, but a batch may sum in a different order from a gemv_q2 call and so
- * need not match it bit for bit.
+ * A batch meets gemv_q2's accuracy and non-finite behaviour and is
+ * reproducible run to run, but it may take a different kernel from a gemv_q2
+ * call (on the configurations' shapes it rounds x to 24-bit integers per 64
+ * columns and multiplies with integer dot products), so the two need not
+ * agree bit for bit.
  */
 int gemv_q2_batched(int64_t count, int64_t M, int64_t K,
                     const uint8_t *const *Q, int64_t ldq,
@@ -197,7 +205,8 @@ int gemv_q2_batched(int64_t count, int64_t M, int64_t K,
  *   Q: ldq >= ceil(K/2) bytes per row;  S: lds >= ceil(K/64) halves per row;
  *   x (fp32) and y (fp32) contiguous.
  * Bits of Q for columns k >= K and scales past ceil(K/64) are never used.
- * A non-uniform codebook such as NF4 is not this format.
+ * A non-uniform codebook such as NF4 is not this format.  Accuracy and
+ * non-finite inputs as for gemv_q2.
  */
 int gemv_q4(int64_t M, int64_t K, const uint8_t *Q, int64_t ldq,
             const uint16_t *S, int64_t lds,

@@ -160,3 +160,31 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_summarize_counters(bench, tmp_path):
+    """Medians per dispatch and the derived figures of a 40-product 2-bit
+    batch: VALU instructions per lane per weight, issue share, L2 hit rate."""
+    p = str(tmp_path / "c.db")
+    name = ("void gg::(anonymous namespace)::gemv_q2_idot<3, 16, 64>(int, long, long, "
+            "gg::(anonymous namespace)::PackedPtrs<64>)")
+    vals = {"SQ_INSTS_VALU": 14.5e6, "SQ_ACTIVE_INST_VALU": 14.5e6, "GRBM_GUI_ACTIVE": 8.0e5,
+            "SQ_INSTS_LDS": 7.0e5, "SQ_LDS_BANK_CONFLICT": 1.4e6, "TCC_HIT_sum": 1.0e5,
+            "TCC_MISS_sum": 9.0e5}
+    rows = []
+    for disp, f in ((1, 1.0), (2, 1.1), (3, 0.9)):
+        rows += [(name, disp, c, v * f, 3840 * 192, 192) for c, v in vals.items()]
+    _counter_db_shapes(p, "unused", [])
+    db = sqlite3.connect(p)
+    db.executemany("insert into counters_collection values (?, ?, ?, ?, ?, ?)", rows)
+    db.commit()
+    db.close()
+    out = bench.summarize_counters([p])
+    derived = [l for l in out.splitlines() if l.startswith("| gemv_q2_idot") and
+               l.count("|") == 7][0]
+    cells = [c.strip() for c in derived.strip("|").split("|")]
+    weights = 40 * 12288 * 1536
+    assert float(cells[1]) == pytest.approx(14.5e6 * 64 / weights, abs=1e-3)
+    assert float(cells[2]) == pytest.approx(4 * 14.5e6 / (1024 * 8.0e5 / 8), abs=0.01)
+    assert float(cells[4]) == pytest.approx(2.0, abs=0.01)
+    assert float(cells[5]) == pytest.approx(0.1, abs=1e-3)
