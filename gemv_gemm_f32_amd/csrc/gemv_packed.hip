@@ -700,11 +700,15 @@ hipError_t launch_chunk(int count, int M, int K, const uint8_t *const *Q, int64_
 //
 //  * x as integers.  Per 64-column chunk (one scale group) let E be the
 //    exponent of the chunk's largest |x| (max |x| < 2^E) and
-//    q_k = rint(x_k 2^(22-E)), so |q_k| <= 2^22 and |x_k - q_k 2^(E-22)| <=
-//    2^(E-23).  q + 0x888888 has six nibbles d_i + 8 with
-//    q = sum_i d_i 16^i and d_i in [-8, 7]; flipping bit 3 of each nibble
-//    gives d_i as a signed nibble.  The rounding to an integer is done by the
-//    fp32 add of 1.5 * 2^23, whose bit pattern then holds q + 2^22.
+//    q_k = rint(x_k 2^k) with k = 22 - E, so |q_k| <= 2^22 and
+//    |x_k - q_k 2^-k| <= 2^(-k-1).  q + 0x888888 has six nibbles d_i + 8
+//    with q = sum_i d_i 16^i and d_i in [-8, 7]; flipping bit 3 of each
+//    nibble gives d_i as a signed nibble.  The rounding to an integer is done
+//    by the fp32 add of 1.5 * 2^23, whose bit pattern then holds q + 2^22.
+//  * Five digits where they suffice.  A chunk whose sum of |x| is at least
+//    2^(E+3) takes k = 18 - E (|q| <= 2^18, top digit zero); the wave takes
+//    six digits if any of its 8 chunks needs them, so the branch is uniform
+//    over the wave.
 //  * Lanes.  A wave reads 8 chunks of 8 rows per step: lane l takes chunk
 //    8 * wave + (l & 7) of row l >> 3, so each load instruction covers eight
 //    128-byte segments, and the 8 lanes that share a chunk sit in one wave.
@@ -713,23 +717,26 @@ hipError_t launch_chunk(int count, int M, int K, const uint8_t *const *Q, int64_
 //    they quantise their 8 columns and transpose the 8 x 6 nibbles into six
 //    digit words (word i holds digit i of the 8 columns), and swap them
 //    through LDS inside the wave, so every lane holds the 48 digit words of
-//    its chunk.  The chunk's maximum and sum of q meet by lane shuffles.
+//    its chunk.  The chunk's maximum, sum of |x| and sum of q meet by lane
+//    shuffles.
 //  * Steps.  For a code word w, w & 0x33333333 holds the codes of its even
 //    columns in nibbles 0..7 and (w >> 2) & 0x33333333 those of its odd
-//    columns.  Twelve v_dot8_i32_i4 per word (one chain per digit) give
-//    acc_i = sum c d_i over the chunk, exactly; then
-//        T = sum_i acc_i 16^i = sum_k c_k q_k            (|T| < 2^30),
+//    columns.  One chain of v_dot8_i32_i4 walks the digits from the top one
+//    down, shifting by one digit in between, and gives, exactly,
+//        T = sum_i 16^i sum_k c_k d_ik = sum_k c_k q_k    (|T| < 2^30),
 //        Z = 2 T - 3 sum_k q_k = 2 sum_k (c_k - 3/2) q_k   (|Z| < 2^31),
-//    both exact in int32, and the chunk's share of the row is
-//    s 2^(E-23) Z.  That is 15 instructions per 16 weights and 9 per chunk.
+//    both in int32, and the chunk's share of the row is s 2^(-k-1) Z.  Per
+//    16 weights: 10 or 12 dot products and 3 bit operations, against 25
+//    instructions for the multiply-add unpack.
 //  * Rounding.  Only x is rounded.  Over a chunk that moves the sum by at
-//    most 64 * (3/2) s 2^(E-23), while the chunk's share of the bound is
-//    sum |w x| >= (s/2) max |x| >= s 2^(E-2): at most 48 * 2^-20 = 4.6e-5 of
-//    it.  Converting Z to fp32, the scale product and the row's sum over
-//    chunks add at most (3 + chunks) * 3 * 2^-24 of it: below 1e-5 for up to
-//    48 chunks.  This holds for every finite x and s for which no partial
-//    sum overflows or falls below the normal range (s 2^(E-23) |Z| above
-//    2^-126 wherever it is not zero).
+//    most 64 * (3/2) s 2^(-k-1), while the chunk's share of the bound is
+//    sum |w x| >= (s/2) sum |x|: at most 96 2^-k / sum |x|, which is
+//    96 2^(E-22) / 2^(E-1) = 4.6e-5 with six digits (sum |x| >= max |x|) and
+//    96 2^(E-18) / 2^(E+3) = 4.6e-5 with five.  Converting Z to fp32, the
+//    scale product and the row's sum over chunks add at most
+//    (3 + chunks) * 3 * 2^-24 of it: below 1e-5 for up to 48 chunks.  This
+//    holds for every finite x and s for which no partial result overflows or
+//    falls below the normal range.
 //  * Non-finite x.  A NaN or an infinity in x makes every output NaN (its
 //    chunk's quantised values leave the 24-bit range, which the set-up
 //    detects); a non-finite scale makes its own row non-finite.
@@ -965,12 +972,13 @@ void gemv_q2_idot(int M, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
         D[4 * q + 3] = t.w;
     }
 
-    // ---- Steps: the chunk of row 8t + j.  Two chains, over the even and the
-    // odd columns, each walking the digits from the top one down and shifting
-    // by one digit in between (Horner's rule inside the chain):
+    // ---- Steps: the chunk of row 8t + j.  One chain over the even and the odd
+    // columns walks the digits from the top one down, shifting by one digit
+    // in between (Horner's rule inside the chain):
     //     a = ((acc_top 16 + ...) 16 + acc_1) 16 + acc_0,
     // from digit 5 when the wave takes six digits, else from digit 4 (the
-    // branch is uniform over the wave).
+    // branch is uniform over the wave).  Integer sums are exact, so the
+    // order of the dot products does not change the result.
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const unsigned sb = sm.scl[w][(8 * t + j) * 8 + cl];
@@ -982,42 +990,40 @@ void gemv_q2_idot(int M, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
             od[q] = (int)((wd >> 2) & 0x33333333u);
         }
         if (t + NBUF < T) ld.codes(t + NBUF, craw[t % NBUF]);
-        int ae, ao;
+        int a;
         if (six) {
-            ae = dot8_first(ev[0], (int)D[5]);
-            ao = dot8_first(od[0], (int)D[6 + 5]);
+            a = dot8_first(ev[0], (int)D[5]);
+            a = __builtin_amdgcn_sdot8(od[0], (int)D[6 + 5], a, false);
 #pragma unroll
             for (int q = 1; q < 4; ++q) {
-                ae = __builtin_amdgcn_sdot8(ev[q], (int)D[12 * q + 5], ae, false);
-                ao = __builtin_amdgcn_sdot8(od[q], (int)D[12 * q + 6 + 5], ao, false);
+                a = __builtin_amdgcn_sdot8(ev[q], (int)D[12 * q + 5], a, false);
+                a = __builtin_amdgcn_sdot8(od[q], (int)D[12 * q + 6 + 5], a, false);
             }
-            ae = (int)((unsigned)ae << 4);
-            ao = (int)((unsigned)ao << 4);
+            a = (int)((unsigned)a << 4);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                ae = __builtin_amdgcn_sdot8(ev[q], (int)D[12 * q + 4], ae, false);
-                ao = __builtin_amdgcn_sdot8(od[q], (int)D[12 * q + 6 + 4], ao, false);
+                a = __builtin_amdgcn_sdot8(ev[q], (int)D[12 * q + 4], a, false);
+                a = __builtin_amdgcn_sdot8(od[q], (int)D[12 * q + 6 + 4], a, false);
             }
         } else {
-            ae = dot8_first(ev[0], (int)D[4]);
-            ao = dot8_first(od[0], (int)D[6 + 4]);
+            a = dot8_first(ev[0], (int)D[4]);
+            a = __builtin_amdgcn_sdot8(od[0], (int)D[6 + 4], a, false);
 #pragma unroll
             for (int q = 1; q < 4; ++q) {
-                ae = __builtin_amdgcn_sdot8(ev[q], (int)D[12 * q + 4], ae, false);
-                ao = __builtin_amdgcn_sdot8(od[q], (int)D[12 * q + 6 + 4], ao, false);
+                a = __builtin_amdgcn_sdot8(ev[q], (int)D[12 * q + 4], a, false);
+                a = __builtin_amdgcn_sdot8(od[q], (int)D[12 * q + 6 + 4], a, false);
             }
         }
 #pragma unroll
         for (int d = 3; d >= 0; --d) {
-            ae = (int)((unsigned)ae << 4);
-            ao = (int)((unsigned)ao << 4);
+            a = (int)((unsigned)a << 4);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                ae = __builtin_amdgcn_sdot8(ev[q], (int)D[12 * q + d], ae, false);
-                ao = __builtin_amdgcn_sdot8(od[q], (int)D[12 * q + 6 + d], ao, false);
+                a = __builtin_amdgcn_sdot8(ev[q], (int)D[12 * q + d], a, false);
+                a = __builtin_amdgcn_sdot8(od[q], (int)D[12 * q + 6 + d], a, false);
             }
         }
-        const int z = (int)(((unsigned)(ae + ao) << 1) + neg3q);
+        const int z = (int)(((unsigned)a << 1) + neg3q);
         sm.part[(8 * t + j) * PS + c] = __builtin_amdgcn_ldexpf(mul_half(sb, (float)z), kz);
         if (NB == 1) __builtin_amdgcn_sched_barrier(0);
     }
