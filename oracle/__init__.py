@@ -56,9 +56,26 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+def build_sanitized(path: str) -> str:
+    """Compile oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer
+    (any finding aborts) into `path`, for the sanitizer test; load it by
+    setting ORACLE_LIB=path in a process that preloads the gcc sanitizer
+    runtimes."""
+    subprocess.check_call(["gcc", "-O1", "-g", "-std=c11", "-fPIC", "-shared",
+                           "-fno-fast-math", "-ffp-contract=off",
+                           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                           "-fno-omit-frame-pointer", _SRC, "-o", path, "-lm"])
+    return path
+
+
 def _load():
     global _lib
     if _lib is not None:
+        return _lib
+    alt = os.environ.get("ORACLE_LIB")
+    if alt:
+        # another build of oracle.c (the sanitizer test's), used as is
+        _lib = bind(ctypes.CDLL(alt))
         return _lib
     if not os.path.exists(_LIB_PATH) or (
             os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
