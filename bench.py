@@ -258,6 +258,77 @@ def gemm_configs(torch, bd, inputs, oracle, dev, capture, window):
     return out, all_ok
 
 
+PROBE_LIB = os.path.join(ROOT, "libbench_probes.so")
+PROBE_SHAPES = ((1, 64), (512, 576))     # the 2-bit GEMV's single call: 512 x 576 lanes
+PROBE_CHAINS = (("l2_1mib", 1 << 20, 100000), ("infinity_cache_64mib", 64 << 20, 100000),
+                ("hbm_4gib", 4 << 30, 20000))
+
+
+def probe_context(torch, dev, stream, capture, window):
+    """Physics reference points from bench_probes.hip: the per-launch floor of
+    an empty kernel (back to back in one graph, at the single call's launch
+    shape and at one wave), and the load-to-use latency of one lane chasing
+    random 256-byte-spaced links through 1 MiB (L2), 64 MiB (Infinity Cache)
+    and 4 GiB (HBM, translation included; the chain starts where no earlier
+    run went and a 1 GiB fill evicts the caches first)."""
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        log("probe library not built (%s): no probe context" % PROBE_LIB)
+        return None
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.probe_empty.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.probe_chase.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int,
+                                ctypes.c_void_p, ctypes.c_void_p]
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    out = {"empty_kernel_us": {}, "load_latency_ns": {}}
+    for grid, block in PROBE_SHAPES:
+        def launches():
+            for _ in range(WIN_SINGLE[0]):
+                rc = lib.probe_empty(grid, block, sp)
+                if rc != 0:
+                    raise RuntimeError("probe_empty failed: %d" % rc)
+        g = capture(launches)
+        out["empty_kernel_us"]["%dx%d" % (grid, block)] = window(g, WIN_SINGLE[0], 2)["mean_us"]
+        del g
+    res = torch.zeros(64, dtype=torch.int32, device=dev)
+    for name, region, links in PROBE_CHAINS:
+        slots = region // 256
+        n = region // 4
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7)
+        with torch.cuda.stream(stream):
+            perm = torch.randperm(slots, device=dev, generator=gen) * 64
+            nxt = torch.zeros(n, dtype=torch.int32, device=dev)
+            nxt[perm] = torch.roll(perm, -1).to(torch.int32)
+            lo, hi = int(nxt.min().item()), int(nxt.max().item())
+            if lo < 0 or hi >= n:
+                raise RuntimeError("chain index out of range")
+            cold = region > (256 << 20)
+            start = int(perm[slots // 2].item())
+            if cold:
+                flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+                flush.fill_(1.0)
+                del flush
+            else:   # one full pass first, so the chain is resident
+                if lib.probe_chase(ctypes.c_void_p(nxt.data_ptr()), n, start, slots,
+                                   ctypes.c_void_p(res.data_ptr()), sp) != 0:
+                    raise RuntimeError("probe_chase failed")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if lib.probe_chase(ctypes.c_void_p(nxt.data_ptr()), n, start, links,
+                               ctypes.c_void_p(res.data_ptr()), sp) != 0:
+                raise RuntimeError("probe_chase failed")
+            e1.record(stream)
+            stream.synchronize()
+        out["load_latency_ns"][name] = 1e6 * e0.elapsed_time(e1) / links
+        del perm, nxt
+    torch.cuda.synchronize()
+    log("probes: empty kernel %s us; load latency %s ns" % (
+        ", ".join("%s %.3f" % kv for kv in out["empty_kernel_us"].items()),
+        ", ".join("%s %.0f" % kv for kv in out["load_latency_ns"].items())))
+    return out
+
+
 def host_cpu():
     try:
         with open("/proc/cpuinfo") as f:
@@ -849,6 +920,7 @@ def main():
         stream.synchronize()
     copy_gbs = 2 * copy_bytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del csrc, cdst
+    probes = probe_context(torch, dev, stream, capture, window)
     vendor = vendor_context(torch, stream, capture, window, dA, dB, Wf, dxf)
     torch.cuda.synchronize()
     configs, configs_ok = gemm_configs(torch, bd, inputs, oracle, dev, capture, window)
@@ -987,6 +1059,11 @@ def main():
             "launch_floor_us": floor_us,
             "launch_floor_note": ("a fill of 256 KiB (a near-empty kernel) back to back in "
                                   "one graph: the queue's per-launch floor"),
+            "probes": probes,
+            "probes_note": ("bench_probes.hip: empty_kernel_us is an empty kernel back to back "
+                            "in one graph at grid x workgroup lanes (512x576 is the 2-bit "
+                            "GEMV's single call); load_latency_ns is one lane chasing random "
+                            "links through a region of that size"),
             "hbm_copy_gbs": copy_gbs,
             "hbm_copy_note": ("torch device-to-device copy of 1 GiB, 10 times, "
                               "read + write bytes / time: what plain streaming reaches"),
@@ -1013,6 +1090,8 @@ def main():
         "q2_single": {"us": round(q2_us, 3),
                       "weight_gbs": round(Q2_WEIGHT_BYTES / q2_us / 1e3, 0),
                       "frac": round(Q2_ALG_BYTES / q2_us / 1e3 / PEAK_HBM_GBS, 3),
+                      "empty_kernel_us": (round(probes["empty_kernel_us"]["512x576"], 3)
+                                          if probes else None),
                       "parity": ok_s(q2_ok)},
         "q4_batched_frac": round(Q4_ALG_BYTES / q4b_us / 1e3 / PEAK_HBM_GBS, 3),
         "gemv_f32_frac": round(F32_ALG_BYTES / gf_us / 1e3 / PEAK_HBM_GBS, 3),

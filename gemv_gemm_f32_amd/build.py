@@ -68,6 +68,19 @@ def build(save_temps: str | None = None, verbose: bool = False) -> str:
     return LIB
 
 
+def build_probes(src: str, out: str) -> str:
+    """Compile a stand-alone HIP source (the benchmark's probe kernels) into
+    the shared library `out`, with the library's device flags."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + CFLAGS + ["-shared", src, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        err = "\n".join(ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln)
+        raise RuntimeError("hipcc failed on %s:\n%s" % (src, err))
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--save-temps", default=None)

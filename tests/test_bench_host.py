@@ -188,3 +188,24 @@ def test_summarize_counters(bench, tmp_path):
     assert float(cells[2]) == pytest.approx(4 * 14.5e6 / (1024 * 8.0e5 / 8), abs=0.01)
     assert float(cells[4]) == pytest.approx(2.0, abs=0.01)
     assert float(cells[5]) == pytest.approx(0.1, abs=1e-3)
+
+
+def test_probe_library_exports_and_checks(bench):
+    """The probe kernels' library (built by the build entry point) exports
+    both probes, and each rejects out-of-range sizes before any HIP call."""
+    import ctypes
+    if not os.path.exists(bench.PROBE_LIB):
+        sys.path.insert(0, ROOT)
+        from gemv_gemm_f32_amd import build as b
+        b.build_probes(os.path.join(ROOT, "bench_probes.hip"), bench.PROBE_LIB)
+    lib = ctypes.CDLL(bench.PROBE_LIB)
+    lib.probe_empty.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.probe_chase.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int,
+                                ctypes.c_void_p, ctypes.c_void_p]
+    invalid = 1   # hipErrorInvalidValue
+    for grid, block in ((0, 64), (1, 0), (1, 1025)):
+        assert lib.probe_empty(grid, block, None) == invalid
+    dummy = ctypes.c_void_p(0x10000000)
+    assert lib.probe_chase(dummy, 100, 100, 10, dummy, None) == invalid     # start >= n
+    assert lib.probe_chase(dummy, 100, 0, -1, dummy, None) == invalid       # links < 0
+    assert lib.probe_chase(dummy, 1 << 33, 0, 10, dummy, None) == invalid   # n beyond 32 bits
