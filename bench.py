@@ -260,6 +260,8 @@ def gemm_configs(torch, bd, inputs, oracle, dev, capture, window):
 
 PROBE_LIB = os.path.join(ROOT, "libbench_probes.so")
 PROBE_SHAPES = ((1, 64), (512, 576))     # the 2-bit GEMV's single call: 512 x 576 lanes
+# (shape, independent accumulators per wave, workgroups, lanes per workgroup)
+PROBE_MFMA = ((32, 1, 256, 256), (32, 1, 1024, 256), (32, 4, 1024, 256), (16, 4, 1024, 256))
 PROBE_CHAINS = (("l2_1mib", 1 << 20, 100000), ("infinity_cache_64mib", 64 << 20, 100000),
                 ("hbm_4gib", 4 << 30, 20000))
 
@@ -267,7 +269,9 @@ PROBE_CHAINS = (("l2_1mib", 1 << 20, 100000), ("infinity_cache_64mib", 64 << 20,
 def probe_context(torch, dev, stream, capture, window):
     """Physics reference points from bench_probes.hip: the per-launch floor of
     an empty kernel (back to back in one graph, at the single call's launch
-    shape and at one wave), and the load-to-use latency of one lane chasing
+    shape and at one wave), the fp32 MFMA rate with no memory traffic (one
+    or four independent accumulators per wave, one or four waves per SIMD),
+    and the load-to-use latency of one lane chasing
     random 256-byte-spaced links through 1 MiB (L2), 64 MiB (Infinity Cache)
     and 4 GiB (HBM, translation included; the chain starts where no earlier
     run went and a 1 GiB fill evicts the caches first)."""
@@ -279,8 +283,26 @@ def probe_context(torch, dev, stream, capture, window):
     lib.probe_empty.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.probe_chase.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int,
                                 ctypes.c_void_p, ctypes.c_void_p]
+    lib.probe_mfma.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p, ctypes.c_void_p]
     sp = ctypes.c_void_p(stream.cuda_stream)
-    out = {"empty_kernel_us": {}, "load_latency_ns": {}}
+    out = {"empty_kernel_us": {}, "mfma_tflops": {}, "load_latency_ns": {}}
+    for shape, nacc, grid, block in PROBE_MFMA:
+        iters = 4000 if shape == 32 else 8000
+        buf = torch.empty(grid * block, dtype=torch.float32, device=dev)
+        with torch.cuda.stream(stream):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            for k in range(6):   # one warm-up launch, five timed
+                if k == 1:
+                    e0.record(stream)
+                if lib.probe_mfma(shape, nacc, grid, block, iters, ctypes.c_void_p(buf.data_ptr()),
+                                  sp) != 0:
+                    raise RuntimeError("probe_mfma failed")
+            e1.record(stream)
+            stream.synchronize()
+        flops = 5 * grid * block // 64 * iters * nacc * (4096 if shape == 32 else 2048)
+        key = "%dx%d_%dacc_%dx%d" % (shape, shape, nacc, grid, block)
+        out["mfma_tflops"][key] = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+        del buf
     for grid, block in PROBE_SHAPES:
         def launches():
             for _ in range(WIN_SINGLE[0]):
@@ -323,8 +345,9 @@ def probe_context(torch, dev, stream, capture, window):
         out["load_latency_ns"][name] = 1e6 * e0.elapsed_time(e1) / links
         del perm, nxt
     torch.cuda.synchronize()
-    log("probes: empty kernel %s us; load latency %s ns" % (
+    log("probes: empty kernel %s us; MFMA %s TFLOP/s; load latency %s ns" % (
         ", ".join("%s %.3f" % kv for kv in out["empty_kernel_us"].items()),
+        ", ".join("%s %.1f" % kv for kv in out["mfma_tflops"].items()),
         ", ".join("%s %.0f" % kv for kv in out["load_latency_ns"].items())))
     return out
 
@@ -1062,7 +1085,9 @@ def main():
             "probes": probes,
             "probes_note": ("bench_probes.hip: empty_kernel_us is an empty kernel back to back "
                             "in one graph at grid x workgroup lanes (512x576 is the 2-bit "
-                            "GEMV's single call); load_latency_ns is one lane chasing random "
+                            "GEMV's single call); mfma_tflops is back-to-back fp32 MFMAs of "
+                            "that shape with that many independent accumulators per wave on "
+                            "workgroups x lanes; load_latency_ns is one lane chasing random "
                             "links through a region of that size"),
             "hbm_copy_gbs": copy_gbs,
             "hbm_copy_note": ("torch device-to-device copy of 1 GiB, 10 times, "

@@ -209,3 +209,15 @@ def test_probe_library_exports_and_checks(bench):
     assert lib.probe_chase(dummy, 100, 100, 10, dummy, None) == invalid     # start >= n
     assert lib.probe_chase(dummy, 100, 0, -1, dummy, None) == invalid       # links < 0
     assert lib.probe_chase(dummy, 1 << 33, 0, 10, dummy, None) == invalid   # n beyond 32 bits
+
+
+def test_probe_mfma_checks(bench):
+    import ctypes
+    lib = ctypes.CDLL(bench.PROBE_LIB)
+    lib.probe_mfma.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p, ctypes.c_void_p]
+    dummy = ctypes.c_void_p(0x10000000)
+    invalid = 1   # hipErrorInvalidValue
+    for shape, nacc, grid, block, iters in ((8, 1, 1, 64, 1), (32, 3, 1, 64, 1), (16, 1, 0, 64, 1),
+                                            (32, 1, 1, 96, 1), (32, 1, 1, 2048, 1),
+                                            (16, 2, 1, 64, -1)):
+        assert lib.probe_mfma(shape, nacc, grid, block, iters, dummy, None) == invalid
