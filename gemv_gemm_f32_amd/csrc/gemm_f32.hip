@@ -62,6 +62,8 @@
 //    reproducible bit for bit.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace gg {
@@ -307,26 +309,38 @@ typedef __attribute__((address_space(3))) void lds_void;
 // chunk slot of x-major row r (8 chunks of 16 B per row of BK = 32 floats)
 __device__ __forceinline__ int xswz(int r) { return (r ^ (r >> 3)) & 7; }
 
-// One operand's k-slab (TX values of x by 32 of k) as NI buffer loads per
-// wave of a group of WPG waves; instruction j of wave w fills the 1 KB block
-// WPG*j + w of the stage.
+// One operand's k-slab (TX values of x by 32 of k) as NBLK buffer loads of
+// 1 KB, spread over the WPG waves of a group: instruction j of wave w fills
+// block WPG*j + w of the stage (when the blocks do not split evenly, the
+// last round of instructions is issued by the first waves only).
 //   XMAJOR: element (x, k) at P[x*ld + k]; the stage holds TX rows of 128 B.
 //   else  : element (x, k) at P[k*ld + x]; the stage holds 32 rows of TX*4 B.
 // KT: K is not a multiple of 4, so an x-major chunk can straddle K.
-template <int TX, bool XMAJOR, int WPG = 4, bool KT = false>
+// MF: the MFMA block the fragments feed, 32 (32 x 32 x 2) or 16 (16 x 16 x 4).
+template <int TX, bool XMAJOR, int WPG = 4, bool KT = false, int MF = 32>
 struct DirectOperand {
     static constexpr int BK = 32;
     static constexpr int STAGE = TX * BK * 4;     // bytes per stage
-    static constexpr int NI = STAGE / 1024 / WPG; // loads per wave per slab
-    static_assert(NI >= 1 && NI * 1024 * WPG == STAGE, "tile must split over the waves");
-    // k-major rows of CPR 16-byte chunks turn by 8 chunks (128 bytes) on
-    // every other group of four rows, so that the two half-waves of a
-    // fragment read (4 rows apart) use different banks; rows of 32 floats
-    // have no second half and take 2-way conflicts instead.
+    static constexpr int NBLK = STAGE / 1024;     // 1 KB load instructions per slab
+    static constexpr int NI = (NBLK + WPG - 1) / WPG;   // per wave, at most
+    static_assert(NBLK >= WPG && NBLK * 1024 == STAGE, "tile must split over the waves");
+    // k-major rows of CPR 16-byte chunks are rotated so that the lane groups
+    // of a fragment read, which read rows 4 apart, use different banks: by 8
+    // chunks (128 bytes) on every other group of four rows for 32 x 32
+    // blocks (two half-waves), and by 4 chunks (64 bytes) per group of four
+    // rows, cycling over four groups, for 16 x 16 blocks (four quarter-waves).
+    // Rows of 32 floats have no second half and take 2-way conflicts instead.
     static constexpr int CPR = TX / 4;
-    static_assert(XMAJOR || CPR % 8 == 0, "k-major tiles are a multiple of 32 wide");
-    static __device__ __forceinline__ int kslot(int c, int row) {
-        return (c + 8 * ((row >> 2) & 1)) % CPR;
+    static_assert(XMAJOR || CPR % (MF == 32 ? 8 : 16) == 0,
+                  "k-major tiles are a multiple of 32 (64 for 16 x 16 blocks) wide");
+    static __device__ __forceinline__ int krot(int row) {
+        return MF == 32 ? 8 * ((row >> 2) & 1) : 4 * ((row >> 2) & 3);
+    }
+    static __device__ __forceinline__ int kslot(int c, int row) { return (c + krot(row)) % CPR; }
+    // whether this wave issues instruction j
+    static __device__ __forceinline__ bool has(int j, int wave) {
+        if constexpr (NBLK % WPG == 0) return true;
+        return WPG * j + wave < NBLK;
     }
     unsigned voff[NI];   // byte offset of this lane's chunk at k = 0
     int kof[NI];         // k of this lane's chunk (x-major) or row (k-major) in the slab
@@ -334,7 +348,7 @@ struct DirectOperand {
     __device__ __forceinline__ void init(int64_t ld, int x0, int X, int lane, int wave) {
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-            const int blk = WPG * j + wave;
+            const int blk = has(j, wave) ? WPG * j + wave : 0;
             if (XMAJOR) {
                 const int row = 8 * blk + lane / 8;
                 const int c = (lane % 8) ^ xswz(row);
@@ -345,7 +359,7 @@ struct DirectOperand {
                 // q % CPR), so it fetches the chunk of that row whose slot it is
                 const int q = 64 * blk + lane;
                 const int row = q / CPR;
-                const int c = (q % CPR + CPR - 8 * ((row >> 2) & 1) % CPR) % CPR;
+                const int c = (q % CPR + CPR - krot(row) % CPR) % CPR;
                 // chunks past the row's last one load that one (their columns
                 // are never stored); the last one may run past X into the next
                 // row, or past the operand's end, which reads zeros
@@ -367,8 +381,9 @@ struct DirectOperand {
         const unsigned so = (unsigned)((XMAJOR ? (int64_t)k0 : k0 * ld) * 4);
 #pragma unroll
         for (int j = 0; j < NI; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc, (lds_void *)(stage + (WPG * j + wave) * 1024), 16, voff[j], so, 0, 0);
+            if (has(j, wave))
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc, (lds_void *)(stage + (WPG * j + wave) * 1024), 16, voff[j], so, 0, 0);
 #endif
     }
     // after this wave's loads of the slab at k0 have landed: zero what lies at
@@ -377,6 +392,7 @@ struct DirectOperand {
     __device__ __forceinline__ void zero_tail(char *stage, int k0, int K, int wave, int lane) const {
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
+            if (!has(j, wave)) continue;
             float *p = reinterpret_cast<float *>(stage + (WPG * j + wave) * 1024 + lane * 16);
             const int k = k0 + kof[j];
             if (k >= K) {
@@ -386,15 +402,17 @@ struct DirectOperand {
             }
         }
     }
-    // byte offset, within a stage, of lane (l32, h)'s operand of k-group g
-    // for the 32-block at x = xb
-    static __device__ __forceinline__ int frag_offset(int xb, int l32, int h, int g) {
-        if (XMAJOR) {
-            const int r = xb + l32;
-            return r * 128 + (((2 * g + h) ^ xswz(r)) * 16);
-        }
-        const int x = xb + l32;
-        return (8 * g + 4 * h) * TX * 4 + kslot(x >> 2, 4 * h) * 16 + (x & 3) * 4;
+    // byte offset, within a stage, of a lane's operand of k-group g for the
+    // MF-block at x = xb.  32 x 32 x 2: half-wave h = lane / 32 takes x =
+    // xb + lane % 32 at k = 8g + 4h + t in step t.  16 x 16 x 4: quarter-wave
+    // q = lane / 16 takes x = xb + lane % 16 at k = 16g + 4q + t.  Either
+    // way an x-major lane reads the 4 k of its step from one 16-byte chunk.
+    static __device__ __forceinline__ int frag_offset(int xb, int lane, int g) {
+        const int x = xb + (lane & (MF - 1));
+        const int part = lane / MF;               // h or q
+        const int krow = (64 / MF) * 4 * g + 4 * part;
+        if (XMAJOR) return x * 128 + ((((64 / MF) * g + part) ^ xswz(x)) * 16);
+        return krow * TX * 4 + kslot(x >> 2, 4 * part) * 16 + (x & 3) * 4;
     }
     static __device__ __forceinline__ v4f frag(const char *stage, int off) {
         if (XMAJOR) return *reinterpret_cast<const v4f *>(stage + off);
@@ -406,25 +424,34 @@ struct DirectOperand {
 // KS groups of WPG waves split the k-slabs of one output tile: group g takes
 // slabs g, g + KS, g + 2 KS, ... through its own double-buffered stages.  At
 // the end groups 1 .. KS-1 hand their accumulators to group 0 through LDS,
-// which adds them in group order, so the sum is fixed for a given KS.  The
-// WPG waves of a group lay out as 2 x 2 (WPG = 4), 1 x 2 or 2 x 1 (WPG = 2,
-// along the longer side of the tile) or 1 x 1 over the tile, each wave
-// holding 32 x 32 MFMA blocks.
-template <int BM, int BN, bool AX, bool BX, int KS, int WPG = 4, bool KT = false>
+// which adds them in group order, so the sum is fixed for a given KS.  With
+// 32 x 32 MFMA blocks (MF = 32) the WPG waves of a group lay out as 2 x 2
+// (WPG = 4), 1 x 2 or 2 x 1 (WPG = 2, along the longer side of the tile) or
+// 1 x 1 over the tile; with 16 x 16 blocks (MF = 16) they stack along M,
+// each wave holding a row of BN / 16 blocks (64 x 48 tiles: 16 x 48 per
+// wave, three independent accumulators).
+template <int BM, int BN, bool AX, bool BX, int KS, int WPG = 4, bool KT = false, int MF = 32>
 __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
     int M, int N, int K, float alpha, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float beta, float *__restrict__ C, int64_t ldc,
     int tiles_m, int tiles_n) {
     constexpr int BK = 32;
-    constexpr int WC = WPG == 4 ? 2 : (WPG == 2 && BN >= BM ? 2 : 1);   // wave columns
+    constexpr int WC = MF == 16 ? 1 : (WPG == 4 ? 2 : (WPG == 2 && BN >= BM ? 2 : 1));   // wave columns
     constexpr int WR = WPG / WC;                  // wave rows
     constexpr int WM = BM / WR, WN = BN / WC;
-    constexpr int IB = WM / 32, JB = WN / 32;
-    static_assert(IB * 32 == WM && JB * 32 == WN && WR * WC == WPG, "tile must split into 32-blocks");
-    using OA = DirectOperand<BM, AX, WPG, KT>;
-    using OB = DirectOperand<BN, BX, WPG, KT>;
+    constexpr int IB = WM / MF, JB = WN / MF;
+    static_assert(IB * MF == WM && JB * MF == WN && WR * WC == WPG, "tile must split into MF-blocks");
+    // 16 x 16 blocks: a k-major B tile 48 wide is staged 64 wide (the next
+    // 16 columns ride along unused) so that its rows keep the conflict-free
+    // rotation of 64-float rows
+    constexpr int TB = (MF == 16 && !BX && BN == 48) ? 64 : BN;
+    using OA = DirectOperand<BM, AX, WPG, KT, MF>;
+    using OB = DirectOperand<TB, BX, WPG, KT, MF>;
+    using Acc = typename std::conditional<MF == 32, v16f, v4f>::type;
+    constexpr int AR = MF == 32 ? 16 : 4;         // accumulator words per block
+    constexpr int NG = MF == 32 ? 4 : 2;          // k-groups of 4 steps per slab
     constexpr int STAGE = OA::STAGE + OB::STAGE;
-    constexpr int ACCW = IB * JB * 16;            // accumulator words per lane
+    constexpr int ACCW = IB * JB * AR;            // accumulator words per lane
     static_assert(KS == 1 || (KS - 1) * 64 * WPG * ACCW * 4 <= KS * 2 * STAGE,
                   "the hand-over of partial sums must fit in the stages");
     __shared__ __attribute__((aligned(1024))) char smem[KS * 2 * STAGE];
@@ -432,7 +459,7 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave / WPG, wq = wave % WPG;  // k-group, wave within the group
-    const int h = lane >> 5, l32 = lane & 31;
+    const int h = lane >> 5;
     int tm, tn;
     tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -446,22 +473,22 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
     char *const gsmem = smem + grp * 2 * STAGE;
     auto stage_a = [&](int b) { return gsmem + b * STAGE; };
     auto stage_b = [&](int b) { return gsmem + b * STAGE + OA::STAGE; };
-    int aoff[IB][4], boff[JB][4];
+    int aoff[IB][NG], boff[JB][NG];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int g = 0; g < NG; ++g) {
 #pragma unroll
-        for (int i = 0; i < IB; ++i) aoff[i][g] = OA::frag_offset(wm + 32 * i, l32, h, g);
+        for (int i = 0; i < IB; ++i) aoff[i][g] = OA::frag_offset(wm + MF * i, lane, g);
 #pragma unroll
-        for (int j = 0; j < JB; ++j) boff[j][g] = OB::frag_offset(wn + 32 * j, l32, h, g);
+        for (int j = 0; j < JB; ++j) boff[j][g] = OB::frag_offset(wn + MF * j, lane, g);
     }
 
-    v16f acc[IB][JB];
+    Acc acc[IB][JB];
 #pragma unroll
     for (int i = 0; i < IB; ++i)
 #pragma unroll
         for (int j = 0; j < JB; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+            for (int r = 0; r < AR; ++r) acc[i][j][r] = 0.f;
 
     const int nk = (K + BK - 1) / BK;
     const int rounds = (nk + KS - 1) / KS;        // the same for every group
@@ -497,14 +524,14 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
 #pragma unroll
             for (int j = 0; j < JB; ++j) fb[j] = OB::frag(bs, boff[j][0]);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
+            for (int g = 0; g < NG; ++g) {
                 v4f na[IB], nb[JB];
 #pragma unroll
                 for (int i = 0; i < IB; ++i)
-                    na[i] = g + 1 < 4 ? OA::frag(as, aoff[i][g + 1]) : fa[i];
+                    na[i] = g + 1 < NG ? OA::frag(as, aoff[i][g + 1]) : fa[i];
 #pragma unroll
                 for (int j = 0; j < JB; ++j)
-                    nb[j] = g + 1 < 4 ? OB::frag(bs, boff[j][g + 1]) : fb[j];
+                    nb[j] = g + 1 < NG ? OB::frag(bs, boff[j][g + 1]) : fb[j];
                 // keep the next group's LDS reads ahead of this group's MFMAs
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -512,9 +539,14 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
 #pragma unroll
                     for (int i = 0; i < IB; ++i)
 #pragma unroll
-                        for (int j = 0; j < JB; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                fa[i][t], fb[j][t], acc[i][j], 0, 0, 0);
+                        for (int j = 0; j < JB; ++j) {
+                            if constexpr (MF == 32)
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                                    fa[i][t], fb[j][t], acc[i][j], 0, 0, 0);
+                            else
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                    fa[i][t], fb[j][t], acc[i][j], 0, 0, 0);
+                        }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int i = 0; i < IB; ++i) fa[i] = na[i];
@@ -546,7 +578,7 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
 #pragma unroll
                 for (int j = 0; j < JB; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) dst[((i * JB + j) * 16 + r) * 64] = acc[i][j][r];
+                    for (int r = 0; r < AR; ++r) dst[((i * JB + j) * AR + r) * 64] = acc[i][j][r];
         }
         __syncthreads();
         if (grp > 0) return;
@@ -558,30 +590,34 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
 #pragma unroll
                 for (int j = 0; j < JB; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] += src[((i * JB + j) * 16 + r) * 64];
+                    for (int r = 0; r < AR; ++r) acc[i][j][r] += src[((i * JB + j) * AR + r) * 64];
         }
     }
 
+    // Accumulator layouts: register r of lane l holds, in a 32 x 32 block,
+    // row 8*(r/4) + 4*(l/32) + r%4 and column l%32; in a 16 x 16 block, row
+    // 4*(l/16) + r and column l%16.
 #pragma unroll
     for (int i = 0; i < IB; ++i)
 #pragma unroll
         for (int j = 0; j < JB; ++j) {
-            const int col = n0 + wn + 32 * j + l32;
+            const int col = n0 + wn + MF * j + (lane & (MF - 1));
             if (col >= N) continue;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+            for (int r = 0; r < AR; ++r) {
+                const int row = m0 + wm + MF * i +
+                                (MF == 32 ? 8 * (r >> 2) + 4 * h + (r & 3) : 4 * (lane >> 4) + r);
                 if (row < M) store_c(C + (int64_t)row * ldc + col, acc[i][j][r], alpha, beta);
             }
         }
 }
 
-template <bool AX, bool BX, int BM, int BN, int KS = 1, int WPG = 4, bool KT = false>
+template <bool AX, bool BX, int BM, int BN, int KS = 1, int WPG = 4, bool KT = false, int MF = 32>
 hipError_t launch_direct(int M, int N, int K, float alpha, const float *A, int64_t lda,
                          const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
                          hipStream_t s) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    return launch(gemm_f32_direct<BM, BN, AX, BX, KS, WPG, KT>, dim3(tiles_m * tiles_n),
+    return launch(gemm_f32_direct<BM, BN, AX, BX, KS, WPG, KT, MF>, dim3(tiles_m * tiles_n),
                   dim3(64 * WPG * KS), s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tiles_m,
                   tiles_n);
 }
@@ -617,10 +653,12 @@ hipError_t launch_quarter(int ks, int M, int N, int K, float alpha, const float 
 
 // The direct kernel for a tile choice made by launch_gemm.
 template <bool AX, bool BX, bool KT>
-hipError_t launch_pick(bool quarter, bool half, bool tall, int ksq, int ksh, int ks, int M, int N,
-                       int K, float alpha, const float *A, int64_t lda, const float *B,
-                       int64_t ldb, float beta, float *C, int64_t ldc, hipStream_t s) {
+hipError_t launch_pick(bool quarter, bool half, bool tall, bool t48, int ksq, int ksh, int ks,
+                       int M, int N, int K, float alpha, const float *A, int64_t lda,
+                       const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
+                       hipStream_t s) {
     if (quarter) return launch_quarter<AX, BX, KT>(ksq, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
+    if (t48) return launch_direct<AX, BX, 64, 48, 4, 4, KT, 16>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
     if (half)
         return tall ? launch_half<AX, BX, true, KT>(ksh, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s)
                     : launch_half<AX, BX, false, KT>(ksh, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s);
@@ -707,13 +745,22 @@ hipError_t launch_gemm(bool ax, bool bx, int M, int N, int K, float alpha, const
     const bool quarter = small && tiles_32 <= (int64_t)num_cus;
     const bool half = small ? !quarter
                             : tiles_64 > (int64_t)num_cus && 10 * share(tiles_64) >= 6 * share(tiles_h);
+    // Between half the CUs and all of them, where 64 x 64 tiles leave CUs
+    // idle: 64 x 48 tiles of 16 x 16 MFMA blocks in four k-groups when their
+    // grid still fits one tile per CU (1024 x 768 outputs: 256 tiles for 256
+    // CUs instead of 192; 1024 x 768 x 3072 53.7 -> 44.8 us).  With more
+    // tiles than CUs, 64 x 48 tiles in two k-groups ran slower than narrow
+    // tiles on 1024 x 2304 x 768 and 768 x 3072 x 1024 (41.5 against 39.7
+    // us, 53.4 against 50.8), so they serve only this case.
+    const int64_t tiles_48 = (int64_t)((M + 63) / 64) * ((N + 47) / 48);
+    const bool t48 = !small && ks == 4 && tiles_48 <= (int64_t)num_cus && tiles_48 > tiles_64;
     const int ksq = slabs >= 8 ? 8 : (slabs >= 4 ? 4 : (slabs >= 2 ? 2 : 1));
     const int ksh = !small ? ks : (slabs >= 12 ? 6 : (slabs >= 8 ? 4 : (slabs >= 4 ? 2 : 1)));
 #define GG_ARGS M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s
 #define GG_GEMM_DIRECT(AX_, BX_)                                                     \
     if (K % 4 != 0 && (AX_ || BX_))                                                  \
-        return launch_pick<AX_, BX_, true>(quarter, half, tall, ksq, ksh, ks, GG_ARGS); \
-    return launch_pick<AX_, BX_, false>(quarter, half, tall, ksq, ksh, ks, GG_ARGS);
+        return launch_pick<AX_, BX_, true>(quarter, half, tall, t48, ksq, ksh, ks, GG_ARGS); \
+    return launch_pick<AX_, BX_, false>(quarter, half, tall, t48, ksq, ksh, ks, GG_ARGS);
 #define GG_GEMM_SHAPE(AX_, BX_, VA_, VB_)                                     \
     return big ? launch_t<AX_, BX_, VA_, VB_, 128, 64>(GG_ARGS)            \
                : launch_t<AX_, BX_, VA_, VB_, 64, 64>(GG_ARGS);

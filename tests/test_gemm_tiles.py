@@ -28,8 +28,9 @@ def _cus():
 
 
 def regime(M, N, K, ta, cus):
-    """'quarter', 'half' or 'full' (64 x 64) for an operand layout that takes
-    the direct loads; ta is the transpose flag of A (A x-major when not)."""
+    """'quarter', 'half', 't48' (64 x 48 tiles of 16 x 16 blocks) or 'full'
+    (64 x 64) for an operand layout that takes the direct loads; ta is the
+    transpose flag of A (A x-major when not)."""
     cdiv = lambda a, b: -(-a // b)
     t64 = cdiv(M, 64) * cdiv(N, 64)
     t32 = cdiv(M, 32) * cdiv(N, 32)
@@ -37,7 +38,13 @@ def regime(M, N, K, ta, cus):
     th = tall if tall < wide or (tall == wide and not ta) else wide
     if 2 * t64 < cus:
         return "quarter" if t32 <= cus else "half"
-    if t64 > cus and 10 * cdiv(t64, cus) >= 6 * cdiv(th, cus):
+    share = lambda t: cdiv(t, cus)
+    slabs = cdiv(K, 32)
+    ks = 4 if t64 <= cus and slabs >= 8 else (2 if slabs >= 4 else 1)
+    t48 = cdiv(M, 64) * cdiv(N, 48)
+    if ks == 4 and t64 < t48 <= cus:
+        return "t48"
+    if t64 > cus and 10 * share(t64) >= 6 * share(th):
         return "half"
     return "full"
 
@@ -54,8 +61,8 @@ CASES = [
     # rows) with 1, 2, 4 and 6 k-groups
     ("half", 500, 600, 100), ("half", 348, 772, 772), ("half", 500, 600, 300),
     ("half", 500, 600, 60),
-    # narrow tiles on a grid a little larger than the CUs, K tail in a slab
-    ("half", 1000, 1212, 300), ("half", 1024, 1216, 60),
+    # narrow tiles on grids larger than the CUs, K tails in a slab
+    ("half", 1000, 1212, 300), ("half", 1024, 1216, 60), ("half", 1280, 2044, 300),
 ]
 
 
@@ -72,20 +79,21 @@ def test_matches_oracle(want, M, N, K, ta, tb):
 
 
 @pytest.mark.parametrize("ta,tb", PAIRS)
-def test_transformer_shape_narrow_tiles(ta, tb):
-    """1024 x 2304 x 768 (576 tiles of 64 x 64): narrow tiles, every element
-    against the oracle, N(0, 1) activations and N(0, 0.02) weights."""
-    M, N, K = 1024, 2304, 768
+@pytest.mark.parametrize("M,N,K", [(1024, 2304, 768), (1280, 2048, 1024)])
+def test_transformer_shape_narrow_tiles(ta, tb, M, N, K):
+    """1024 x 2304 x 768 (576 tiles of 64 x 64) and 1280 x 2048 x 1024 (640):
+    narrow tiles, every element against the oracle, N(0, 1) activations and
+    N(0, 0.02) weights."""
     assert regime(M, N, K, ta, _cus()) == "half"
     A = inputs.normal(RNG, (K, M) if ta else (M, K))
     B = (0.02 * inputs.normal(RNG, (N, K) if tb else (K, N))).astype(np.float32)
     ref, bound = oracle.gemm_ex(A, B, None, 1.0, 0.0, trans_a=bool(ta), trans_b=bool(tb))
     got = host(bd.gemm_f32_ex(dev(A), dev(B), None, 1.0, 0.0, trans_a=bool(ta), trans_b=bool(tb)))
-    assert_close(got, ref, bound, "1024x2304x768 t%d%d" % (ta, tb))
+    assert_close(got, ref, bound, "%dx%dx%d t%d%d" % (M, N, K, ta, tb))
 
 
 @pytest.mark.parametrize("ta,tb", PAIRS)
-@pytest.mark.parametrize("M,N,K", [(100, 200, 1028), (500, 600, 100), (1000, 1212, 300)])
+@pytest.mark.parametrize("M,N,K", [(100, 200, 1028), (500, 600, 100), (1280, 2044, 300)])
 def test_integer_exact(ta, tb, M, N, K):
     A, B = _ops(ta, tb, M, N, K, lambda s: inputs.integers(RNG, s))
     ref, _ = oracle.gemm_ex(A, B, None, 1.0, 0.0, trans_a=bool(ta), trans_b=bool(tb))
@@ -94,7 +102,7 @@ def test_integer_exact(ta, tb, M, N, K):
 
 
 @pytest.mark.parametrize("ta,tb", PAIRS)
-@pytest.mark.parametrize("M,N,K", [(96, 136, 300), (1000, 1212, 300)])
+@pytest.mark.parametrize("M,N,K", [(96, 136, 300), (1280, 2044, 300)])
 def test_padded_leading_dimensions(ta, tb, M, N, K):
     """Leading dimensions padded by 4 and 8 floats (16-byte rows kept, so the
     direct loads apply), NaN in the padding, C padded with a canary."""
