@@ -364,7 +364,11 @@ def host_cpu():
 
 
 def _short_name(kernel):
-    k = kernel.replace("void gg::(anonymous namespace)::", "")
+    k = kernel.replace("(anonymous namespace)::", "")
+    for prefix in ("void gg::", "gg::", "void "):
+        if k.startswith(prefix):
+            k = k[len(prefix):]
+            break
     return k.split("(")[0]
 
 
