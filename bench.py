@@ -24,8 +24,9 @@ HIP events on the replay stream.  Each kernel's launch duration comes from a
 fixed window that does not depend on K: one graph of L back-to-back launches
 of that kernel alone (inputs rotating as above), replayed for at least
 0.1 s of warm-up and then R times with a HIP event after each replay; `mean_us`
-is the window's time over its R * L launches and `median_us` the median of the
-per-replay means.  The rooflines use `mean_us`.
+is the window's time over its R * L launches; `median_us`, `min_us`, `max_us`,
+`p10_us` and `p90_us` are taken over the per-replay means.  The rooflines use
+`mean_us`.
 
 Output: one JSON line.  `value` is the GEMM's TFLOP/s (2 * 2048^3 flops per
 launch over its mean launch duration).  `q2_gemv` and `q2_gemv_batched` give
@@ -852,7 +853,9 @@ def main():
         return {"mean_us": total_us / (launches * replays),
                 "median_us": per[len(per) // 2] if replays % 2 else
                 0.5 * (per[replays // 2 - 1] + per[replays // 2]),
-                "min_us": per[0], "max_us": per[-1], "launches": launches * replays,
+                "min_us": per[0], "max_us": per[-1],
+                "p10_us": float(np.percentile(per, 10)), "p90_us": float(np.percentile(per, 90)),
+                "launches": launches * replays,
                 "launches_per_replay": launches, "replays": replays, "warmup_s": warm_s}
 
     def tok_idx(t, rot):
