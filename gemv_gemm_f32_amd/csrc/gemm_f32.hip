@@ -450,6 +450,12 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
     using Acc = typename std::conditional<MF == 32, v16f, v4f>::type;
     constexpr int AR = MF == 32 ? 16 : 4;         // accumulator words per block
     constexpr int NG = MF == 32 ? 4 : 2;          // k-groups of 4 steps per slab
+    // Narrow tiles (two waves per k-group) issue the next slab's loads after
+    // the first k-group's MFMAs rather than before them: on the GPT-2 shapes
+    // that take them, 1024 x 2304 x 768 40.3 -> 36.5 us and 768 x 3072 x 1024
+    // 50.6 -> 46.9 us.  The 64 x 64 and 64 x 48 tiles keep the early issue
+    // (2048^3 127.5 -> 129.2 us, 1024 x 768 x 3072 44.8 -> 46.3 us late).
+    constexpr bool LATE = WPG == 2;
     constexpr int STAGE = OA::STAGE + OB::STAGE;
     constexpr int ACCW = IB * JB * AR;            // accumulator words per lane
     static_assert(KS == 1 || (KS - 1) * 64 * WPG * ACCW * 4 <= KS * 2 * STAGE,
@@ -512,7 +518,7 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
         const bool more = r + 1 < rounds;
         // slab kn goes to the stage last read in round r-1, whose reads all
         // finished before the previous barrier
-        if (more && kn < nk) {
+        if (!LATE && more && kn < nk) {
             oa.issue(stage_a(buf ^ 1), A, exta, lda, k1, wq);
             ob.issue(stage_b(buf ^ 1), B, extb, ldb, k1, wq);
         }
@@ -548,6 +554,11 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
                                     fa[i][t], fb[j][t], acc[i][j], 0, 0, 0);
                         }
                 __builtin_amdgcn_sched_barrier(0);
+                if (LATE && g == 0 && more && kn < nk) {
+                    oa.issue(stage_a(buf ^ 1), A, exta, lda, k1, wq);
+                    ob.issue(stage_b(buf ^ 1), B, extb, ldb, k1, wq);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
 #pragma unroll
                 for (int i = 0; i < IB; ++i) fa[i] = na[i];
 #pragma unroll
