@@ -450,12 +450,15 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
     using Acc = typename std::conditional<MF == 32, v16f, v4f>::type;
     constexpr int AR = MF == 32 ? 16 : 4;         // accumulator words per block
     constexpr int NG = MF == 32 ? 4 : 2;          // k-groups of 4 steps per slab
-    // Narrow tiles (two waves per k-group) issue the next slab's loads after
-    // the first k-group's MFMAs rather than before them: on the GPT-2 shapes
-    // that take them, 1024 x 2304 x 768 40.3 -> 36.5 us and 768 x 3072 x 1024
-    // 50.6 -> 46.9 us.  The 64 x 64 and 64 x 48 tiles keep the early issue
-    // (2048^3 127.5 -> 129.2 us, 1024 x 768 x 3072 44.8 -> 46.3 us late).
-    constexpr bool LATE = WPG == 2;
+    // Narrow and 32 x 32 tiles (one or two waves per k-group), and 64 x 64
+    // tiles in four k-groups, issue the next slab's loads after the first
+    // k-group's MFMAs rather than before them: 1024 x 2304 x 768 40.3 -> 36.5
+    // us, 768 x 3072 x 1024 50.6 -> 46.9, 500 x 500 x 2000 14.8 -> 13.5,
+    // 1024 x 1024 x 4096 69.6 -> 65.9.  64 x 64 tiles in two k-groups (two
+    // workgroups per CU) and the 64 x 48 tiles keep the early issue: late,
+    // 2048^3 took 129.2 us against 127.5 and 1024 x 768 x 3072 46.3 against
+    // 44.8.
+    constexpr bool LATE = WPG <= 2 || (KS == 4 && MF == 32);
     constexpr int STAGE = OA::STAGE + OB::STAGE;
     constexpr int ACCW = IB * JB * AR;            // accumulator words per lane
     static_assert(KS == 1 || (KS - 1) * 64 * WPG * ACCW * 4 <= KS * 2 * STAGE,
