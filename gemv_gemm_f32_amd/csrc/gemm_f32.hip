@@ -543,7 +543,7 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
                     nb[j] = g + 1 < NG ? OB::frag(bs, boff[j][g + 1]) : fb[j];
                 // The next group's LDS reads and this group's MFMAs: with one
                 // 32 x 32 accumulator per wave, each MFMA is followed by up to
-                // two of the reads (the pattern below); 16 x 16 blocks over a
+                // two of the reads, one in narrow tiles (the pattern below); 16 x 16 blocks over a
                 // k-major B keep all reads ahead of the MFMAs; 16 x 16 blocks
                 // over an x-major B are left to the compiler.  Same box,
                 // against all reads ahead: 2048^3 126.8 -> 125.7 us, the
@@ -567,7 +567,9 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
+                        // two LDS reads (one in narrow tiles: 1280 x 2048 x 1024
+                        // 53.1 -> 45.6 us, the others within 1%)
+                        __builtin_amdgcn_sched_group_barrier(0x100, WPG == 2 ? 1 : 2, 0);
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
