@@ -541,15 +541,11 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
 #pragma unroll
                 for (int j = 0; j < JB; ++j)
                     nb[j] = g + 1 < NG ? OB::frag(bs, boff[j][g + 1]) : fb[j];
-                // The next group's LDS reads and this group's MFMAs: with one
-                // 32 x 32 accumulator per wave, each MFMA is followed by up to
-                // two of the reads, one in narrow tiles (the pattern below); 16 x 16 blocks over a
-                // k-major B keep all reads ahead of the MFMAs; 16 x 16 blocks
-                // over an x-major B are left to the compiler.  Same box,
-                // against all reads ahead: 2048^3 126.8 -> 125.7 us, the
-                // narrow-tile GPT-2 products 1-3% and the 64 x 48 tiles over
-                // an x-major B 3% faster, 1024 x 768 x 3072 unchanged.
-                if constexpr (MF == 16 && !BX) __builtin_amdgcn_sched_barrier(0);
+                // The next group's LDS reads and this group's MFMAs, interleaved
+                // by the pattern below: each MFMA is followed by up to two of
+                // the reads (one in narrow tiles).  Same box, against all reads
+                // ahead of the MFMAs: 2048^3 126.8 -> 125.7 us, the GPT-2
+                // products 1-3.5% faster.
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -563,14 +559,12 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
                                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
                                     fa[i][t], fb[j][t], acc[i][j], 0, 0, 0);
                         }
-                if constexpr (MF == 32 && IB * JB == 1) {
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                        // two LDS reads (one in narrow tiles: 1280 x 2048 x 1024
-                        // 53.1 -> 45.6 us, the others within 1%)
-                        __builtin_amdgcn_sched_group_barrier(0x100, WPG == 2 ? 1 : 2, 0);
-                    }
+                for (int t = 0; t < 4 * IB * JB; ++t) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    // two LDS reads (one in narrow tiles: 1280 x 2048 x 1024
+                    // 53.1 -> 45.6 us, the others within 1%)
+                    __builtin_amdgcn_sched_group_barrier(0x100, WPG == 2 ? 1 : 2, 0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 if (LATE && g == 0 && more && kn < nk) {
