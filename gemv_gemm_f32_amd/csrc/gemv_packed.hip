@@ -366,12 +366,11 @@ constexpr int FLAT_THREADS = 192;
 // 4.46 us).
 constexpr int FLAT_SINGLE_THREADS = 576;
 constexpr int FLAT_MIN_CPR = 8, FLAT_MAX_CPR = 48;
-constexpr int FLAT_MAX_RPS = FLAT_THREADS / FLAT_MIN_CPR;
 
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
 
 // Cache policy of the code loads: non-temporal (each code byte is read once).
-constexpr int NT = 2;
+[[maybe_unused]] constexpr int NT = 2;
 
 // The per-lane pieces of the flat split, shared by the one-shot and the
 // streaming kernels so that both form every row the same way.
@@ -745,7 +744,6 @@ hipError_t launch_chunk(int count, int M, int K, const uint8_t *const *Q, int64_
 //    through LDS, instead of one 2-byte load per lane and step.
 //  * Reduction.  The row's partial sums meet in LDS after one barrier and one
 //    lane per row adds them in a fixed pairwise tree: deterministic.
-constexpr int IDOT_MAX_WAVES = FLAT_MAX_CPR / 8;
 
 template <int WAVES, int T>
 struct IdotSmem {
