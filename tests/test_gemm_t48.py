@@ -93,3 +93,42 @@ def test_repeat_bits():
     B = inputs.uniform(RNG, (K, N))
     dA, dB = dev(A), dev(B)
     assert np.array_equal(host(bd.gemm_f32(dA, dB)), host(bd.gemm_f32(dA, dB)))
+
+
+def _placed(a, offset, pad):
+    """Device copy of 2-D float32 array a, `offset` floats into a NaN-filled
+    buffer, with `pad` extra floats per row."""
+    t = torch()
+    rows, cols = a.shape
+    ld = cols + pad
+    buf = t.full((offset + rows * ld,), float("nan"), dtype=t.float32, device="cuda")
+    view = buf[offset:offset + rows * ld].view(rows, ld)[:, :cols]
+    view.copy_(t.from_numpy(np.ascontiguousarray(a)).to("cuda"))
+    return view
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_cases(seed):
+    """Seeded shapes drawn until the launcher's rule takes 64 x 48 tiles:
+    random transpose pairs, K with tails, base offsets of 1 to 4 floats,
+    padded leading dimensions and alpha/beta."""
+    rng = np.random.default_rng(48000 + seed)
+    cus = _cus()
+    while True:
+        M, N = int(rng.integers(500, 1100)), int(rng.integers(300, 1000))
+        K = int(rng.integers(256, 1000))
+        ta, tb = (bool(v) for v in rng.integers(0, 2, 2))
+        if regime(M, N, K, ta, cus) == "t48":
+            break
+    alpha, beta = (float(v) for v in rng.choice([1.0, -1.5, 0.5], 2))
+    A = inputs.uniform(rng, (K, M) if ta else (M, K))
+    B = inputs.uniform(rng, (N, K) if tb else (K, N))
+    C = inputs.uniform(rng, (M, N))
+    oa, ob, oc = (int(v) for v in rng.choice([0, 4, 1, 3], 3))
+    pa, pb, pc = (int(v) for v in rng.choice([0, 4, 8, 5], 3))
+    dA, dB, dC = _placed(A, oa, pa), _placed(B, ob, pb), _placed(C, oc, pc)
+    bd.gemm_f32_ex(dA, dB, dC, alpha, beta, trans_a=ta, trans_b=tb)
+    ref, bound = oracle.gemm_ex(A, B, C, alpha, beta, trans_a=ta, trans_b=tb)
+    assert_close(host(dC), ref, bound,
+                 "seed %d: %s%s %dx%dx%d offsets %d/%d/%d pads %d/%d/%d"
+                 % (seed, "T" if ta else "N", "T" if tb else "N", M, N, K, oa, ob, oc, pa, pb, pc))
