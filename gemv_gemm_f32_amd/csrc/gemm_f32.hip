@@ -590,31 +590,77 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
         }
     }
 
-    if (KS > 1) {
-        // groups 1 .. KS-1 hand their sums to group 0 (word e of lane l of
-        // wave wq of group g at float index ((g-1)*WPG + wq)*ACCW*64 + e*64 + l)
+    // The k-groups' sums meet in LDS.  With four or more k-groups (where KS
+    // divides a lane's accumulator words), group g finishes the g-th KS-th
+    // of them: every group writes the words the others finish, and after a
+    // barrier each adds, for its own words, all groups' values in group
+    // order and stores them, so every wave takes part in the hand-over and
+    // the stores (500 x 500 x 2000 13.7 -> 13.0 us, 1024^3 20.2 -> 19.8,
+    // 256^3 4.9 -> 4.35).  With two k-groups, where the other workgroup on
+    // the CU keeps the matrix cores busy meanwhile, group 1 hands its words
+    // to group 0, which adds them and stores the tile (split, the narrow
+    // tiles ran 1.5-2.5% slower and 1024 x 3072 x 768 NT 4%).  Either way
+    // each output is ((g0 + g1) + g2) + ..., fixed for a given KS.
+    constexpr bool SPLIT_OUT = KS >= 4 && ACCW % KS == 0;
+    constexpr int SW = SPLIT_OUT ? ACCW / KS : ACCW;   // words each group stores
+    if constexpr (KS > 1) {
         float *red = reinterpret_cast<float *>(smem);
         __syncthreads();                          // every stage read is done
-        if (grp > 0) {
-            float *dst = red + ((grp - 1) * WPG + wq) * ACCW * 64 + lane;
+        if constexpr (SPLIT_OUT) {
+            static_assert(KS * WPG * ACCW * 64 * 4 <= KS * 2 * STAGE,
+                          "the hand-over of partial sums must fit in the stages");
+            // word e of lane l of wave wq of group g at (g*WPG + wq)*ACCW*64 + e*64 + l
+            float *dst = red + (grp * WPG + wq) * ACCW * 64 + lane;
 #pragma unroll
             for (int i = 0; i < IB; ++i)
 #pragma unroll
                 for (int j = 0; j < JB; ++j)
 #pragma unroll
-                    for (int r = 0; r < AR; ++r) dst[((i * JB + j) * AR + r) * 64] = acc[i][j][r];
-        }
-        __syncthreads();
-        if (grp > 0) return;
-#pragma unroll
-        for (int g = 1; g < KS; ++g) {
-            const float *src = red + ((g - 1) * WPG + wq) * ACCW * 64 + lane;
+                    for (int r = 0; r < AR; ++r) {
+                        const int e = (i * JB + j) * AR + r;
+                        if (e / SW != grp) dst[e * 64] = acc[i][j][r];
+                    }
+            __syncthreads();
 #pragma unroll
             for (int i = 0; i < IB; ++i)
 #pragma unroll
                 for (int j = 0; j < JB; ++j)
 #pragma unroll
-                    for (int r = 0; r < AR; ++r) acc[i][j][r] += src[((i * JB + j) * AR + r) * 64];
+                    for (int r = 0; r < AR; ++r) {
+                        const int e = (i * JB + j) * AR + r;
+                        if (e / SW != grp) continue;
+                        float v = 0.f;
+#pragma unroll
+                        for (int g = 0; g < KS; ++g) {
+                            const float x =
+                                g == grp ? acc[i][j][r] : red[(g * WPG + wq) * ACCW * 64 + e * 64 + lane];
+                            v = g == 0 ? x : v + x;
+                        }
+                        acc[i][j][r] = v;
+                    }
+        } else {
+            // word e of lane l of wave wq of group g at ((g-1)*WPG + wq)*ACCW*64 + e*64 + l
+            if (grp > 0) {
+                float *dst = red + ((grp - 1) * WPG + wq) * ACCW * 64 + lane;
+#pragma unroll
+                for (int i = 0; i < IB; ++i)
+#pragma unroll
+                    for (int j = 0; j < JB; ++j)
+#pragma unroll
+                        for (int r = 0; r < AR; ++r) dst[((i * JB + j) * AR + r) * 64] = acc[i][j][r];
+            }
+            __syncthreads();
+            if (grp > 0) return;
+#pragma unroll
+            for (int g = 1; g < KS; ++g) {
+                const float *src = red + ((g - 1) * WPG + wq) * ACCW * 64 + lane;
+#pragma unroll
+                for (int i = 0; i < IB; ++i)
+#pragma unroll
+                    for (int j = 0; j < JB; ++j)
+#pragma unroll
+                        for (int r = 0; r < AR; ++r) acc[i][j][r] += src[((i * JB + j) * AR + r) * 64];
+            }
         }
     }
 
@@ -629,6 +675,7 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
             if (col >= N) continue;
 #pragma unroll
             for (int r = 0; r < AR; ++r) {
+                if (SPLIT_OUT && ((i * JB + j) * AR + r) / SW != grp) continue;
                 const int row = m0 + wm + MF * i +
                                 (MF == 32 ? 8 * (r >> 2) + 4 * h + (r & 3) : 4 * (lane >> 4) + r);
                 if (row < M) store_c(C + (int64_t)row * ldc + col, acc[i][j][r], alpha, beta);
