@@ -598,19 +598,24 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
         }
     }
 
-    // The k-groups' sums meet in LDS.  With four or more k-groups (where KS
-    // divides a lane's accumulator words), group g finishes the g-th KS-th
-    // of them: every group writes the words the others finish, and after a
+    // The k-groups' sums meet in LDS.  With four or more k-groups, group g
+    // finishes about a KS-th of a lane's accumulator words (split below):
+    // every group writes the words the others finish, and after a
     // barrier each adds, for its own words, all groups' values in group
     // order and stores them, so every wave takes part in the hand-over and
     // the stores (500 x 500 x 2000 13.7 -> 13.0 us, 1024^3 20.2 -> 19.8,
-    // 256^3 4.9 -> 4.35).  With two k-groups, where the other workgroup on
-    // the CU keeps the matrix cores busy meanwhile, group 1 hands its words
-    // to group 0, which adds them and stores the tile (split, the narrow
-    // tiles ran 1.5-2.5% slower and 1024 x 3072 x 768 NT 4%).  Either way
-    // each output is ((g0 + g1) + g2) + ..., fixed for a given KS.
-    constexpr bool SPLIT_OUT = KS >= 4 && ACCW % KS == 0;
-    constexpr int SW = SPLIT_OUT ? ACCW / KS : ACCW;   // words each group stores
+    // 256^3 4.9 -> 4.35; with 6 groups on narrow tiles 346 x 768 x 1536
+    // 16.9 -> 16.3, 400 x 1024 x 2048 20.8 -> 20.1).  With two k-groups,
+    // where the other workgroup on the CU keeps the matrix cores busy
+    // meanwhile, group 1 hands its words to group 0, which adds them and
+    // stores the tile (split, the narrow tiles ran 1.5-2.5% slower and
+    // 1024 x 3072 x 768 NT 4%).  Either way each output is
+    // ((g0 + g1) + g2) + ..., fixed for a given KS.
+    // Word e of a lane goes to group e * KS / ACCW: ACCW / KS words each,
+    // one more for some groups when KS does not divide ACCW (16 words over
+    // 6 groups: 3, 3, 2, 3, 3, 2).
+    constexpr bool SPLIT_OUT = KS >= 4 && ACCW >= KS;
+    const auto owner = [](int e) { return e * KS / ACCW; };
     if constexpr (KS > 1) {
         float *red = reinterpret_cast<float *>(smem);
         __syncthreads();                          // every stage read is done
@@ -626,7 +631,7 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
 #pragma unroll
                     for (int r = 0; r < AR; ++r) {
                         const int e = (i * JB + j) * AR + r;
-                        if (e / SW != grp) dst[e * 64] = acc[i][j][r];
+                        if (owner(e) != grp) dst[e * 64] = acc[i][j][r];
                     }
             __syncthreads();
 #pragma unroll
@@ -636,7 +641,7 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
 #pragma unroll
                     for (int r = 0; r < AR; ++r) {
                         const int e = (i * JB + j) * AR + r;
-                        if (e / SW != grp) continue;
+                        if (owner(e) != grp) continue;
                         float v = 0.f;
 #pragma unroll
                         for (int g = 0; g < KS; ++g) {
@@ -683,7 +688,7 @@ __global__ __launch_bounds__(64 * WPG * KS) void gemm_f32_direct(
             if (col >= N) continue;
 #pragma unroll
             for (int r = 0; r < AR; ++r) {
-                if (SPLIT_OUT && ((i * JB + j) * AR + r) / SW != grp) continue;
+                if (SPLIT_OUT && owner((i * JB + j) * AR + r) != grp) continue;
                 const int row = m0 + wm + MF * i +
                                 (MF == 32 ? 8 * (r >> 2) + 4 * h + (r & 3) : 4 * (lane >> 4) + r);
                 if (row < M) store_c(C + (int64_t)row * ldc + col, acc[i][j][r], alpha, beta);
@@ -803,11 +808,15 @@ hipError_t launch_gemm(bool ax, bool bx, int M, int N, int K, float alpha, const
     // less is taken, on a tie 64 x 32 when A is x-major (A . B, A . B^T)
     // and 32 x 64 otherwise.
     //  - Small grids (64 x 64 tiles for fewer than half the CUs): 32 x 32
-    //    tiles when those still fit one per CU, else narrow tiles, with the
-    //    k-slabs split over as many groups as the LDS holds: 8 for 32 x 32
-    //    (500 x 500 x 2000: 24.0 us with 64 x 32 tiles, 18.4 with 32 x 32 in
-    //    4 groups, 15.3 in 8) and 6 for narrow tiles (346 x 768 x 768: 11.8
-    //    us for 64 x 32 in 4 groups, 10.9 for 32 x 64 in 6).
+    //    tiles when those still fit one per CU, else narrow tiles.  The
+    //    k-slabs split over 8 groups for 32 x 32 tiles, as many as the LDS
+    //    holds (500 x 500 x 2000: 24.0 us with 64 x 32 tiles, 18.4 with
+    //    32 x 32 in 4 groups, 15.3 in 8; 4 groups ran 5-19% slower from 8
+    //    to 63 slabs).  Narrow tiles take 6 groups, which the LDS also
+    //    holds, from 40 slabs on and 4 below (346 x 768 x 768: 9.2 us in 4,
+    //    9.5 in 6; 346 x 768 x 1536 16.9 in 4, 16.3 in 6): with fewer
+    //    slabs per group, filling and draining each group's pipeline costs
+    //    more than the extra waves gain.
     //  - More tiles than CUs: narrow tiles when the share of 64 x 64 tiles
     //    is at least 1.2 times that of narrow ones in 64 x 64 units, i.e. a
     //    last round of 64 x 64 tiles that would leave most CUs idle.  On
@@ -834,7 +843,7 @@ hipError_t launch_gemm(bool ax, bool bx, int M, int N, int K, float alpha, const
     const int64_t tiles_48 = (int64_t)((M + 63) / 64) * ((N + 47) / 48);
     const bool t48 = !small && ks == 4 && tiles_48 <= (int64_t)num_cus && tiles_48 > tiles_64;
     const int ksq = slabs >= 8 ? 8 : (slabs >= 4 ? 4 : (slabs >= 2 ? 2 : 1));
-    const int ksh = !small ? ks : (slabs >= 12 ? 6 : (slabs >= 8 ? 4 : (slabs >= 4 ? 2 : 1)));
+    const int ksh = !small ? ks : (slabs >= 40 ? 6 : (slabs >= 8 ? 4 : (slabs >= 4 ? 2 : 1)));
 #define GG_ARGS M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s
 #define GG_GEMM_DIRECT(AX_, BX_)                                                     \
     if (K % 4 != 0 && (AX_ || BX_))                                                  \

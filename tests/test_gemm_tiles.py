@@ -60,7 +60,8 @@ CASES = [
     # narrow tiles on a small grid: 64 x 32 (500 rows) and 32 x 64 (348
     # rows) with 1, 2, 4 and 6 k-groups
     ("half", 500, 600, 100), ("half", 348, 772, 772), ("half", 500, 600, 300),
-    ("half", 500, 600, 60),
+    ("half", 500, 600, 60), ("half", 348, 772, 1540), ("half", 500, 600, 2020),
+    ("half", 348, 772, 1249), ("half", 500, 600, 1247),
     # narrow tiles on grids larger than the CUs, K tails in a slab
     ("half", 1000, 1212, 300), ("half", 1024, 1216, 60), ("half", 1280, 2044, 300),
 ]

@@ -43,7 +43,8 @@ SHAPES = [
     (130, 2, 7),         # K below one slab and below one chunk
     (1, 1, 3),           # one element
     (501, 610, 301),     # narrow tiles on a small grid, 4 k-groups
-    (349, 770, 771),     # narrow tiles on a small grid, 6 k-groups
+    (349, 770, 771),     # narrow tiles on a small grid, 4 k-groups
+    (349, 770, 1539),    # narrow tiles on a small grid, 6 k-groups
     (1023, 767, 1031),   # 64 x 64 tiles, 4 k-groups
     (2049, 2047, 131),   # 64 x 64 tiles, 2 k-groups
     (1025, 2301, 259),   # narrow tiles past the CU count
