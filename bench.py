@@ -34,7 +34,8 @@ the 2-bit GEMV's weight GB/s (codes + scales per product over its duration)
 for one product per launch and for a token's 40 products per launch, each
 with a roofline object; `q4_gemv`, `q2_gemv_transposed` and `gemv_f32` do the
 same for the 4-bit product, the transposed 1,536 x 12,288 shape and the fp32
-product.  `gemm_configs` checks and times the other GEMM configurations (the
+product (single calls and a token's 40 products per gemv_f32_batched
+launch).  `gemm_configs` checks and times the other GEMM configurations (the
 nine products of a GPT-2-small block, the 346 x 768 x 768 classifier layer,
 256^3).  `cpu_baseline` times the oracle on the host, on one core and on every
 usable core.  `context` holds reference points measured in the same run.  The
@@ -437,7 +438,8 @@ WEIGHTS_PER_DISPATCH = (
     ("gemv_packed_flat<2, 1, 1,", "", Q2_M * Q2_K),
     ("gemv_packed_flat<4, 2, 1,", "", Q2_M * Q2_K),
     ("gemv_packed_flat<4, 8, 64,", "", CALLS_PER_TOKEN * Q2_M * Q2_K),
-    ("gemv_f32_kernel<1, 6, true>", "", Q2_M * Q2_K),
+    ("gemv_f32_kernel<1, 6, true, 1>", "", Q2_M * Q2_K),
+    ("gemv_f32_kernel<1, 6, true, 64>", "", CALLS_PER_TOKEN * Q2_M * Q2_K),
 )
 N_SIMD = 1024                      # 256 CUs x 4 SIMDs
 N_XCD = 8                          # GRBM_GUI_ACTIVE is summed over the 8 XCDs
@@ -536,8 +538,11 @@ def write_traffic(fetch_db, write_db):
             (lambda n: n.startswith("gemv_packed_kernel<2, 256, 6,")
              and n.split(" @")[0].endswith(", 1>"),
              "traffic_gemv_q2_1536x12288.json", q2_srcs, QT_ALG_BYTES),
-            (lambda n: n.startswith("gemv_f32_kernel<1, 6, true>"),
-             "traffic_gemv_f32_12288x1536.json", ("gemv_f32.hip", "wave.hpp"), F32_ALG_BYTES)):
+            (lambda n: n.startswith("gemv_f32_kernel<1, 6, true, 1>"),
+             "traffic_gemv_f32_12288x1536.json", ("gemv_f32.hip", "wave.hpp"), F32_ALG_BYTES),
+            (lambda n: n.startswith("gemv_f32_kernel<1, 6, true, 64>"),
+             "traffic_gemv_f32_batched_12288x1536.json", ("gemv_f32.hip", "wave.hpp"),
+             CALLS_PER_TOKEN * F32_ALG_BYTES)):
         k = [n for n in fetch if match(n)]
         if not k:
             continue
@@ -574,7 +579,8 @@ def counters_run(torch, bd, inputs):
     eagerly, after one device-to-device copy of CALIBRATION_BYTES (the
     reference that scales rocprofv3's byte counters): 5 GEMMs at 2048^3, 128
     single 2-bit products and 4 batches of 40 over the 128-matrix set, the
-    same for 4-bit over its 64 matrices, and 48 fp32 GEMVs."""
+    same for 4-bit over its 64 matrices, and 48 fp32 GEMVs and 4 batches of
+    40 of them."""
     dev = torch.device("cuda:0")
     A, B = inputs.large_square(3)
     dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
@@ -610,6 +616,9 @@ def counters_run(torch, bd, inputs):
                     [dx] * CALLS_PER_TOKEN, ys=dys)
     for W in Wf:
         bd.gemv_f32(W, dxf, y=dy)
+    for t in range(4):
+        idx = [(t * CALLS_PER_TOKEN + c) % F32_ROTATION for c in range(CALLS_PER_TOKEN)]
+        bd.gemv_f32_batched([Wf[i] for i in idx], [dxf] * CALLS_PER_TOKEN, ys=dys)
     torch.cuda.synchronize()
     log("counters run done")
     return 0
@@ -776,13 +785,22 @@ def main():
     del qt_refs
 
     gf = torch.empty((F32_ROTATION, Q2_M), dtype=torch.float32, device=dev)
+    gfb = torch.full((F32_ROTATION, Q2_M), float("nan"), dtype=torch.float32, device=dev)
     for r in range(F32_ROTATION):
         bd.gemv_f32(Wf[r], dxf, y=gf[r])
-    gf = gf.cpu().numpy()
+    for b0 in range(0, F32_ROTATION, CALLS_PER_TOKEN):
+        idx = range(b0, min(F32_ROTATION, b0 + CALLS_PER_TOKEN))
+        bd.gemv_f32_batched([Wf[r] for r in idx], [dxf] * len(idx), ys=[gfb[r] for r in idx])
+    gf, gfb = gf.cpu().numpy(), gfb.cpu().numpy()
+    # each batched product runs the single call's arithmetic: equal bit for bit
+    gfb_ok = bool(np.array_equal(gfb, gf))
+    if not gfb_ok:
+        log("parity FAIL: gemv_f32_batched differs from gemv_f32")
     with ThreadPoolExecutor(max_workers=usable_cores()) as pool:
         gf_refs = list(pool.map(lambda r: oracle.gemv(inputs.gemv_f32_weight(r), xf),
                                 range(F32_ROTATION)))
     gf_ok, gf_worst = check_set(gf, gf_refs, "gemv_f32")
+    gfb_ok = gfb_ok and gf_ok
     del gf_refs
     parity = {
         "gemm_f32_2048": "pass" if gemm_ok else "FAIL", "gemm_worst_err_over_bound": gemm_worst,
@@ -794,16 +812,18 @@ def main():
         "gemv_q2_transposed_batched": "pass" if qtb_ok else "FAIL",
         "gemv_q2_transposed_batched_worst": qtb_worst,
         "gemv_f32": "pass" if gf_ok else "FAIL", "gemv_f32_worst": gf_worst,
+        "gemv_f32_batched": "pass" if gfb_ok else "FAIL",
         "note": ("worst |gpu - oracle| / sum|a*b| per element (bound 1e-4); the packed and "
                  "fp32 GEMVs on every matrix of their rotation sets, through the single and "
-                 "the batched entry points; the 2048^3 GEMM on 512 sampled cells"),
+                 "the batched entry points (the fp32 batch must also equal the single calls "
+                 "bit for bit); the 2048^3 GEMM on 512 sampled cells"),
     }
     log("parity in %.1f s: gemm %.3g, q2 %.3g, q2 batched %.3g, q4 %.3g, q4 batched %.3g, "
         "q2 transposed %.3g / %.3g, gemv_f32 %.3g (x 1e-4 bound)" %
         (time.perf_counter() - t0, gemm_worst / 1e-4, q2_worst / 1e-4, qb_worst / 1e-4,
          q4_worst / 1e-4, q4b_worst / 1e-4, qt_worst / 1e-4, qtb_worst / 1e-4,
          gf_worst / 1e-4))
-    del q2s, q2b, q4s, q4b, qts, qtb, gf
+    del q2s, q2b, q4s, q4b, qts, qtb, gf, gfb
 
     if args.copy_calibration > 0:
         n = args.copy_calibration // 4
@@ -917,7 +937,11 @@ def main():
             ("gemv_q2_transposed", singles(bd.gemv_q2, QTd, STd, dxt, dyt, Q2_ROTATION),
              WIN_SINGLE),
             ("gemv_f32", lambda: [bd.gemv_f32(Wf[n % F32_ROTATION], dxf, y=dy)
-                                  for n in range(WIN_SINGLE[0])], WIN_SINGLE)):
+                                  for n in range(WIN_SINGLE[0])], WIN_SINGLE),
+            ("gemv_f32_batched",
+             lambda: [bd.gemv_f32_batched([Wf[i] for i in tok_idx(t, F32_ROTATION)],
+                                          [dxf] * CALLS_PER_TOKEN, ys=dys)
+                      for t in range(N_TOK)], WIN_BATCHED)):
         g = capture(mk)
         win[name] = window(g, *gw)
         del g
@@ -966,6 +990,8 @@ def main():
     qt_traffic = traffic_from_profile("traffic_gemv_q2_1536x12288.json", psha)
     gf_traffic = traffic_from_profile("traffic_gemv_f32_12288x1536.json",
                                       src_sha("gemv_f32.hip", "wave.hpp"))
+    gfb_traffic = traffic_from_profile("traffic_gemv_f32_batched_12288x1536.json",
+                                       src_sha("gemv_f32.hip", "wave.hpp"))
     per_prod_note = "HBM bytes per product (launch total / 40)"
 
     cpu = None
@@ -974,11 +1000,11 @@ def main():
         cpu = cpu_baseline(A, B, Q0, S0, x)
 
     all_ok = (gemm_ok and q2_ok and qb_ok and q4_ok and q4b_ok and qt_ok and qtb_ok and gf_ok
-              and configs_ok)
+              and gfb_ok and configs_ok)
     qb_us, q2_us = per_product["gemv_q2_batched"], per_product["gemv_q2"]
     q4b_us, q4_us = per_product["gemv_q4_batched"], per_product["gemv_q4"]
     qtb_us, qt_us = per_product["gemv_q2_transposed_batched"], per_product["gemv_q2_transposed"]
-    gf_us = per_product["gemv_f32"]
+    gf_us, gfb_us = per_product["gemv_f32"], per_product["gemv_f32_batched"]
     out = {
         "metric": "fp32 GEMM TFLOP/s at 2048^3; 2-bit GEMV weight GB/s at 12288x1536",
         "value": gemm_tflops if gemm_ok else None,
@@ -1079,6 +1105,17 @@ def main():
             "unit": "GB/s",
             "avg_launch_us": gf_us,
             "roofline": roofline("gemv_f32 (12288x1536)", F32_ALG_BYTES, gf_us, gf_traffic),
+            "batched": {
+                "metric": ("the same, one token's 40 products in one gemv_f32_batched launch"),
+                "value": F32_ALG_BYTES / gfb_us / 1e3 if gfb_ok else None,
+                "unit": "GB/s",
+                "us_per_gemv": gfb_us,
+                "us_per_token": win["gemv_f32_batched"]["mean_us"],
+                "roofline": roofline("gemv_f32_batched (40 x 12288x1536 per launch)",
+                                     F32_ALG_BYTES, gfb_us,
+                                     gfb_traffic / CALLS_PER_TOKEN if gfb_traffic else None,
+                                     per_prod_note),
+            },
         },
         "windows": win,
         "gemm_configs": configs,
@@ -1127,6 +1164,7 @@ def main():
                       "parity": ok_s(q2_ok)},
         "q4_batched_frac": round(Q4_ALG_BYTES / q4b_us / 1e3 / PEAK_HBM_GBS, 3),
         "gemv_f32_frac": round(F32_ALG_BYTES / gf_us / 1e3 / PEAK_HBM_GBS, 3),
+        "gemv_f32_batched_frac": round(F32_ALG_BYTES / gfb_us / 1e3 / PEAK_HBM_GBS, 3),
         "gpt2_block_frac": round(configs.get("gpt2_block_9_products", {})
                                  .get("frac_of_fp32_mfma_peak", float("nan")), 3),
         "parity_all": ok_s(all_ok),

@@ -26,8 +26,9 @@ GG_ERR_ALIAS = -2
 GG_ERR_NO_DEVICE = -3
 GG_ERR_LAUNCH = -4
 
-ENTRY_POINTS = ("gemm_f32", "gemm_f32_tn", "gemm_f32_nt", "gemm_f32_ex", "gemv_f32", "gemv_q2",
-                "gemv_q2_batched", "gemv_q4", "gemv_q4_batched", "gg_strerror")
+ENTRY_POINTS = ("gemm_f32", "gemm_f32_tn", "gemm_f32_nt", "gemm_f32_ex", "gemv_f32",
+                "gemv_f32_batched", "gemv_q2", "gemv_q2_batched", "gemv_q4", "gemv_q4_batched",
+                "gg_strerror")
 
 _lib = None
 
@@ -70,6 +71,8 @@ def load(path: str = LIB_PATH):
     lib.gemv_f32.argtypes = [i64, i64, vp, i64, vp, vp, vp]
     lib.gemv_f32.restype = ctypes.c_int
     pp = ctypes.POINTER(ctypes.c_void_p)
+    lib.gemv_f32_batched.argtypes = [i64, i64, i64, pp, i64, pp, pp, vp]
+    lib.gemv_f32_batched.restype = ctypes.c_int
     for name in ("gemv_q2", "gemv_q4"):
         f = getattr(lib, name)
         f.argtypes = [i64, i64, vp, i64, vp, i64, vp, vp, vp]
@@ -218,6 +221,36 @@ def gemv_f32(W, x, y=None, stream=None):
     _check(load().gemv_f32(M, K, pw, ldw, _vec(x, torch.float32, "x"),
                            _vec(y, torch.float32, "y"), _stream(stream)), "gemv_f32")
     return y
+
+
+def gemv_f32_batched(Ws, xs, ys=None, stream=None):
+    """y_b = W_b.x_b for every b: lists of W (fp32 M x K, one shape and
+    leading dimension for all) and x (K,) fp32.  Returns the list of
+    outputs."""
+    torch = _torch()
+    n = len(Ws)
+    if len(xs) != n:
+        raise ValueError("Ws and xs must have the same length")
+    if n == 0:
+        return []
+    M, K = Ws[0].shape
+    if ys is None:
+        ys = [torch.empty(M, dtype=torch.float32, device=Ws[0].device) for _ in range(n)]
+    wp, xp, yp, ldw = [], [], [], None
+    for W, x, y in zip(Ws, xs, ys):
+        if tuple(W.shape) != (M, K) or x.shape != (K,) or y.shape != (M,):
+            raise ValueError("every product must have the same M and K")
+        pw, lw = _mat(W, torch.float32, "W")
+        if ldw is None:
+            ldw = lw
+        elif lw != ldw:
+            raise ValueError("every W must have the same leading dimension")
+        wp.append(pw)
+        xp.append(_vec(x, torch.float32, "x"))
+        yp.append(_vec(y, torch.float32, "y"))
+    _check(load().gemv_f32_batched(n, M, K, _ptr_array(wp), ldw, _ptr_array(xp),
+                                   _ptr_array(yp), _stream(stream)), "gemv_f32_batched")
+    return ys
 
 
 def _packed(name, Q, S, x, y, stream):

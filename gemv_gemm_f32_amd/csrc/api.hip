@@ -80,6 +80,60 @@ bool bad_ptr(const void *p, int64_t align) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? GG_OK : GG_ERR_LAUNCH; }
 
+// The byte range of one operand of a batch, and whether it is an output.
+struct Iv {
+    Span s;
+    bool out;
+};
+
+// True when every output is disjoint from every input and from every other
+// output (inputs may overlap each other, e.g. a shared x).  Sorted sweep: an
+// interval overlaps an earlier one exactly when its start lies below the
+// largest end seen so far.
+bool outputs_disjoint(std::vector<Iv> &iv) {
+    std::sort(iv.begin(), iv.end(), [](const Iv &a, const Iv &b) { return a.s.lo < b.s.lo; });
+    uintptr_t end_all = 0, end_out = 0;
+    for (const Iv &v : iv) {
+        if (v.s.lo >= v.s.hi) continue;
+        if (v.out ? end_all > v.s.lo : end_out > v.s.lo) return false;
+        end_all = end_all > v.s.hi ? end_all : v.s.hi;
+        if (v.out) end_out = end_out > v.s.hi ? end_out : v.s.hi;
+    }
+    return true;
+}
+
+// The checks and launch shared by gemv_f32 and gemv_f32_batched.
+int f32_batched(int64_t count, int64_t M, int64_t K, const float *const *W, int64_t ldw,
+                const float *const *x, float *const *y, gg_stream_t stream) {
+    if (count < 0 || count > kMaxDim || M < 0 || K < 0 || M > kMaxDim || K > kMaxDim)
+        return GG_ERR_INVALID_ARG;
+    if (count == 0 || M == 0) return GG_OK;
+    if (W == nullptr || x == nullptr || y == nullptr) return GG_ERR_INVALID_ARG;
+    if (K > 0 && (ldw < K || ldw > kMaxDim)) return GG_ERR_INVALID_ARG;
+    for (int64_t b = 0; b < count; ++b) {
+        if (bad_ptr(y[b], 4) || wraps(y[b], 1, M, M, 4)) return GG_ERR_INVALID_ARG;
+        if (K > 0 && (bad_ptr(W[b], 4) || bad_ptr(x[b], 4) || wraps(W[b], M, K, ldw, 4) ||
+                      wraps(x[b], 1, K, K, 4)))
+            return GG_ERR_INVALID_ARG;
+    }
+    if (K > 0 || count > 1) {
+        std::vector<Iv> iv;
+        iv.reserve((size_t)count * 3);
+        for (int64_t b = 0; b < count; ++b) {
+            iv.push_back({span(y[b], 1, M, M, 4), true});
+            if (K > 0) {
+                iv.push_back({span(W[b], M, K, ldw, 4), false});
+                iv.push_back({span(x[b], 1, K, K, 4), false});
+            }
+        }
+        if (!outputs_disjoint(iv)) return GG_ERR_ALIAS;
+    }
+    int cus = 0;
+    if (int st = check_device(&cus)) return st;
+    return launch_status(gg::launch_gemv_f32((int)count, (int)M, (int)K, W, ldw, x, y,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
 // op(A) = A^T when ta (A stored K x M), op(B) = B^T when tb (B stored N x K).
 int gemm_common(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha, const float *A,
                 int64_t lda, const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
@@ -142,18 +196,13 @@ int gemv_f32(int64_t M, int64_t K, const float *W, int64_t ldw, const float *x, 
              gg_stream_t stream) {
     if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim) return GG_ERR_INVALID_ARG;
     if (M == 0) return GG_OK;
-    if (bad_ptr(y, 4)) return GG_ERR_INVALID_ARG;
-    if (K > 0 && (bad_ptr(W, 4) || bad_ptr(x, 4))) return GG_ERR_INVALID_ARG;
-    if (K > 0 && (ldw < K || ldw > kMaxDim)) return GG_ERR_INVALID_ARG;
-    if (wraps(y, 1, M, M, 4) || (K > 0 && (wraps(W, M, K, ldw, 4) || wraps(x, 1, K, K, 4))))
-        return GG_ERR_INVALID_ARG;
-    const Span ys = span(y, 1, M, M, 4);
-    if (K > 0 && (overlaps(ys, span(W, M, K, ldw, 4)) || overlaps(ys, span(x, 1, K, K, 4))))
-        return GG_ERR_ALIAS;
-    int cus = 0;
-    if (int st = check_device(&cus)) return st;
-    return launch_status(gg::launch_gemv_f32((int)M, (int)K, W, ldw, x, y,
-                                             reinterpret_cast<hipStream_t>(stream)));
+    // one product of the batched entry point (same checks, same kernel)
+    return f32_batched(1, M, K, &W, ldw, &x, &y, stream);
+}
+
+int gemv_f32_batched(int64_t count, int64_t M, int64_t K, const float *const *W, int64_t ldw,
+                     const float *const *x, float *const *y, gg_stream_t stream) {
+    return f32_batched(count, M, K, W, ldw, x, y, stream);
 }
 
 }  // extern "C"
@@ -180,11 +229,8 @@ int packed_batched(int bits, int64_t count, int64_t M, int64_t K, const uint8_t 
             return GG_ERR_INVALID_ARG;
     }
     // Every output must be disjoint from every input and from every other
-    // output, across the whole batch (inputs may overlap each other, e.g. a
-    // shared x).  Sorted sweep: an interval overlaps an earlier one exactly
-    // when its start lies below the largest end seen so far.
+    // output, across the whole batch.
     if (K > 0 || count > 1) {
-        struct Iv { Span s; bool out; };
         std::vector<Iv> iv;
         iv.reserve((size_t)count * 4);
         for (int64_t b = 0; b < count; ++b) {
@@ -195,14 +241,7 @@ int packed_batched(int bits, int64_t count, int64_t M, int64_t K, const uint8_t 
                 iv.push_back({span(x[b], 1, K, K, 4), false});
             }
         }
-        std::sort(iv.begin(), iv.end(), [](const Iv &a, const Iv &b) { return a.s.lo < b.s.lo; });
-        uintptr_t end_all = 0, end_out = 0;
-        for (const Iv &v : iv) {
-            if (v.s.lo >= v.s.hi) continue;
-            if (v.out ? end_all > v.s.lo : end_out > v.s.lo) return GG_ERR_ALIAS;
-            end_all = end_all > v.s.hi ? end_all : v.s.hi;
-            if (v.out) end_out = end_out > v.s.hi ? end_out : v.s.hi;
-        }
+        if (!outputs_disjoint(iv)) return GG_ERR_ALIAS;
     }
     int cus = 0;
     if (int st = check_device(&cus)) return st;

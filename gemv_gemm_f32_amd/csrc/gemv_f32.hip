@@ -22,6 +22,11 @@
 //    lane 0 writes y.
 //  * Scalar-load specialisation of the same kernel for K, ldw or a base that
 //    is not a multiple of 4 floats.
+//  * Batches: the same kernel runs up to 64 products of one shape per launch,
+//    blockIdx.y picking the product, whose W, x and y pointers travel in the
+//    kernel arguments.  The page counts 40 of these products per generated
+//    token; one launch each pays the fixed dispatch cost 40 times.  Every
+//    product's arithmetic is the single call's, so the two agree bit for bit.
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
@@ -35,10 +40,22 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int THREADS = 256;
 constexpr int WAVES = THREADS / 64;
 
-template <int R, int U, bool VEC>
-__global__ __launch_bounds__(THREADS) void gemv_f32_kernel(
-    int M, int K, const float *__restrict__ W, int64_t ldw,
-    const float *__restrict__ x, float *__restrict__ y) {
+// The pointers of NB products (kernel arguments; entries past the launch's
+// product count repeat product 0 and are never used).
+template <int NB>
+struct F32Ptrs {
+    const float *W[NB];
+    const float *x[NB];
+    float *y[NB];
+};
+
+template <int R, int U, bool VEC, int NB>
+__global__ __launch_bounds__(THREADS) void gemv_f32_kernel(int M, int K, int64_t ldw,
+                                                           F32Ptrs<NB> p) {
+    const int b = NB == 1 ? 0 : (int)blockIdx.y;
+    const float *__restrict__ W = p.W[b];
+    const float *__restrict__ x = p.x[b];
+    float *__restrict__ y = p.y[b];
     const int lane = threadIdx.x & 63;
     const int row0 = (blockIdx.x * WAVES + (threadIdx.x >> 6)) * R;
     if (row0 >= M) return;   // uniform per wave
@@ -123,18 +140,37 @@ __global__ __launch_bounds__(THREADS) void gemv_f32_kernel(
     }
 }
 
-}  // namespace
-
-hipError_t launch_gemv_f32(int M, int K, const float *W, int64_t ldw, const float *x,
-                           float *y, hipStream_t s) {
+template <int NB>
+hipError_t launch_f32(int count, int M, int K, const float *const *W, int64_t ldw,
+                      const float *const *x, float *const *y, hipStream_t s) {
     constexpr int R = 1;
     const int waves = (M + R - 1) / R;
-    const int nwg = (waves + WAVES - 1) / WAVES;
-    const bool vec = (reinterpret_cast<uintptr_t>(W) % 16 == 0) &&
-                     (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (ldw % 4 == 0) &&
-                     (K % 4 == 0);
-    if (vec) return launch(gemv_f32_kernel<R, 6, true>, dim3(nwg), dim3(THREADS), s, M, K, W, ldw, x, y);
-    return launch(gemv_f32_kernel<R, 8, false>, dim3(nwg), dim3(THREADS), s, M, K, W, ldw, x, y);
+    const dim3 grid((waves + WAVES - 1) / WAVES, count);
+    F32Ptrs<NB> p;
+    bool vec = ldw % 4 == 0 && K % 4 == 0;
+    for (int b = 0; b < NB; ++b) {
+        const int i = b < count ? b : 0;
+        p.W[b] = W[i];
+        p.x[b] = x[i];
+        p.y[b] = y[i];
+        vec = vec && reinterpret_cast<uintptr_t>(W[i]) % 16 == 0 &&
+              reinterpret_cast<uintptr_t>(x[i]) % 16 == 0;
+    }
+    if (vec) return launch(gemv_f32_kernel<R, 6, true, NB>, grid, dim3(THREADS), s, M, K, ldw, p);
+    return launch(gemv_f32_kernel<R, 8, false, NB>, grid, dim3(THREADS), s, M, K, ldw, p);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_f32(int count, int M, int K, const float *const *W, int64_t ldw,
+                           const float *const *x, float *const *y, hipStream_t s) {
+    if (count == 1) return launch_f32<1>(1, M, K, W, ldw, x, y, s);
+    for (int b0 = 0; b0 < count; b0 += F32_MAX_BATCH) {
+        const int n = count - b0 < F32_MAX_BATCH ? count - b0 : F32_MAX_BATCH;
+        const hipError_t e = launch_f32<F32_MAX_BATCH>(n, M, K, W + b0, ldw, x + b0, y + b0, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace gg

@@ -40,9 +40,12 @@ hipError_t launch_gemm(bool ax, bool bx, int M, int N, int K, float alpha, const
                        int64_t lda, const float *B, int64_t ldb, float beta, float *C,
                        int64_t ldc, int num_cus, hipStream_t stream);
 
-// y = W.x, fp32.
-hipError_t launch_gemv_f32(int M, int K, const float *W, int64_t ldw,
-                           const float *x, float *y, hipStream_t stream);
+// y_b = W_b.x_b for b < count, fp32; the pointer arrays are host arrays of
+// device pointers.  More than F32_MAX_BATCH products take several launches
+// in order; if one of them is rejected the earlier ones stay queued.
+constexpr int F32_MAX_BATCH = 64;
+hipError_t launch_gemv_f32(int count, int M, int K, const float *const *W, int64_t ldw,
+                           const float *const *x, float *const *y, hipStream_t stream);
 
 // y_b = W_b.x_b for b < count, W_b as 2-bit (q2) or 4-bit (q4) codes with
 // one binary16 scale per 64 columns; the pointer arrays are host arrays of

@@ -143,6 +143,26 @@ int gemv_f32(int64_t M, int64_t K, const float *W, int64_t ldw,
              const float *x, float *y, gg_stream_t stream);
 
 /*
+ * y_b = W_b . x_b for b = 0 .. count-1: count independent fp32 products of
+ * one shape (M, K, ldw), each exactly as gemv_f32 defines it, in as few
+ * launches as possible (up to 64 products per launch).  "Kernel 0112",
+ * section "What is being measured", counts 40 matrix-vector products per
+ * generated token; one launch per product pays a fixed dispatch cost each
+ * time.
+ *   W, x, y: HOST arrays of count DEVICE pointers (W[b], x[b], y[b] as in
+ *   gemv_f32).  The arrays are read during the call and not kept.
+ *   Every y[b] must be disjoint from every input and from every other y[c]
+ *   (else GG_ERR_ALIAS); inputs may be shared (for example one x for all).
+ *   Products 64 at a time share a launch, in order; GG_ERR_LAUNCH from a
+ *   batch of more than 64 may leave the products of earlier launches queued.
+ * Each product runs gemv_f32's arithmetic, so a batch equals count separate
+ * gemv_f32 calls bit for bit.
+ */
+int gemv_f32_batched(int64_t count, int64_t M, int64_t K,
+                     const float *const *W, int64_t ldw,
+                     const float *const *x, float *const *y, gg_stream_t stream);
+
+/*
  * y[M] = W[M x K] . x[K] with W held as 2-bit codes and binary16 scales.
  *
  * The 2-bit weight matrix times an input vector of "Kernel 0112", sections

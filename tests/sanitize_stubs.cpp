@@ -13,7 +13,8 @@ hipError_t launch_gemm(bool, bool, int, int, int, float, const float *, int64_t,
     return hipErrorNotSupported;
 }
 
-hipError_t launch_gemv_f32(int, int, const float *, int64_t, const float *, float *, hipStream_t) {
+hipError_t launch_gemv_f32(int, int, int, const float *const *, int64_t, const float *const *,
+                           float *const *, hipStream_t) {
     return hipErrorNotSupported;
 }
 

@@ -241,3 +241,26 @@ def test_gemv_q2_batched_validation():
     # y[0] overlaps the shared x
     assert f(2, 4, 64, Q, 16, S, 1, x, _parr(PX + 4, PC), None) == bd.GG_ERR_ALIAS
     passes_checks(lambda: f(2, 4, 64, Q, 16, S, 1, x, y, None))
+
+
+def test_gemv_f32_batched_validation():
+    f = lib.gemv_f32_batched
+    W = _parr(PA, PA + 0x100000)
+    x = _parr(PX, PX)                    # a shared x is allowed
+    y = _parr(PC, PC + 0x100000)
+    assert f(-1, 4, 64, W, 64, x, y, None) == bd.GG_ERR_INVALID_ARG
+    assert f(0, 4, 64, None, 64, None, None, None) == bd.GG_OK
+    assert f(2, 0, 64, W, 64, x, y, None) == bd.GG_OK
+    assert f(2, 4, 64, None, 64, x, y, None) == bd.GG_ERR_INVALID_ARG
+    assert f(2, 4, 64, W, 63, x, y, None) == bd.GG_ERR_INVALID_ARG
+    assert f(2, 4, 64, _parr(PA, PA + 2), 64, x, y, None) == bd.GG_ERR_INVALID_ARG
+    assert f(2, 4, 64, W, 64, x, _parr(PC, PC + 2), None) == bd.GG_ERR_INVALID_ARG
+    # y[1] overlaps y[0]
+    assert f(2, 4, 64, W, 64, x, _parr(PC, PC + 8), None) == bd.GG_ERR_ALIAS
+    # y[1] overlaps W of product 0
+    assert f(2, 4, 64, W, 64, x, _parr(PC, PA + 64), None) == bd.GG_ERR_ALIAS
+    # y[0] overlaps the shared x
+    assert f(2, 4, 64, W, 64, x, _parr(PX + 4, PC), None) == bd.GG_ERR_ALIAS
+    passes_checks(lambda: f(2, 4, 64, W, 64, x, y, None))
+    # K = 0 reads no input: null W and x pass, only the outputs are checked
+    passes_checks(lambda: f(2, 4, 0, _parr(0, 0), 0, _parr(0, 0), y, None))

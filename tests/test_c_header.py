@@ -69,6 +69,18 @@ int main(void) {
                "negative count");
     }
     {
+        const float *ws[2] = {A, B};
+        const float *xs[2] = {x, x};
+        float *ys[2] = {y, (float *)A};
+        expect(gemv_f32_batched(2, 8, 8, ws, 7, xs, ys, s), GG_ERR_INVALID_ARG,
+               "ldw < K in an fp32 batch");
+        expect(gemv_f32_batched(2, 8, 8, ws, 8, xs, ys, s), GG_ERR_ALIAS,
+               "an fp32 batch output on another product's W");
+        expect(gemv_f32_batched(2, 8, 8, NULL, 8, xs, ys, s), GG_ERR_INVALID_ARG,
+               "null W array");
+        expect(gemv_f32_batched(0, 8, 8, NULL, 8, NULL, NULL, s), GG_OK, "empty fp32 batch");
+    }
+    {
         const int codes[] = {GG_OK, GG_ERR_INVALID_ARG, GG_ERR_ALIAS, GG_ERR_NO_DEVICE,
                              GG_ERR_LAUNCH, 12345};
         for (unsigned i = 0; i < sizeof codes / sizeof codes[0]; ++i) {

@@ -101,3 +101,75 @@ def test_k_zero_writes_zeros():
     y = t.full((40,), 3.0, dtype=t.float32, device="cuda")
     bd.gemv_f32(W, x, y=y)
     assert np.all(host(y) == 0)
+
+
+def _batch_vs_single(Ws, xs):
+    """gemv_f32_batched over the products against one gemv_f32 call each:
+    equal bit for bit, and each within the oracle's bound."""
+    t = torch()
+    dW = [dev(W) for W in Ws]
+    dx = [dev(x) for x in xs]
+    n, M = len(Ws), Ws[0].shape[0]
+    ys = [host(bd.gemv_f32(w, x)) for w, x in zip(dW, dx)]
+    buf, yv = guarded(n, M)
+    bd.gemv_f32_batched(dW, dx, ys=[yv[b] for b in range(n)])
+    yb = host(yv)
+    assert canaries_intact(buf)
+    for b in range(n):
+        assert np.array_equal(yb[b], ys[b]), "product %d of %d" % (b, n)
+    for b in sorted({0, n // 2, n - 1}):
+        ref, bound = oracle.gemv(Ws[b], xs[b])
+        assert_close(yb[b], ref, bound, "batched product %d of %d" % (b, n))
+
+
+@pytest.mark.parametrize("n", [1, 2, 40, 64, 65, 130])
+def test_batched_equals_single_calls(n):
+    M, K = 300, 1536
+    Ws = [inputs.normal(RNG, (M, K), 0.02) for _ in range(n)]
+    x = inputs.normal(RNG, (K,))
+    _batch_vs_single(Ws, [x] * n)
+
+
+@pytest.mark.parametrize("M,K", [(1, 1), (17, 257), (129, 1535), (250, 1538), (7, 5000),
+                                 (1000, 61), (4100, 1536)])
+def test_batched_ragged_shapes_distinct_x(M, K):
+    n = 5
+    Ws = [inputs.normal(RNG, (M, K)) for _ in range(n)]
+    xs = [inputs.normal(RNG, (K,)) for _ in range(n)]
+    _batch_vs_single(Ws, xs)
+
+
+def test_batched_integer_inputs_bitwise():
+    M, K, n = 333, 1536, 6
+    Ws = [inputs.integers(RNG, (M, K)) for _ in range(n)]
+    x = inputs.integers(RNG, (K,))
+    ys = bd.gemv_f32_batched([dev(W) for W in Ws], [dev(x)] * n)
+    for W, y in zip(Ws, ys):
+        ref, _ = oracle.gemv(W, x)
+        assert np.array_equal(host(y).astype(np.float64), ref)
+
+
+def test_batched_padded_and_misaligned_rows():
+    M, K, n = 200, 1536, 4
+    Ws = [inputs.normal(RNG, (M, K)) for _ in range(n)]
+    x = inputs.normal(RNG, (K,))
+    for off, ld in ((0, K + 12), (1, K + 1)):
+        dW = []
+        for W in Ws:
+            Wp = np.zeros((M, ld), np.float32)
+            Wp[:, off:off + K] = W
+            dW.append(dev(Wp)[:, off:off + K])
+        ys = bd.gemv_f32_batched(dW, [dev(x)] * n)
+        for W, y in zip(Ws, ys):
+            ref, bound = oracle.gemv(W, x)
+            assert_close(host(y), ref, bound, "offset %d, ldw %d" % (off, ld))
+
+
+def test_batched_k_zero_writes_zeros():
+    t = torch()
+    W = t.empty((40, 0), dtype=t.float32, device="cuda")
+    x = t.empty((0,), dtype=t.float32, device="cuda")
+    ys = [t.full((40,), 3.0, dtype=t.float32, device="cuda") for _ in range(3)]
+    bd.gemv_f32_batched([W] * 3, [x] * 3, ys=ys)
+    for y in ys:
+        assert np.all(host(y) == 0)

@@ -1,8 +1,8 @@
 """GPU check that the entry points can be captured in a HIP graph and
 replayed: they allocate nothing, clear nothing with memsets and keep no state
 between calls, so a replay must redo exactly what an eager call does.  One
-graph holds the GEMM (plain, TN, NT and accumulating), the fp32 GEMV and the
-single and batched 2-bit and 4-bit GEMVs.  It is replayed five times, with
+graph holds the GEMM (plain, TN, NT and accumulating), the single and batched
+fp32 GEMV and the single and batched 2-bit and 4-bit GEMVs.  It is replayed five times, with
 eager library calls and torch work on the same buffers' neighbours in
 between, and after every replay each output is compared bit for bit with
 eager calls.  The accumulating product (beta = 1) grows by one term per
@@ -43,7 +43,8 @@ def test_capture_and_replay():
         return {"nn": t.empty((520, 330), **f32), "tn": t.empty((520, 330), **f32),
                 "nt": t.empty((520, 330), **f32), "gemv": t.empty(2000, **f32),
                 "q2": t.empty(3000, **f32), "q4": t.empty(3000, **f32),
-                "q2b": [t.empty(3000, **f32) for _ in range(3)]}
+                "q2b": [t.empty(3000, **f32) for _ in range(3)],
+                "gemvb": [t.empty(2000, **f32) for _ in range(2)]}
 
     def run(o, acc, stream):
         bd.gemm_f32(A, B, o["nn"], stream=stream)
@@ -55,6 +56,7 @@ def test_capture_and_replay():
         bd.gemv_q4(*q4, o["q4"], stream=stream)
         bd.gemv_q2_batched([q[0] for q in q2], [q[1] for q in q2], [q[2] for q in q2],
                            o["q2b"], stream=stream)
+        bd.gemv_f32_batched([W, W], [xv, xv], o["gemvb"], stream=stream)
 
     def flat(o):
         return [host(v) for k in sorted(o) for v in (o[k] if isinstance(o[k], list) else [o[k]])]

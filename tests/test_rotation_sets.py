@@ -1,8 +1,9 @@
 """Every matrix of every rotation set the benchmark streams, element by element
 against the oracle: the 128 2-bit matrices at 12,288 x 1,536 and at the
 transposed 1,536 x 12,288, the 64 4-bit matrices and the 48 fp32 matrices,
-each through the single-product entry point and (packed) through batched
-launches of up to 64 products.  The oracle runs on all host cores."""
+each through the single-product entry point and through batched launches of
+up to 64 products (the fp32 batch must equal the single calls bit for bit).
+The oracle runs on all host cores."""
 import os
 from concurrent.futures import ThreadPoolExecutor
 
@@ -68,12 +69,16 @@ def test_f32_set():
     dx = t.from_numpy(x).cuda()
     n = inputs.GEMV_F32_ROTATION
     y = t.empty((n, inputs.GEMV_M), dtype=t.float32, device="cuda")
+    yb = t.full((n, inputs.GEMV_M), float("nan"), dtype=t.float32, device="cuda")
+    Ws = []
     for r in range(n):
-        W = t.from_numpy(inputs.gemv_f32_weight(r)).cuda()
-        bd.gemv_f32(W, dx, y=y[r])
-        del W
+        Ws.append(t.from_numpy(inputs.gemv_f32_weight(r)).cuda())
+        bd.gemv_f32(Ws[r], dx, y=y[r])
+    bd.gemv_f32_batched(Ws, [dx] * n, ys=[yb[r] for r in range(n)])
     t.cuda.synchronize()
-    y = y.cpu().numpy()
+    del Ws
+    y, yb = y.cpu().numpy(), yb.cpu().numpy()
+    assert np.array_equal(yb, y), "fp32 batch differs from single calls"
     refs = _refs(lambda r: oracle.gemv(inputs.gemv_f32_weight(r), x), n)
     for r in range(n):
         assert_close(y[r], refs[r][0], refs[r][1], "fp32 matrix %d" % r)

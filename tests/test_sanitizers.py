@@ -50,7 +50,9 @@ EXTRA_CALLS = r"""
         static const uint16_t *ss[NB];
         static const float *xs[NB];
         static float *ys[NB];
+        static const float *ws[NB];
         for (int b = 0; b < NB; ++b) {
+            ws[b] = A + (size_t)b * 256;
             qs[b] = Q + (size_t)b * 4096;
             ss[b] = (const uint16_t *)((const char *)S + (size_t)b * 4096);
             xs[b] = x;
@@ -66,7 +68,11 @@ EXTRA_CALLS = r"""
         if (st != GG_ERR_NO_DEVICE && st != GG_ERR_LAUNCH) { printf("FAIL valid q2 %d\n", st); ++failures; }
         st = gemv_q2_batched(NB, 16, 1536, qs, 384, ss, 24, xs, ys, s);
         if (st != GG_ERR_NO_DEVICE && st != GG_ERR_LAUNCH) { printf("FAIL valid batch %d\n", st); ++failures; }
+        st = gemv_f32_batched(NB, 16, 16, ws, 16, xs, ys, s);
+        if (st != GG_ERR_NO_DEVICE && st != GG_ERR_LAUNCH) { printf("FAIL valid f32 batch %d\n", st); ++failures; }
         ys[NB - 1] = ys[3];
+        expect(gemv_f32_batched(NB, 16, 16, ws, 16, xs, ys, s), GG_ERR_ALIAS,
+               "two outputs of an fp32 batch overlap");
         expect(gemv_q4_batched(NB, 16, 1536, qs, 768, ss, 24, xs, ys, s), GG_ERR_ALIAS,
                "two outputs of a batch overlap");
     }
