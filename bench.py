@@ -33,9 +33,9 @@ launch over its mean launch duration).  `q2_gemv` and `q2_gemv_batched` give
 the 2-bit GEMV's weight GB/s (codes + scales per product over its duration)
 for one product per launch and for a token's 40 products per launch, each
 with a roofline object; `q4_gemv`, `q2_gemv_transposed` and `gemv_f32` do the
-same for the 4-bit product, the transposed 1,536 x 12,288 shape and the fp32
-product (single calls and a token's 40 products per gemv_f32_batched
-launch).  `gemm_configs` checks and times the other GEMM configurations (the
+same for the 4-bit product, the transposed 1,536 x 12,288 shape (batches
+also through gemv_q2_batched_ws, rows cut into slices) and the fp32 product
+(single calls and a token's 40 products per gemv_f32_batched launch).  `gemm_configs` checks and times the other GEMM configurations (the
 nine products of a GPT-2-small block, the 346 x 768 x 768 classifier layer,
 256^3).  `cpu_baseline` times the oracle on the host, on one core and on every
 usable core.  `context` holds reference points measured in the same run.  The
@@ -434,7 +434,8 @@ def _median_per_kernel(per):
 # Weights per dispatch of the GEMV kernels at the bench's shapes, for counts
 # per weight: (kernel-name prefix, whole name suffix, weights per dispatch).
 WEIGHTS_PER_DISPATCH = (
-    ("gemv_q2_idot<3,", ", 64>", CALLS_PER_TOKEN * Q2_M * Q2_K),
+    ("gemv_q2_idot<3,", ", 64, false>", CALLS_PER_TOKEN * Q2_M * Q2_K),
+    ("gemv_q2_idot<3,", ", 64, true>", CALLS_PER_TOKEN * QT_M * QT_K),
     ("gemv_packed_flat<2, 1, 1,", "", Q2_M * Q2_K),
     ("gemv_packed_flat<4, 2, 1,", "", Q2_M * Q2_K),
     ("gemv_packed_flat<4, 8, 64,", "", CALLS_PER_TOKEN * Q2_M * Q2_K),
@@ -527,7 +528,7 @@ def write_traffic(fetch_db, write_db):
              "traffic_gemm_f32_2048.json", ("gemm_f32.hip",), 3 * 4 * GEMM_N * GEMM_N),
             (lambda n: n.startswith("gemv_packed_flat<2, 1, 1,"),
              "traffic_gemv_q2_12288x1536.json", q2_srcs, Q2_ALG_BYTES),
-            (lambda n: n.startswith("gemv_q2_idot<3,") and n.split(" @")[0].endswith(", 64>"),
+            (lambda n: n.startswith("gemv_q2_idot<3,") and n.split(" @")[0].endswith(", 64, false>"),
              "traffic_gemv_q2_batched_12288x1536.json", q2_srcs,
              CALLS_PER_TOKEN * Q2_ALG_BYTES),
             (lambda n: n.startswith("gemv_packed_flat<4, 2, 1,"),
@@ -711,6 +712,11 @@ def main():
     dyt = torch.empty(QT_M, dtype=torch.float32, device=dev)
     dys = [torch.empty(Q2_M, dtype=torch.float32, device=dev) for _ in range(CALLS_PER_TOKEN)]
     dyts = [torch.empty(QT_M, dtype=torch.float32, device=dev) for _ in range(CALLS_PER_TOKEN)]
+    # the workspace of the transposed shape's sliced batches (64 products)
+    wst = torch.empty(bd.gemv_q2_batched_ws_size(64, QT_M, QT_K), dtype=torch.uint8, device=dev)
+
+    def q2_ws(Qs, Ss, xs, ys=None, stream=None):
+        return bd.gemv_q2_batched_ws(Qs, Ss, xs, ys=ys, workspace=wst, stream=stream)
     torch.cuda.synchronize()
     hashes = {"gemm_A_B": inputs.sha256(A, B)[:16], "q2_x": inputs.sha256(x)[:16],
               "q2_set": hq, "q4_set": h4, "q2_transposed_set": ht,
@@ -774,6 +780,7 @@ def main():
     del q4_refs
 
     qts, qtb = packed_outputs(bd.gemv_q2, bd.gemv_q2_batched, QTd, STd, dxt, QT_M)
+    _, qtw = packed_outputs(bd.gemv_q2, q2_ws, QTd, STd, dxt, QT_M)
 
     def qt_ref(r):
         Q, S = inputs.q2_weight(r, QT_M, QT_K)
@@ -782,6 +789,7 @@ def main():
         qt_refs = list(pool.map(qt_ref, range(Q2_ROTATION)))
     qt_ok, qt_worst = check_set(qts, qt_refs, "gemv_q2 1536x12288")
     qtb_ok, qtb_worst = check_set(qtb, qt_refs, "gemv_q2_batched 1536x12288")
+    qtw_ok, qtw_worst = check_set(qtw, qt_refs, "gemv_q2_batched_ws 1536x12288")
     del qt_refs
 
     gf = torch.empty((F32_ROTATION, Q2_M), dtype=torch.float32, device=dev)
@@ -811,6 +819,8 @@ def main():
         "gemv_q2_transposed": "pass" if qt_ok else "FAIL", "gemv_q2_transposed_worst": qt_worst,
         "gemv_q2_transposed_batched": "pass" if qtb_ok else "FAIL",
         "gemv_q2_transposed_batched_worst": qtb_worst,
+        "gemv_q2_transposed_batched_ws": "pass" if qtw_ok else "FAIL",
+        "gemv_q2_transposed_batched_ws_worst": qtw_worst,
         "gemv_f32": "pass" if gf_ok else "FAIL", "gemv_f32_worst": gf_worst,
         "gemv_f32_batched": "pass" if gfb_ok else "FAIL",
         "note": ("worst |gpu - oracle| / sum|a*b| per element (bound 1e-4); the packed and "
@@ -823,7 +833,7 @@ def main():
         (time.perf_counter() - t0, gemm_worst / 1e-4, q2_worst / 1e-4, qb_worst / 1e-4,
          q4_worst / 1e-4, q4b_worst / 1e-4, qt_worst / 1e-4, qtb_worst / 1e-4,
          gf_worst / 1e-4))
-    del q2s, q2b, q4s, q4b, qts, qtb, gf, gfb
+    del q2s, q2b, q4s, q4b, qts, qtb, qtw, gf, gfb
 
     if args.copy_calibration > 0:
         n = args.copy_calibration // 4
@@ -936,6 +946,8 @@ def main():
              batches(bd.gemv_q2_batched, QTd, STd, dxt, dyts, Q2_ROTATION), WIN_BATCHED),
             ("gemv_q2_transposed", singles(bd.gemv_q2, QTd, STd, dxt, dyt, Q2_ROTATION),
              WIN_SINGLE),
+            ("gemv_q2_transposed_batched_ws",
+             batches(q2_ws, QTd, STd, dxt, dyts, Q2_ROTATION), WIN_BATCHED),
             ("gemv_f32", lambda: [bd.gemv_f32(Wf[n % F32_ROTATION], dxf, y=dy)
                                   for n in range(WIN_SINGLE[0])], WIN_SINGLE),
             ("gemv_f32_batched",
@@ -947,7 +959,7 @@ def main():
         del g
         log("%-28s mean %.3f us, median %.3f us per launch" %
             (name, win[name]["mean_us"], win[name]["median_us"]))
-    per_product = {k: (win[k]["mean_us"] / CALLS_PER_TOKEN if k.endswith("_batched")
+    per_product = {k: (win[k]["mean_us"] / CALLS_PER_TOKEN if "_batched" in k
                        else win[k]["mean_us"]) for k in win}
 
     # ---- context, after the main timing
@@ -999,11 +1011,12 @@ def main():
         Q0, S0 = inputs.q2_weight(0)
         cpu = cpu_baseline(A, B, Q0, S0, x)
 
-    all_ok = (gemm_ok and q2_ok and qb_ok and q4_ok and q4b_ok and qt_ok and qtb_ok and gf_ok
-              and gfb_ok and configs_ok)
+    all_ok = (gemm_ok and q2_ok and qb_ok and q4_ok and q4b_ok and qt_ok and qtb_ok and qtw_ok
+              and gf_ok and gfb_ok and configs_ok)
     qb_us, q2_us = per_product["gemv_q2_batched"], per_product["gemv_q2"]
     q4b_us, q4_us = per_product["gemv_q4_batched"], per_product["gemv_q4"]
     qtb_us, qt_us = per_product["gemv_q2_transposed_batched"], per_product["gemv_q2_transposed"]
+    qtw_us = per_product["gemv_q2_transposed_batched_ws"]
     gf_us, gfb_us = per_product["gemv_f32"], per_product["gemv_f32_batched"]
     out = {
         "metric": "fp32 GEMM TFLOP/s at 2048^3; 2-bit GEMV weight GB/s at 12288x1536",
@@ -1098,6 +1111,15 @@ def main():
                 "us_per_gemv": qtb_us,
                 "frac": QT_ALG_BYTES / qtb_us / 1e3 / PEAK_HBM_GBS,
             },
+            "batched_ws": {
+                "metric": ("the same, a token's 40 products per gemv_q2_batched_ws launch: "
+                           "rows cut into 8 slices of 1,536 columns, partial sums in a "
+                           "workspace, added by a second kernel (both timed)"),
+                "value": Q2_WEIGHT_BYTES / qtw_us / 1e3 if qtw_ok else None,
+                "unit": "GB/s",
+                "us_per_gemv": qtw_us,
+                "frac": QT_ALG_BYTES / qtw_us / 1e3 / PEAK_HBM_GBS,
+            },
         },
         "gemv_f32": {
             "metric": "fp32 GEMV GB/s at 12288x1536 (cold rotation over 48 matrices, 3.375 GiB)",
@@ -1165,6 +1187,8 @@ def main():
         "q4_batched_frac": round(Q4_ALG_BYTES / q4b_us / 1e3 / PEAK_HBM_GBS, 3),
         "gemv_f32_frac": round(F32_ALG_BYTES / gf_us / 1e3 / PEAK_HBM_GBS, 3),
         "gemv_f32_batched_frac": round(F32_ALG_BYTES / gfb_us / 1e3 / PEAK_HBM_GBS, 3),
+        "q2_transposed_batched_frac": round(QT_ALG_BYTES / min(qtb_us, qtw_us) / 1e3
+                                            / PEAK_HBM_GBS, 3),
         "gpt2_block_frac": round(configs.get("gpt2_block_9_products", {})
                                  .get("frac_of_fp32_mfma_peak", float("nan")), 3),
         "parity_all": ok_s(all_ok),

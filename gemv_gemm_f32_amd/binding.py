@@ -27,8 +27,8 @@ GG_ERR_NO_DEVICE = -3
 GG_ERR_LAUNCH = -4
 
 ENTRY_POINTS = ("gemm_f32", "gemm_f32_tn", "gemm_f32_nt", "gemm_f32_ex", "gemv_f32",
-                "gemv_f32_batched", "gemv_q2", "gemv_q2_batched", "gemv_q4", "gemv_q4_batched",
-                "gg_strerror")
+                "gemv_f32_batched", "gemv_q2", "gemv_q2_batched", "gemv_q2_batched_ws",
+                "gemv_q2_batched_ws_size", "gemv_q4", "gemv_q4_batched", "gg_strerror")
 
 _lib = None
 
@@ -80,6 +80,10 @@ def load(path: str = LIB_PATH):
         f = getattr(lib, name + "_batched")
         f.argtypes = [i64, i64, i64, pp, i64, pp, i64, pp, pp, vp]
         f.restype = ctypes.c_int
+    lib.gemv_q2_batched_ws.argtypes = [i64, i64, i64, pp, i64, pp, i64, pp, pp, vp, i64, vp]
+    lib.gemv_q2_batched_ws.restype = ctypes.c_int
+    lib.gemv_q2_batched_ws_size.argtypes = [i64, i64, i64]
+    lib.gemv_q2_batched_ws_size.restype = i64
     lib.gg_strerror.argtypes = [ctypes.c_int]
     lib.gg_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -293,7 +297,7 @@ def _ptr_array(ptrs):
     return arr
 
 
-def _packed_batched(name, Qs, Ss, xs, ys, stream):
+def _packed_batched(name, Qs, Ss, xs, ys, stream, ws=None):
     torch = _torch()
     n = len(Qs)
     if len(Ss) != n or len(xs) != n:
@@ -319,8 +323,12 @@ def _packed_batched(name, Qs, Ss, xs, ys, stream):
         sp.append(ps)
         xp.append(_vec(x, torch.float32, "x"))
         yp.append(_vec(y, torch.float32, "y"))
-    _check(getattr(load(), name)(n, M, K, _ptr_array(qp), ldq, _ptr_array(sp), lds,
-                                 _ptr_array(xp), _ptr_array(yp), _stream(stream)), name)
+    args = [n, M, K, _ptr_array(qp), ldq, _ptr_array(sp), lds, _ptr_array(xp), _ptr_array(yp)]
+    if ws is not None:
+        if ws.numel() and (ws.device.type != "cuda" or not ws.is_contiguous()):
+            raise ValueError("the workspace must be a contiguous GPU tensor")
+        args += [ws.data_ptr() if ws.numel() else None, ws.numel() * ws.element_size()]
+    _check(getattr(load(), name)(*args, _stream(stream)), name)
     return ys
 
 
@@ -329,6 +337,25 @@ def gemv_q2_batched(Qs, Ss, xs, ys=None, stream=None):
     (float16/int16 M x >= ceil(K/64)), x (K,) fp32; all Q share one shape and
     leading dimension, as do all S.  Returns the list of outputs."""
     return _packed_batched("gemv_q2_batched", Qs, Ss, xs, ys, stream)
+
+
+def gemv_q2_batched_ws_size(count, M, K):
+    """Bytes of workspace gemv_q2_batched_ws needs for count products of M x K."""
+    n = load().gemv_q2_batched_ws_size(count, M, K)
+    if n < 0:
+        raise GGError(n, "gemv_q2_batched_ws_size")
+    return n
+
+
+def gemv_q2_batched_ws(Qs, Ss, xs, ys=None, workspace=None, stream=None):
+    """gemv_q2_batched with a workspace (a contiguous GPU tensor of at least
+    gemv_q2_batched_ws_size bytes; allocated here as uint8 when None)."""
+    torch = _torch()
+    if workspace is None:
+        n = gemv_q2_batched_ws_size(len(Qs), Qs[0].shape[0] if Qs else 0,
+                                    xs[0].shape[0] if xs else 0)
+        workspace = torch.empty(n, dtype=torch.uint8, device=Qs[0].device if Qs else "cuda")
+    return _packed_batched("gemv_q2_batched_ws", Qs, Ss, xs, ys, stream, ws=workspace)
 
 
 def gemv_q4_batched(Qs, Ss, xs, ys=None, stream=None):

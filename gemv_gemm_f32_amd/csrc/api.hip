@@ -209,10 +209,18 @@ int gemv_f32_batched(int64_t count, int64_t M, int64_t K, const float *const *W,
 
 namespace {
 
-// The checks and launch shared by the 2-bit and 4-bit entry points.
+// A caller's workspace, or none.
+struct Workspace {
+    void *p;
+    int64_t bytes;
+};
+
+// The checks and launch shared by the 2-bit and 4-bit entry points.  With a
+// workspace (2-bit only) a batch of long rows may cut them into slices whose
+// partial sums go there.
 int packed_batched(int bits, int64_t count, int64_t M, int64_t K, const uint8_t *const *Q,
                    int64_t ldq, const uint16_t *const *S, int64_t lds, const float *const *x,
-                   float *const *y, gg_stream_t stream) {
+                   float *const *y, const Workspace *ws, gg_stream_t stream) {
     if (count < 0 || count > kMaxDim || M < 0 || K < 0 || M > kMaxDim || K > kMaxDim)
         return GG_ERR_INVALID_ARG;
     if (count == 0 || M == 0) return GG_OK;
@@ -228,11 +236,18 @@ int packed_batched(int bits, int64_t count, int64_t M, int64_t K, const uint8_t 
                       wraps(x[b], 1, K, K, 4)))
             return GG_ERR_INVALID_ARG;
     }
+    // The workspace this batch uses, if any: 16-byte aligned, large enough,
+    // and written like an output.
+    const int64_t ws_floats = (ws && bits == 2) ? gg::gemv_q2_workspace_floats(count, M, K) : 0;
+    if (ws_floats > 0) {
+        if (ws->bytes < ws_floats * 4 || bad_ptr(ws->p, 16) || wraps(ws->p, 1, ws_floats, ws_floats, 4))
+            return GG_ERR_INVALID_ARG;
+    }
     // Every output must be disjoint from every input and from every other
     // output, across the whole batch.
-    if (K > 0 || count > 1) {
+    if (K > 0 || count > 1 || ws_floats > 0) {
         std::vector<Iv> iv;
-        iv.reserve((size_t)count * 4);
+        iv.reserve((size_t)count * 4 + 1);
         for (int64_t b = 0; b < count; ++b) {
             iv.push_back({span(y[b], 1, M, M, 4), true});
             if (K > 0) {
@@ -241,13 +256,15 @@ int packed_batched(int bits, int64_t count, int64_t M, int64_t K, const uint8_t 
                 iv.push_back({span(x[b], 1, K, K, 4), false});
             }
         }
+        if (ws_floats > 0) iv.push_back({span(ws->p, 1, ws_floats, ws_floats, 4), true});
         if (!outputs_disjoint(iv)) return GG_ERR_ALIAS;
     }
     int cus = 0;
     if (int st = check_device(&cus)) return st;
     const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    float *wsp = ws_floats > 0 ? static_cast<float *>(ws->p) : nullptr;
     return launch_status(bits == 2 ? gg::launch_gemv_q2((int)count, (int)M, (int)K, Q, ldq, S,
-                                                        lds, x, y, hs)
+                                                        lds, x, y, wsp, hs)
                                    : gg::launch_gemv_q4((int)count, (int)M, (int)K, Q, ldq, S,
                                                         lds, x, y, hs));
 }
@@ -259,7 +276,21 @@ extern "C" {
 int gemv_q2_batched(int64_t count, int64_t M, int64_t K, const uint8_t *const *Q, int64_t ldq,
                     const uint16_t *const *S, int64_t lds, const float *const *x,
                     float *const *y, gg_stream_t stream) {
-    return packed_batched(2, count, M, K, Q, ldq, S, lds, x, y, stream);
+    return packed_batched(2, count, M, K, Q, ldq, S, lds, x, y, nullptr, stream);
+}
+
+int64_t gemv_q2_batched_ws_size(int64_t count, int64_t M, int64_t K) {
+    if (count < 0 || count > kMaxDim || M < 0 || K < 0 || M > kMaxDim || K > kMaxDim)
+        return GG_ERR_INVALID_ARG;
+    return 4 * gg::gemv_q2_workspace_floats(count, M, K);
+}
+
+int gemv_q2_batched_ws(int64_t count, int64_t M, int64_t K, const uint8_t *const *Q,
+                       int64_t ldq, const uint16_t *const *S, int64_t lds, const float *const *x,
+                       float *const *y, void *workspace, int64_t workspace_bytes,
+                       gg_stream_t stream) {
+    const Workspace ws{workspace, workspace_bytes};
+    return packed_batched(2, count, M, K, Q, ldq, S, lds, x, y, &ws, stream);
 }
 
 int gemv_q2(int64_t M, int64_t K, const uint8_t *Q, int64_t ldq, const uint16_t *S,
@@ -267,20 +298,20 @@ int gemv_q2(int64_t M, int64_t K, const uint8_t *Q, int64_t ldq, const uint16_t 
     if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim) return GG_ERR_INVALID_ARG;
     if (M == 0) return GG_OK;
     // one product of the batched entry point (same checks, same kernel)
-    return packed_batched(2, 1, M, K, &Q, ldq, &S, lds, &x, &y, stream);
+    return packed_batched(2, 1, M, K, &Q, ldq, &S, lds, &x, &y, nullptr, stream);
 }
 
 int gemv_q4_batched(int64_t count, int64_t M, int64_t K, const uint8_t *const *Q, int64_t ldq,
                     const uint16_t *const *S, int64_t lds, const float *const *x,
                     float *const *y, gg_stream_t stream) {
-    return packed_batched(4, count, M, K, Q, ldq, S, lds, x, y, stream);
+    return packed_batched(4, count, M, K, Q, ldq, S, lds, x, y, nullptr, stream);
 }
 
 int gemv_q4(int64_t M, int64_t K, const uint8_t *Q, int64_t ldq, const uint16_t *S,
             int64_t lds, const float *x, float *y, gg_stream_t stream) {
     if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim) return GG_ERR_INVALID_ARG;
     if (M == 0) return GG_OK;
-    return packed_batched(4, 1, M, K, &Q, ldq, &S, lds, &x, &y, stream);
+    return packed_batched(4, 1, M, K, &Q, ldq, &S, lds, &x, &y, nullptr, stream);
 }
 
 const char *gg_strerror(int status) {

@@ -744,6 +744,17 @@ hipError_t launch_chunk(int count, int M, int K, const uint8_t *const *Q, int64_
 //    through LDS, instead of one 2-byte load per lane and step.
 //  * Reduction.  The row's partial sums meet in LDS after one barrier and one
 //    lane per row adds them in a fixed pairwise tree: deterministic.
+//  * Slices.  Rows longer than 48 chunks (the transposed 12,288 -> 1,536
+//    shape) are cut into slices of 1,536 columns, each slice of each row
+//    block a workgroup of its own (blockIdx.z; the workgroups of a slice,
+//    which share its x, are dispatched together: interleaving the slices of
+//    each row block ran 5% slower).  The kernel then reads the slice's
+//    codes, scales and x from offsets of z slices and
+//    writes its partial row sums, block z of M values per product, to a
+//    workspace; gemv_slices_sum adds a row's partials in slice order.  A
+//    slice is exactly the 24-chunk row the kernel is tuned for, with three
+//    waves per workgroup, and the workgroups of all slices of all products
+//    of a batch run in one launch.
 
 template <int WAVES, int T>
 struct IdotSmem {
@@ -832,10 +843,11 @@ struct IdotLoads {
 };
 
 // WAVES waves per workgroup (the row has 8 * WAVES chunks), T steps of 8
-// rows, NB products per pointer block.
+// rows, NB products per pointer block; SLICED: rows cut into slices
+// (blockIdx.z), partial sums out.
 constexpr int IDOT_WAVES_PER_SIMD = 4;   // occupancy asked for in a batch
 
-template <int WAVES, int T, int NB>
+template <int WAVES, int T, int NB, bool SLICED = false>
 __global__ __launch_bounds__(64 * WAVES)
 __attribute__((amdgpu_waves_per_eu(NB == 1 ? 1 : IDOT_WAVES_PER_SIMD)))
 void gemv_q2_idot(int M, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
@@ -846,6 +858,7 @@ void gemv_q2_idot(int M, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
     __shared__ __attribute__((aligned(16))) Sm sm;
 
     const int b = NB == 1 ? 0 : (int)blockIdx.y;
+    const int z = SLICED ? (int)blockIdx.z : 0;    // column slice
     const int w = (int)threadIdx.x >> 6, l = (int)threadIdx.x & 63;
     const int cl = l & 7, j = l >> 3, c = 8 * w + cl, u = j >> 1;
     const unsigned odd = 0u - (unsigned)(j & 1);   // all ones for the odd-column lanes
@@ -857,13 +870,15 @@ void gemv_q2_idot(int M, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
     // issued as soon as a slot frees up.
     v4f xr[4];
     {
-        const v4f *xp = reinterpret_cast<const v4f *>(ptrs.x[b] + 64 * c + 16 * u);
+        const v4f *xp =
+            reinterpret_cast<const v4f *>(ptrs.x[b] + (size_t)z * (64 * CPR) + 64 * c + 16 * u);
 #pragma unroll
         for (int q = 0; q < 4; ++q) xr[q] = xp[q];
     }
     __builtin_amdgcn_sched_barrier(0);
     IdotLoads ld;
-    ld.init(ptrs.Q[b], ptrs.S[b], M, row0, CPR, ldq, lds, w, l, j, c);
+    ld.init(ptrs.Q[b] + (size_t)z * (16 * CPR), ptrs.S[b] + (size_t)z * CPR, M, row0, CPR, ldq,
+            lds, w, l, j, c);
     u4 sraw[SL];
 #pragma unroll
     for (int q = 0; q < SL; ++q) sraw[q] = ld.scales(64 * q + l < ROWS ? 64 * q + l : -1);
@@ -1031,7 +1046,7 @@ void gemv_q2_idot(int M, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
     bool nan_out = false;
 #pragma unroll
     for (int q = 0; q < WAVES; ++q) nan_out = nan_out || sm.bad[q] != 0;
-    float *__restrict__ y = ptrs.y[b] + row0;
+    float *__restrict__ y = ptrs.y[b] + (size_t)z * M + row0;
     for (int r = (int)threadIdx.x; r < ROWS; r += 64 * WAVES) {
         if (row0 + r >= M) break;
         const float sum = Flat<2>::template row_sum<CPR / 4>(sm.part + r * PS);
@@ -1083,6 +1098,65 @@ hipError_t launch_idot(int waves, int count, int M, const uint8_t *const *Q, int
     }
 }
 
+// The row sums of sliced rows: y_b[r] = sum over slices s, in slice order,
+// of part[(b * slices + s) * M + r].
+template <int NB>
+struct OutPtrs {
+    float *y[NB];
+};
+
+template <int NB>
+__global__ __launch_bounds__(256) void gemv_slices_sum(int M, int slices,
+                                                       const float *__restrict__ part,
+                                                       OutPtrs<NB> out) {
+    const int b = (int)blockIdx.y;
+    const int r = (int)blockIdx.x * 256 + (int)threadIdx.x;
+    if (r >= M) return;
+    const float *p = part + (size_t)b * slices * M + r;
+    float v = p[0];
+    for (int q = 1; q < slices; ++q) v += p[(size_t)q * M];
+    out.y[b][r] = v;
+}
+
+// Slices per row for this batch (sliced_count), or 0 where the integer-dot
+// kernel's conditions fail on a slice: 16-byte aligned code rows, scale rows
+// (lds a multiple of 8) and x, byte offsets within 31 bits.
+inline int sliced_slices(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
+                         const uint16_t *const *S, int64_t lds, const float *const *x) {
+    const int n = (int)sliced_count(count, M, K);
+    if (n == 0 || ldq % 16 != 0 || lds % 8 != 0) return 0;
+    if ((int64_t)M * ldq >= (int64_t(1) << 31) || (int64_t)M * lds * 2 >= (int64_t(1) << 31))
+        return 0;
+    for (int i = 0; i < count; ++i)
+        if (reinterpret_cast<uintptr_t>(Q[i]) % 16 != 0 ||
+            reinterpret_cast<uintptr_t>(S[i]) % 16 != 0 ||
+            reinterpret_cast<uintptr_t>(x[i]) % 16 != 0)
+            return 0;
+    return n;
+}
+
+// count <= PACKED_MAX_BATCH products, part holding count * slices * M floats.
+hipError_t launch_sliced(int slices, int count, int M, const uint8_t *const *Q, int64_t ldq,
+                         const uint16_t *const *S, int64_t lds, const float *const *x,
+                         float *const *y, float *part, hipStream_t s) {
+    constexpr int NB = PACKED_MAX_BATCH, T = IDOT_BATCH_T, W = SLICE_K / 512;
+    PackedPtrs<NB> p;
+    OutPtrs<NB> o;
+    for (int b = 0; b < NB; ++b) {
+        const int i = b < count ? b : 0;
+        p.Q[b] = Q[i];
+        p.S[b] = S[i];
+        p.x[b] = x[i];
+        p.y[b] = part + (size_t)i * slices * M;
+        o.y[b] = y[i];
+    }
+    const dim3 grid((M + 8 * T - 1) / (8 * T), count, slices);
+    hipError_t e = launch(gemv_q2_idot<W, T, NB, true>, grid, dim3(64 * W), s, M, ldq, lds, p);
+    if (e != hipSuccess) return e;
+    return launch(gemv_slices_sum<NB>, dim3((M + 255) / 256, count), dim3(256), s, M, slices,
+                  (const float *)part, o);
+}
+
 // Rows split 32 ways unless the rows are long and few: at K >= 6,144 (each
 // of 256 lanes then holds at least one live unit per pass in two of its
 // three slots) with fewer rows than 32-way groups of one product would need
@@ -1107,7 +1181,21 @@ hipError_t launch_split(int count, int M, int K, const uint8_t *const *Q, int64_
 template <int BITS>
 hipError_t launch_batch(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
                         const uint16_t *const *S, int64_t lds, const float *const *x,
-                        float *const *y, hipStream_t s) {
+                        float *const *y, float *ws, hipStream_t s) {
+    if (BITS == 2 && ws != nullptr) {
+        const int slices = sliced_slices(count, M, K, Q, ldq, S, lds, x);
+        if (slices) {
+            // the workspace holds one launch's partial sums and is reused by
+            // the next launch, which the stream orders after the sums
+            for (int b0 = 0; b0 < count; b0 += PACKED_MAX_BATCH) {
+                const int n = count - b0 < PACKED_MAX_BATCH ? count - b0 : PACKED_MAX_BATCH;
+                const hipError_t e = launch_sliced(slices, n, M, Q + b0, ldq, S + b0, lds, x + b0,
+                                                   y + b0, ws, s);
+                if (e != hipSuccess) return e;
+            }
+            return hipSuccess;
+        }
+    }
     if (count == 1) return launch_split<BITS, 1>(1, M, K, Q, ldq, S, lds, x, y, s);
     // Up to PACKED_MAX_BATCH products per launch (their pointers travel in
     // the kernel arguments); larger batches take several launches in order.
@@ -1124,14 +1212,14 @@ hipError_t launch_batch(int count, int M, int K, const uint8_t *const *Q, int64_
 
 hipError_t launch_gemv_q2(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
                           const uint16_t *const *S, int64_t lds, const float *const *x,
-                          float *const *y, hipStream_t s) {
-    return launch_batch<2>(count, M, K, Q, ldq, S, lds, x, y, s);
+                          float *const *y, float *ws, hipStream_t s) {
+    return launch_batch<2>(count, M, K, Q, ldq, S, lds, x, y, ws, s);
 }
 
 hipError_t launch_gemv_q4(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
                           const uint16_t *const *S, int64_t lds, const float *const *x,
                           float *const *y, hipStream_t s) {
-    return launch_batch<4>(count, M, K, Q, ldq, S, lds, x, y, s);
+    return launch_batch<4>(count, M, K, Q, ldq, S, lds, x, y, nullptr, s);
 }
 
 }  // namespace gg

@@ -53,9 +53,36 @@ hipError_t launch_gemv_f32(int count, int M, int K, const float *const *W, int64
 // launches in order; if one of them is rejected the earlier ones stay
 // queued.
 constexpr int PACKED_MAX_BATCH = 64;
+// ws: NULL, or a workspace of gemv_q2_workspace_floats(count, M, K) floats
+// that batches of long rows use for partial sums (rows cut into slices);
+// without it they take a kernel that needs none.
 hipError_t launch_gemv_q2(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
                           const uint16_t *const *S, int64_t lds, const float *const *x,
-                          float *const *y, hipStream_t stream);
+                          float *const *y, float *ws, hipStream_t stream);
+// Batches of 2-bit products whose rows are long cut them into slices of
+// SLICE_K columns, each written to the workspace as partial row sums, when
+// a workspace is given: rows of 4 to SLICED_MAX slices, at least
+// SLICED_MIN_COUNT products (at 1,536 x 12,288, 8 products ran 8% slower
+// sliced than whole, 16 the same, 40 15% faster).  Slices of
+// SLICE_K/512 waves each, as the integer-dot kernel is tuned for.
+constexpr int SLICE_K = 1536;
+constexpr int SLICED_MIN_COUNT = 16;
+constexpr int SLICED_MAX = 1024;
+
+// Slices per row for a batch of this shape, 0 where it is not cut.
+inline int64_t sliced_count(int64_t count, int64_t M, int64_t K) {
+    if (count < SLICED_MIN_COUNT || M < 1 || K % SLICE_K != 0) return 0;
+    const int64_t n = K / SLICE_K;
+    return n >= 4 && n <= SLICED_MAX ? n : 0;
+}
+
+// Floats of workspace a 2-bit batch of this shape uses, 0 if none: one
+// launch's partial sums (the next launch of a batch over PACKED_MAX_BATCH
+// products reuses them).
+inline int64_t gemv_q2_workspace_floats(int64_t count, int64_t M, int64_t K) {
+    const int64_t n = sliced_count(count, M, K);
+    return n ? (count < PACKED_MAX_BATCH ? count : PACKED_MAX_BATCH) * n * M : 0;
+}
 hipError_t launch_gemv_q4(int count, int M, int K, const uint8_t *const *Q, int64_t ldq,
                           const uint16_t *const *S, int64_t lds, const float *const *x,
                           float *const *y, hipStream_t stream);

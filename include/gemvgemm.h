@@ -211,6 +211,41 @@ int gemv_q2_batched(int64_t count, int64_t M, int64_t K,
                     const float *const *x, float *const *y, gg_stream_t stream);
 
 /*
+ * gemv_q2_batched with a caller-owned device workspace, for batches whose
+ * rows are long: "Kernel 0112", section "What is being measured", names the
+ * same 2-bit product on the transposed shape (12,288 inputs -> 1,536
+ * outputs), and section "What the kernel costs in a whole token" shows such
+ * long rows need a deeper split than short ones.  With the workspace, a
+ * batch of at least 16 products whose K is a multiple of 1,536 and at least
+ * 6,144 cuts each row into K/1,536 slices handled by separate workgroups,
+ * writes their partial row sums to the workspace, and adds each row's
+ * partials in slice order (deterministic).  Other batches run exactly as
+ * gemv_q2_batched and do not touch the workspace.
+ *   workspace: DEVICE memory of at least gemv_q2_batched_ws_size(count, M,
+ *   K) bytes, 16-byte aligned, disjoint from every input and output (else
+ *   GG_ERR_INVALID_ARG, or GG_ERR_ALIAS for an overlap); it may be NULL
+ *   when that size is 0.  Its contents on entry do not matter and on return
+ *   are unspecified; it must not be used by other work until this call's
+ *   work on `stream` has finished.  Calls on different streams need
+ *   different workspaces.
+ * Other arguments, accuracy, non-finite behaviour and launch splitting as
+ * gemv_q2_batched; results are reproducible run to run, and within the
+ * accuracy bound of (not bit-equal to) gemv_q2_batched's.
+ */
+int gemv_q2_batched_ws(int64_t count, int64_t M, int64_t K,
+                       const uint8_t *const *Q, int64_t ldq,
+                       const uint16_t *const *S, int64_t lds,
+                       const float *const *x, float *const *y,
+                       void *workspace, int64_t workspace_bytes, gg_stream_t stream);
+
+/*
+ * Bytes of workspace gemv_q2_batched_ws needs for count products of M x K
+ * (0 when the batch does not cut its rows), or GG_ERR_INVALID_ARG for a
+ * negative or oversized size.  It depends on the sizes only.
+ */
+int64_t gemv_q2_batched_ws_size(int64_t count, int64_t M, int64_t K);
+
+/*
  * y[M] = W[M x K] . x[K] with W held as 4-bit codes and binary16 scales.
  *
  * 4-bit weight matrices sit beside the 2-bit one on the same path: two of the

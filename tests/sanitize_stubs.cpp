@@ -19,7 +19,7 @@ hipError_t launch_gemv_f32(int, int, int, const float *const *, int64_t, const f
 }
 
 hipError_t launch_gemv_q2(int, int, int, const uint8_t *const *, int64_t, const uint16_t *const *,
-                          int64_t, const float *const *, float *const *, hipStream_t) {
+                          int64_t, const float *const *, float *const *, float *, hipStream_t) {
     return hipErrorNotSupported;
 }
 

@@ -264,3 +264,30 @@ def test_gemv_f32_batched_validation():
     passes_checks(lambda: f(2, 4, 64, W, 64, x, y, None))
     # K = 0 reads no input: null W and x pass, only the outputs are checked
     passes_checks(lambda: f(2, 4, 0, _parr(0, 0), 0, _parr(0, 0), y, None))
+
+
+def test_gemv_q2_batched_ws_validation():
+    f, size = lib.gemv_q2_batched_ws, lib.gemv_q2_batched_ws_size
+    assert size(-1, 4, 6144) == bd.GG_ERR_INVALID_ARG
+    assert size(16, 1 << 31, 6144) == bd.GG_ERR_INVALID_ARG
+    assert size(16, 4, 6144) == 16 * 4 * 4 * 4
+    assert size(15, 4, 6144) == 0 and size(16, 4, 3072) == 0
+    n, M, K = 16, 4, 6144
+    need = size(n, M, K)
+    Q = _parr(*[PA + 0x10000 * b for b in range(n)])
+    S = _parr(*[PB + 0x10000 * b for b in range(n)])
+    x = _parr(*[PX] * n)
+    y = _parr(*[PC + 0x1000 * b for b in range(n)])
+    W = 0x50000000
+    # workspace missing, too small, misaligned
+    assert f(n, M, K, Q, 1536, S, 96, x, y, None, need, None) == bd.GG_ERR_INVALID_ARG
+    assert f(n, M, K, Q, 1536, S, 96, x, y, W, need - 4, None) == bd.GG_ERR_INVALID_ARG
+    assert f(n, M, K, Q, 1536, S, 96, x, y, W + 4, need, None) == bd.GG_ERR_INVALID_ARG
+    # workspace over an output, over an input
+    assert f(n, M, K, Q, 1536, S, 96, x, y, PC + 0x1000 * 3 - 16, need, None) == bd.GG_ERR_ALIAS
+    assert f(n, M, K, Q, 1536, S, 96, x, y, PX, need, None) == bd.GG_ERR_ALIAS
+    # the usual batch checks still apply
+    assert f(n, M, K, Q, 1535, S, 96, x, y, W, need, None) == bd.GG_ERR_INVALID_ARG
+    passes_checks(lambda: f(n, M, K, Q, 1536, S, 96, x, y, W, need, None))
+    # a batch that does not cut its rows ignores the workspace (NULL is fine)
+    passes_checks(lambda: f(15, M, K, Q, 1536, S, 96, x, y, None, 0, None))

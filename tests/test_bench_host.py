@@ -166,7 +166,7 @@ def test_summarize_counters(bench, tmp_path):
     """Medians per dispatch and the derived figures of a 40-product 2-bit
     batch: VALU instructions per lane per weight, issue share, L2 hit rate."""
     p = str(tmp_path / "c.db")
-    name = ("void gg::(anonymous namespace)::gemv_q2_idot<3, 16, 64>(int, long, long, "
+    name = ("void gg::(anonymous namespace)::gemv_q2_idot<3, 16, 64, false>(int, long, long, "
             "gg::(anonymous namespace)::PackedPtrs<64>)")
     vals = {"SQ_INSTS_VALU": 14.5e6, "SQ_ACTIVE_INST_VALU": 14.5e6, "GRBM_GUI_ACTIVE": 8.0e5,
             "SQ_INSTS_LDS": 7.0e5, "SQ_LDS_BANK_CONFLICT": 1.4e6, "TCC_HIT_sum": 1.0e5,

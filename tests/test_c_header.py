@@ -81,6 +81,28 @@ int main(void) {
         expect(gemv_f32_batched(0, 8, 8, NULL, 8, NULL, NULL, s), GG_OK, "empty fp32 batch");
     }
     {
+        const uint8_t *qs[16];
+        const uint16_t *ss[16];
+        const float *xs[16];
+        float *ys[16];
+        const int64_t need = gemv_q2_batched_ws_size(16, 16, 6144);
+        for (int b = 0; b < 16; ++b) {
+            qs[b] = Q;
+            ss[b] = S;
+            xs[b] = x;
+            ys[b] = y + 1024 * b;
+        }
+        if (need != 16 * 4 * 16 * 4) {
+            printf("FAIL workspace size %lld\n", (long long)need);
+            ++failures;
+        }
+        expect((int)gemv_q2_batched_ws_size(-1, 16, 6144), GG_ERR_INVALID_ARG, "negative count size");
+        expect(gemv_q2_batched_ws(16, 16, 6144, qs, 1536, ss, 96, xs, ys, NULL, need, s),
+               GG_ERR_INVALID_ARG, "null workspace");
+        expect(gemv_q2_batched_ws(16, 16, 6144, qs, 1536, ss, 96, xs, ys, (void *)C, need - 1, s),
+               GG_ERR_INVALID_ARG, "short workspace");
+    }
+    {
         const int codes[] = {GG_OK, GG_ERR_INVALID_ARG, GG_ERR_ALIAS, GG_ERR_NO_DEVICE,
                              GG_ERR_LAUNCH, 12345};
         for (unsigned i = 0; i < sizeof codes / sizeof codes[0]; ++i) {

@@ -2,7 +2,8 @@
 replayed: they allocate nothing, clear nothing with memsets and keep no state
 between calls, so a replay must redo exactly what an eager call does.  One
 graph holds the GEMM (plain, TN, NT and accumulating), the single and batched
-fp32 GEMV and the single and batched 2-bit and 4-bit GEMVs.  It is replayed five times, with
+fp32 GEMV, the single and batched 2-bit and 4-bit GEMVs, and a 2-bit batch
+whose rows are cut into slices through a workspace.  It is replayed five times, with
 eager library calls and torch work on the same buffers' neighbours in
 between, and after every replay each output is compared bit for bit with
 eager calls.  The accumulating product (beta = 1) grows by one term per
@@ -37,6 +38,8 @@ def test_capture_and_replay():
     xv = dev(inputs.normal(rng, (1536,)))
     q2 = [_packed(rng, 3000, 1536, 2) for _ in range(3)]
     q4 = _packed(rng, 3000, 1536, 4)
+    sl = [_packed(rng, 100, 6144, 2) for _ in range(16)]           # rows cut into slices
+    ws = t.empty(bd.gemv_q2_batched_ws_size(16, 100, 6144), dtype=t.uint8, device="cuda")
     f32 = dict(dtype=t.float32, device="cuda")
 
     def outputs():
@@ -44,7 +47,8 @@ def test_capture_and_replay():
                 "nt": t.empty((520, 330), **f32), "gemv": t.empty(2000, **f32),
                 "q2": t.empty(3000, **f32), "q4": t.empty(3000, **f32),
                 "q2b": [t.empty(3000, **f32) for _ in range(3)],
-                "gemvb": [t.empty(2000, **f32) for _ in range(2)]}
+                "gemvb": [t.empty(2000, **f32) for _ in range(2)],
+                "q2ws": [t.empty(100, **f32) for _ in range(16)]}
 
     def run(o, acc, stream):
         bd.gemm_f32(A, B, o["nn"], stream=stream)
@@ -57,6 +61,8 @@ def test_capture_and_replay():
         bd.gemv_q2_batched([q[0] for q in q2], [q[1] for q in q2], [q[2] for q in q2],
                            o["q2b"], stream=stream)
         bd.gemv_f32_batched([W, W], [xv, xv], o["gemvb"], stream=stream)
+        bd.gemv_q2_batched_ws([q[0] for q in sl], [q[1] for q in sl], [q[2] for q in sl],
+                              o["q2ws"], workspace=ws, stream=stream)
 
     def flat(o):
         return [host(v) for k in sorted(o) for v in (o[k] if isinstance(o[k], list) else [o[k]])]

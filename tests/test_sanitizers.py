@@ -70,6 +70,13 @@ EXTRA_CALLS = r"""
         if (st != GG_ERR_NO_DEVICE && st != GG_ERR_LAUNCH) { printf("FAIL valid batch %d\n", st); ++failures; }
         st = gemv_f32_batched(NB, 16, 16, ws, 16, xs, ys, s);
         if (st != GG_ERR_NO_DEVICE && st != GG_ERR_LAUNCH) { printf("FAIL valid f32 batch %d\n", st); ++failures; }
+        {
+            static uint8_t wsb[16 * 4 * 16 * 4 + 16];
+            void *ws = (void *)(((uintptr_t)wsb + 15) & ~(uintptr_t)15);
+            st = gemv_q2_batched_ws(16, 16, 6144, qs, 1536, ss, 96, xs, ys, ws,
+                                    gemv_q2_batched_ws_size(16, 16, 6144), s);
+            if (st != GG_ERR_NO_DEVICE && st != GG_ERR_LAUNCH) { printf("FAIL valid ws batch %d\n", st); ++failures; }
+        }
         ys[NB - 1] = ys[3];
         expect(gemv_f32_batched(NB, 16, 16, ws, 16, xs, ys, s), GG_ERR_ALIAS,
                "two outputs of an fp32 batch overlap");
