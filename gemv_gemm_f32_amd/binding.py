@@ -25,10 +25,12 @@ GG_ERR_INVALID_ARG = -1
 GG_ERR_ALIAS = -2
 GG_ERR_NO_DEVICE = -3
 GG_ERR_LAUNCH = -4
+GG_ERR_SCRATCH = -5
 
 ENTRY_POINTS = ("gemm_f32", "gemm_f32_tn", "gemm_f32_nt", "gemm_f32_ex", "gemv_f32",
                 "gemv_f32_batched", "gemv_q2", "gemv_q2_batched", "gemv_q2_batched_ws",
-                "gemv_q2_batched_ws_size", "gemv_q4", "gemv_q4_batched", "gg_strerror")
+                "gemv_q2_batched_ws_size", "gemv_q2_batched_noalloc", "gemv_q4",
+                "gemv_q4_batched", "gg_strerror")
 
 _lib = None
 
@@ -82,6 +84,8 @@ def load(path: str = LIB_PATH):
         f.restype = ctypes.c_int
     lib.gemv_q2_batched_ws.argtypes = [i64, i64, i64, pp, i64, pp, i64, pp, pp, vp, i64, vp]
     lib.gemv_q2_batched_ws.restype = ctypes.c_int
+    lib.gemv_q2_batched_noalloc.argtypes = [i64, i64, i64, pp, i64, pp, i64, pp, pp, vp]
+    lib.gemv_q2_batched_noalloc.restype = ctypes.c_int
     lib.gemv_q2_batched_ws_size.argtypes = [i64, i64, i64]
     lib.gemv_q2_batched_ws_size.restype = i64
     lib.gg_strerror.argtypes = [ctypes.c_int]
@@ -356,6 +360,12 @@ def gemv_q2_batched_ws(Qs, Ss, xs, ys=None, workspace=None, stream=None):
                                     xs[0].shape[0] if xs else 0)
         workspace = torch.empty(n, dtype=torch.uint8, device=Qs[0].device if Qs else "cuda")
     return _packed_batched("gemv_q2_batched_ws", Qs, Ss, xs, ys, stream, ws=workspace)
+
+
+def gemv_q2_batched_noalloc(Qs, Ss, xs, ys=None, stream=None):
+    """gemv_q2_batched_ws on the library's fixed per-GPU scratch buffer
+    instead of a workspace (outputs are allocated here when ys is None)."""
+    return _packed_batched("gemv_q2_batched_noalloc", Qs, Ss, xs, ys, stream)
 
 
 def gemv_q4_batched(Qs, Ss, xs, ys=None, stream=None):

@@ -209,10 +209,12 @@ int gemv_f32_batched(int64_t count, int64_t M, int64_t K, const float *const *W,
 
 namespace {
 
-// A caller's workspace, or none.
+// A caller's workspace (scratch false), or the library's fixed per-device
+// scratch buffer (scratch true: found after the device check).
 struct Workspace {
     void *p;
     int64_t bytes;
+    bool scratch;
 };
 
 // The checks and launch shared by the 2-bit and 4-bit entry points.  With a
@@ -239,7 +241,8 @@ int packed_batched(int bits, int64_t count, int64_t M, int64_t K, const uint8_t 
     // The workspace this batch uses, if any: 16-byte aligned, large enough,
     // and written like an output.
     const int64_t ws_floats = (ws && bits == 2) ? gg::gemv_q2_workspace_floats(count, M, K) : 0;
-    if (ws_floats > 0) {
+    if (ws_floats > 0 && ws->scratch && ws_floats * 4 > gg::SCRATCH_BYTES) return GG_ERR_SCRATCH;
+    if (ws_floats > 0 && !ws->scratch) {
         if (ws->bytes < ws_floats * 4 || bad_ptr(ws->p, 16) || wraps(ws->p, 1, ws_floats, ws_floats, 4))
             return GG_ERR_INVALID_ARG;
     }
@@ -256,13 +259,18 @@ int packed_batched(int bits, int64_t count, int64_t M, int64_t K, const uint8_t 
                 iv.push_back({span(x[b], 1, K, K, 4), false});
             }
         }
-        if (ws_floats > 0) iv.push_back({span(ws->p, 1, ws_floats, ws_floats, 4), true});
+        if (ws_floats > 0 && !ws->scratch)
+            iv.push_back({span(ws->p, 1, ws_floats, ws_floats, 4), true});
         if (!outputs_disjoint(iv)) return GG_ERR_ALIAS;
     }
     int cus = 0;
     if (int st = check_device(&cus)) return st;
     const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    float *wsp = ws_floats > 0 ? static_cast<float *>(ws->p) : nullptr;
+    float *wsp = nullptr;
+    if (ws_floats > 0) {
+        wsp = ws->scratch ? gg::device_scratch() : static_cast<float *>(ws->p);
+        if (wsp == nullptr) return GG_ERR_SCRATCH;
+    }
     return launch_status(bits == 2 ? gg::launch_gemv_q2((int)count, (int)M, (int)K, Q, ldq, S,
                                                         lds, x, y, wsp, hs)
                                    : gg::launch_gemv_q4((int)count, (int)M, (int)K, Q, ldq, S,
@@ -289,7 +297,14 @@ int gemv_q2_batched_ws(int64_t count, int64_t M, int64_t K, const uint8_t *const
                        int64_t ldq, const uint16_t *const *S, int64_t lds, const float *const *x,
                        float *const *y, void *workspace, int64_t workspace_bytes,
                        gg_stream_t stream) {
-    const Workspace ws{workspace, workspace_bytes};
+    const Workspace ws{workspace, workspace_bytes, false};
+    return packed_batched(2, count, M, K, Q, ldq, S, lds, x, y, &ws, stream);
+}
+
+int gemv_q2_batched_noalloc(int64_t count, int64_t M, int64_t K, const uint8_t *const *Q,
+                            int64_t ldq, const uint16_t *const *S, int64_t lds,
+                            const float *const *x, float *const *y, gg_stream_t stream) {
+    const Workspace ws{nullptr, 0, true};
     return packed_batched(2, count, M, K, Q, ldq, S, lds, x, y, &ws, stream);
 }
 
@@ -323,6 +338,9 @@ const char *gg_strerror(int status) {
         case GG_ERR_ALIAS: return "output overlaps an input";
         case GG_ERR_NO_DEVICE: return "no current HIP device, or it is not a gfx950 (MI355X)";
         case GG_ERR_LAUNCH: return "kernel launch failed";
+        case GG_ERR_SCRATCH:
+            return "the batch needs more than the library's fixed scratch buffer holds (4 MiB "
+                   "per GPU), or that buffer could not be located on the current device";
         default: return "unknown status";
     }
 }

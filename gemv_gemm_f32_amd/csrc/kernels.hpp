@@ -76,6 +76,12 @@ inline int64_t sliced_count(int64_t count, int64_t M, int64_t K) {
     return n >= 4 && n <= SLICED_MAX ? n : 0;
 }
 
+// The fixed per-device scratch buffer of the allocation-free entry point
+// (noalloc.hip): its size, and its device address on the current device
+// (found on first use there), or NULL if it cannot be had.
+constexpr int64_t SCRATCH_BYTES = int64_t(4) << 20;
+float *device_scratch();
+
 // Floats of workspace a 2-bit batch of this shape uses, 0 if none: one
 // launch's partial sums (the next launch of a batch over PACKED_MAX_BATCH
 // products reuses them).

@@ -44,6 +44,8 @@
  *    +-inf in rows that meet an infinity; a NaN scale makes its own row NaN.
  *  - Thread safety: the only global state is a per-device property cache
  *    filled once; every entry point may be called from several threads.
+ *    The one exception is gemv_q2_batched_noalloc, whose calls share one
+ *    scratch buffer per GPU: calls of it that overlap on one GPU race.
  */
 #ifndef GEMVGEMM_H
 #define GEMVGEMM_H
@@ -63,7 +65,9 @@ enum gg_status {
                                 pointer, leading dimension too small        */
     GG_ERR_ALIAS = -2,       /* output overlaps an input                     */
     GG_ERR_NO_DEVICE = -3,   /* no current HIP device, or it is not gfx950   */
-    GG_ERR_LAUNCH = -4       /* the kernel launch itself was rejected        */
+    GG_ERR_LAUNCH = -4,      /* the kernel launch itself was rejected        */
+    GG_ERR_SCRATCH = -5      /* gemv_q2_batched_noalloc: the batch needs more
+                                than the fixed scratch buffer holds           */
 };
 
 /*
@@ -244,6 +248,27 @@ int gemv_q2_batched_ws(int64_t count, int64_t M, int64_t K,
  * negative or oversized size.  It depends on the sizes only.
  */
 int64_t gemv_q2_batched_ws_size(int64_t count, int64_t M, int64_t K);
+
+/*
+ * gemv_q2_batched_ws for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the partial sums go to a scratch buffer of 4 MiB that the
+ * library holds on each GPU it runs on (a static device array, kept until
+ * the process ends) instead of a caller's workspace.  The call allocates
+ * nothing.  A batch whose workspace (gemv_q2_batched_ws_size) would exceed
+ * 4 MiB is rejected with GG_ERR_SCRATCH before anything runs.  One launch's
+ * partial sums are reused by the next, so that size stops growing at 64
+ * products (at 1,536 x 12,288: 64 x 8 slices x 1,536 rows x 4 bytes =
+ * 3 MiB).  Every call on a GPU
+ * shares that GPU's buffer, which keeps the last call's partial sums (no
+ * call needs it cleared): calls that overlap on one GPU, from other streams
+ * or threads, race and must not be made.  Arguments and results as
+ * gemv_q2_batched_ws, which it equals bit for bit.
+ */
+int gemv_q2_batched_noalloc(int64_t count, int64_t M, int64_t K,
+                            const uint8_t *const *Q, int64_t ldq,
+                            const uint16_t *const *S, int64_t lds,
+                            const float *const *x, float *const *y, gg_stream_t stream);
 
 /*
  * y[M] = W[M x K] . x[K] with W held as 4-bit codes and binary16 scales.

@@ -28,4 +28,6 @@ hipError_t launch_gemv_q4(int, int, int, const uint8_t *const *, int64_t, const 
     return hipErrorNotSupported;
 }
 
+float *device_scratch() { return nullptr; }
+
 }  // namespace gg

@@ -48,7 +48,7 @@ def test_exports_every_header_function():
 
 def test_strerror_covers_every_status():
     for st in (bd.GG_OK, bd.GG_ERR_INVALID_ARG, bd.GG_ERR_ALIAS,
-               bd.GG_ERR_NO_DEVICE, bd.GG_ERR_LAUNCH):
+               bd.GG_ERR_NO_DEVICE, bd.GG_ERR_LAUNCH, bd.GG_ERR_SCRATCH):
         msg = bd.strerror(st)
         assert msg and msg != "unknown status"
     assert bd.strerror(12345) == "unknown status"
@@ -291,3 +291,19 @@ def test_gemv_q2_batched_ws_validation():
     passes_checks(lambda: f(n, M, K, Q, 1536, S, 96, x, y, W, need, None))
     # a batch that does not cut its rows ignores the workspace (NULL is fine)
     passes_checks(lambda: f(15, M, K, Q, 1536, S, 96, x, y, None, 0, None))
+
+
+def test_gemv_q2_batched_noalloc_validation():
+    f = lib.gemv_q2_batched_noalloc
+    n, K = 64, 12288
+    Q = _parr(*[PA] * n)                       # inputs may be shared
+    S = _parr(*[PB] * n)
+    x = _parr(*[PX] * n)
+    y = _parr(*[PC + 0x10000 * b for b in range(n)])
+    assert f(-1, 16, K, Q, 3072, S, 192, x, y, None) == bd.GG_ERR_INVALID_ARG
+    assert f(n, 16, K, Q, 3071, S, 192, x, y, None) == bd.GG_ERR_INVALID_ARG
+    # partial sums beyond the fixed 4 MiB buffer: 64 x 8 slices x 2,049 rows
+    assert f(n, 2049, K, Q, 3072, S, 192, x, y, None) == bd.GG_ERR_SCRATCH
+    assert f(n, 16, K, Q, 3072, S, 192, x, _parr(*([PC] * n)), None) == bd.GG_ERR_ALIAS
+    passes_checks(lambda: f(n, 2048, K, Q, 3072, S, 192, x, y, None))   # exactly 4 MiB
+    passes_checks(lambda: f(15, 2049, K, Q, 3072, S, 192, x, y, None))  # rows not cut

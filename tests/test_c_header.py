@@ -104,7 +104,7 @@ int main(void) {
     }
     {
         const int codes[] = {GG_OK, GG_ERR_INVALID_ARG, GG_ERR_ALIAS, GG_ERR_NO_DEVICE,
-                             GG_ERR_LAUNCH, 12345};
+                             GG_ERR_LAUNCH, GG_ERR_SCRATCH, 12345};
         for (unsigned i = 0; i < sizeof codes / sizeof codes[0]; ++i) {
             const char *m = gg_strerror(codes[i]);
             if (m == NULL || strlen(m) == 0) {
