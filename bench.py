@@ -543,7 +543,11 @@ def write_traffic(fetch_db, write_db):
              "traffic_gemv_f32_12288x1536.json", ("gemv_f32.hip", "wave.hpp"), F32_ALG_BYTES),
             (lambda n: n.startswith("gemv_f32_kernel<1, 6, true, 64>"),
              "traffic_gemv_f32_batched_12288x1536.json", ("gemv_f32.hip", "wave.hpp"),
-             CALLS_PER_TOKEN * F32_ALG_BYTES)):
+             CALLS_PER_TOKEN * F32_ALG_BYTES),
+            (lambda n: n.startswith("gemv_q2_idot<3,") and n.split(" @")[0].endswith(", 64, true>"),
+             "traffic_gemv_q2_sliced_1536x12288.json", q2_srcs, CALLS_PER_TOKEN * QT_ALG_BYTES),
+            (lambda n: n.startswith("gemv_slices_sum<64>"),
+             "traffic_gemv_slices_sum_1536x12288.json", q2_srcs, CALLS_PER_TOKEN * QT_M * 4)):
         k = [n for n in fetch if match(n)]
         if not k:
             continue
@@ -580,21 +584,28 @@ def counters_run(torch, bd, inputs):
     eagerly, after one device-to-device copy of CALIBRATION_BYTES (the
     reference that scales rocprofv3's byte counters): 5 GEMMs at 2048^3, 128
     single 2-bit products and 4 batches of 40 over the 128-matrix set, the
-    same for 4-bit over its 64 matrices, and 48 fp32 GEMVs and 4 batches of
-    40 of them."""
+    same for 4-bit over its 64 matrices, 4 batches of 40 of the transposed
+    1,536 x 12,288 2-bit products through gemv_q2_batched_ws (rows cut into
+    slices) over its 128-matrix set, and 48 fp32 GEMVs and 4 batches of 40
+    of them."""
     dev = torch.device("cuda:0")
     A, B = inputs.large_square(3)
     dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
     dC = torch.empty((GEMM_N, GEMM_N), dtype=torch.float32, device=dev)
     dx = torch.from_numpy(inputs.q2_x()).to(dev)
 
-    def packed_set(gen, n):
+    def packed_set(gen, n, M=Q2_M, K=Q2_K):
         out = []
         for r in range(n):
-            Q, S = gen(r)
+            Q, S = gen(r, M, K)
             out.append((torch.from_numpy(Q).to(dev), torch.from_numpy(S.view(np.int16)).to(dev)))
         return out
     q2, q4 = packed_set(inputs.q2_weight, Q2_ROTATION), packed_set(inputs.q4_weight, Q4_ROTATION)
+    qt = packed_set(inputs.q2_weight, Q2_ROTATION, QT_M, QT_K)
+    dxt = torch.from_numpy(inputs.q2_x(QT_K)).to(dev)
+    dyts = [torch.empty(QT_M, dtype=torch.float32, device=dev) for _ in range(CALLS_PER_TOKEN)]
+    wst = torch.empty(bd.gemv_q2_batched_ws_size(CALLS_PER_TOKEN, QT_M, QT_K), dtype=torch.uint8,
+                      device=dev)
     Wf = [torch.from_numpy(inputs.gemv_f32_weight(r)).to(dev) for r in range(F32_ROTATION)]
     dxf = torch.from_numpy(inputs.gemv_f32_x()).to(dev)
     dy = torch.empty(Q2_M, dtype=torch.float32, device=dev)
@@ -615,6 +626,10 @@ def counters_run(torch, bd, inputs):
             idx = [(t * CALLS_PER_TOKEN + c) % rot for c in range(CALLS_PER_TOKEN)]
             batched([pset[i][0] for i in idx], [pset[i][1] for i in idx],
                     [dx] * CALLS_PER_TOKEN, ys=dys)
+    for t in range(4):
+        idx = [(t * CALLS_PER_TOKEN + c) % Q2_ROTATION for c in range(CALLS_PER_TOKEN)]
+        bd.gemv_q2_batched_ws([qt[i][0] for i in idx], [qt[i][1] for i in idx],
+                              [dxt] * CALLS_PER_TOKEN, ys=dyts, workspace=wst)
     for W in Wf:
         bd.gemv_f32(W, dxf, y=dy)
     for t in range(4):
@@ -1000,6 +1015,8 @@ def main():
     q4_traffic = traffic_from_profile("traffic_gemv_q4_12288x1536.json", psha)
     q4b_traffic = traffic_from_profile("traffic_gemv_q4_batched_12288x1536.json", psha)
     qt_traffic = traffic_from_profile("traffic_gemv_q2_1536x12288.json", psha)
+    qtw_traffic = traffic_from_profile("traffic_gemv_q2_sliced_1536x12288.json", psha)
+    qts_traffic = traffic_from_profile("traffic_gemv_slices_sum_1536x12288.json", psha)
     gf_traffic = traffic_from_profile("traffic_gemv_f32_12288x1536.json",
                                       src_sha("gemv_f32.hip", "wave.hpp"))
     gfb_traffic = traffic_from_profile("traffic_gemv_f32_batched_12288x1536.json",
@@ -1119,6 +1136,12 @@ def main():
                 "unit": "GB/s",
                 "us_per_gemv": qtw_us,
                 "frac": QT_ALG_BYTES / qtw_us / 1e3 / PEAK_HBM_GBS,
+                "roofline": roofline(
+                    "gemv_q2_idot sliced + gemv_slices_sum (40 x 1536x12288 per launch pair)",
+                    QT_ALG_BYTES, qtw_us,
+                    (qtw_traffic + qts_traffic) / CALLS_PER_TOKEN
+                    if qtw_traffic and qts_traffic else None,
+                    per_prod_note + "; both kernels, the partial sums included"),
             },
         },
         "gemv_f32": {

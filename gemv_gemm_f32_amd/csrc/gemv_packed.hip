@@ -746,10 +746,12 @@ hipError_t launch_chunk(int count, int M, int K, const uint8_t *const *Q, int64_
 //    lane per row adds them in a fixed pairwise tree: deterministic.
 //  * Slices.  Rows longer than 48 chunks (the transposed 12,288 -> 1,536
 //    shape) are cut into slices of 1,536 columns, each slice of each row
-//    block a workgroup of its own (blockIdx.z; the workgroups of a slice,
-//    which share its x, are dispatched together: interleaving the slices of
-//    each row block ran 5% slower).  The kernel then reads the slice's
-//    codes, scales and x from offsets of z slices and
+//    block a workgroup of its own.  The grid is row block x slice x
+//    product (blockIdx.x, y, z), so a product's slices of the same rows are
+//    read close together in time while 12 workgroups share each slice's x
+//    (slices outermost ran 4% slower, the slices of each row block
+//    interleaved 9%).  The kernel then reads the slice's codes, scales and
+//    x from offsets of z slices and
 //    writes its partial row sums, block z of M values per product, to a
 //    workspace; gemv_slices_sum adds a row's partials in slice order.  A
 //    slice is exactly the 24-chunk row the kernel is tuned for, with three
@@ -857,8 +859,9 @@ void gemv_q2_idot(int M, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
     constexpr int SL = (ROWS + 63) / 64;                   // 16-byte scale loads per lane
     __shared__ __attribute__((aligned(16))) Sm sm;
 
-    const int b = NB == 1 ? 0 : (int)blockIdx.y;
-    const int z = SLICED ? (int)blockIdx.z : 0;    // column slice
+    // sliced: blockIdx.y is the slice and blockIdx.z the product
+    const int b = NB == 1 ? 0 : (int)(SLICED ? blockIdx.z : blockIdx.y);
+    const int z = SLICED ? (int)blockIdx.y : 0;    // column slice
     const int w = (int)threadIdx.x >> 6, l = (int)threadIdx.x & 63;
     const int cl = l & 7, j = l >> 3, c = 8 * w + cl, u = j >> 1;
     const unsigned odd = 0u - (unsigned)(j & 1);   // all ones for the odd-column lanes
@@ -1113,8 +1116,16 @@ __global__ __launch_bounds__(256) void gemv_slices_sum(int M, int slices,
     const int r = (int)blockIdx.x * 256 + (int)threadIdx.x;
     if (r >= M) return;
     const float *p = part + (size_t)b * slices * M + r;
-    float v = p[0];
-    for (int q = 1; q < slices; ++q) v += p[(size_t)q * M];
+    // the loads of 8 slices at a time go out together, then the adds in order
+    float v = 0.f;
+    for (int q0 = 0; q0 < slices; q0 += 8) {
+        float t[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) t[q] = q0 + q < slices ? p[(size_t)(q0 + q) * M] : 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (q0 + q < slices) v = q0 + q == 0 ? t[q] : v + t[q];
+    }
     out.y[b][r] = v;
 }
 
@@ -1150,7 +1161,7 @@ hipError_t launch_sliced(int slices, int count, int M, const uint8_t *const *Q, 
         p.y[b] = part + (size_t)i * slices * M;
         o.y[b] = y[i];
     }
-    const dim3 grid((M + 8 * T - 1) / (8 * T), count, slices);
+    const dim3 grid((M + 8 * T - 1) / (8 * T), slices, count);
     hipError_t e = launch(gemv_q2_idot<W, T, NB, true>, grid, dim3(64 * W), s, M, ldq, lds, p);
     if (e != hipSuccess) return e;
     return launch(gemv_slices_sum<NB>, dim3((M + 255) / 256, count), dim3(256), s, M, slices,
