@@ -584,9 +584,9 @@ def counters_run(torch, bd, inputs):
     eagerly, after one device-to-device copy of CALIBRATION_BYTES (the
     reference that scales rocprofv3's byte counters): 5 GEMMs at 2048^3, 128
     single 2-bit products and 4 batches of 40 over the 128-matrix set, the
-    same for 4-bit over its 64 matrices, 4 batches of 40 of the transposed
-    1,536 x 12,288 2-bit products through gemv_q2_batched_ws (rows cut into
-    slices) over its 128-matrix set, and 48 fp32 GEMVs and 4 batches of 40
+    same for 4-bit over its 64 matrices, the transposed 1,536 x 12,288 2-bit
+    products over its 128-matrix set one by one and in 4 batches of 40
+    through gemv_q2_batched_ws (rows cut into slices), and 48 fp32 GEMVs and 4 batches of 40
     of them."""
     dev = torch.device("cuda:0")
     A, B = inputs.large_square(3)
@@ -626,6 +626,8 @@ def counters_run(torch, bd, inputs):
             idx = [(t * CALLS_PER_TOKEN + c) % rot for c in range(CALLS_PER_TOKEN)]
             batched([pset[i][0] for i in idx], [pset[i][1] for i in idx],
                     [dx] * CALLS_PER_TOKEN, ys=dys)
+    for Q, S in qt:
+        bd.gemv_q2(Q, S, dxt, y=dyts[0])
     for t in range(4):
         idx = [(t * CALLS_PER_TOKEN + c) % Q2_ROTATION for c in range(CALLS_PER_TOKEN)]
         bd.gemv_q2_batched_ws([qt[i][0] for i in idx], [qt[i][1] for i in idx],
