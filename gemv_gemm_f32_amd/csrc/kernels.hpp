@@ -62,11 +62,12 @@ hipError_t launch_gemv_q2(int count, int M, int K, const uint8_t *const *Q, int6
 // Batches of 2-bit products whose rows are long cut them into slices of
 // SLICE_K columns, each written to the workspace as partial row sums, when
 // a workspace is given: rows of 4 to SLICED_MAX slices, at least
-// SLICED_MIN_COUNT products (at 1,536 x 12,288, 8 products ran 8% slower
-// sliced than whole, 16 the same, 40 15% faster).  Slices of
+// SLICED_MIN_COUNT products (at 1,536 x 12,288, µs per product sliced
+// against whole: 4 products 2.46 / 2.39, 8: 1.67 / 1.77, 16: 1.32 / 1.49,
+// 40: 1.08 / 1.33).  Slices of
 // SLICE_K/512 waves each, as the integer-dot kernel is tuned for.
 constexpr int SLICE_K = 1536;
-constexpr int SLICED_MIN_COUNT = 16;
+constexpr int SLICED_MIN_COUNT = 8;
 constexpr int SLICED_MAX = 1024;
 
 // Slices per row for a batch of this shape, 0 where it is not cut.

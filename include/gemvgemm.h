@@ -220,7 +220,7 @@ int gemv_q2_batched(int64_t count, int64_t M, int64_t K,
  * same 2-bit product on the transposed shape (12,288 inputs -> 1,536
  * outputs), and section "What the kernel costs in a whole token" shows such
  * long rows need a deeper split than short ones.  With the workspace, a
- * batch of at least 16 products whose K is a multiple of 1,536 and at least
+ * batch of at least 8 products whose K is a multiple of 1,536 and at least
  * 6,144 cuts each row into K/1,536 slices handled by separate workgroups,
  * writes their partial row sums to the workspace, and adds each row's
  * partials in slice order (deterministic).  Other batches run exactly as

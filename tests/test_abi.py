@@ -271,7 +271,7 @@ def test_gemv_q2_batched_ws_validation():
     assert size(-1, 4, 6144) == bd.GG_ERR_INVALID_ARG
     assert size(16, 1 << 31, 6144) == bd.GG_ERR_INVALID_ARG
     assert size(16, 4, 6144) == 16 * 4 * 4 * 4
-    assert size(15, 4, 6144) == 0 and size(16, 4, 3072) == 0
+    assert size(7, 4, 6144) == 0 and size(16, 4, 3072) == 0
     n, M, K = 16, 4, 6144
     need = size(n, M, K)
     Q = _parr(*[PA + 0x10000 * b for b in range(n)])
@@ -290,7 +290,7 @@ def test_gemv_q2_batched_ws_validation():
     assert f(n, M, K, Q, 1535, S, 96, x, y, W, need, None) == bd.GG_ERR_INVALID_ARG
     passes_checks(lambda: f(n, M, K, Q, 1536, S, 96, x, y, W, need, None))
     # a batch that does not cut its rows ignores the workspace (NULL is fine)
-    passes_checks(lambda: f(15, M, K, Q, 1536, S, 96, x, y, None, 0, None))
+    passes_checks(lambda: f(7, M, K, Q, 1536, S, 96, x, y, None, 0, None))
 
 
 def test_gemv_q2_batched_noalloc_validation():
@@ -306,4 +306,4 @@ def test_gemv_q2_batched_noalloc_validation():
     assert f(n, 2049, K, Q, 3072, S, 192, x, y, None) == bd.GG_ERR_SCRATCH
     assert f(n, 16, K, Q, 3072, S, 192, x, _parr(*([PC] * n)), None) == bd.GG_ERR_ALIAS
     passes_checks(lambda: f(n, 2048, K, Q, 3072, S, 192, x, y, None))   # exactly 4 MiB
-    passes_checks(lambda: f(15, 2049, K, Q, 3072, S, 192, x, y, None))  # rows not cut
+    passes_checks(lambda: f(7, 2049, K, Q, 3072, S, 192, x, y, None))   # rows not cut

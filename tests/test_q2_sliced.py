@@ -6,7 +6,7 @@ the C ABI: the transposed 1,536 x 12,288 shape of the rotation set, ragged
 row counts, several slice counts, more than 64 products (the workspace reused
 by a second launch), x far from 1 and chunks of different magnitudes, exact
 integer sums, non-finite x in one slice, a NaN scale, padded rows, batches
-that do not cut their rows (fewer than 16 products, short rows, misaligned
+that do not cut their rows (fewer than 8 products, short rows, misaligned
 operands: same bits as gemv_q2_batched, workspace untouched), and the
 workspace checks.
 """
@@ -60,8 +60,8 @@ def _check_all(mats, xs, ys, what, step=1):
 def test_workspace_size_rule():
     assert bd.gemv_q2_batched_ws_size(40, 1536, 12288) == 40 * 8 * 1536 * 4
     assert bd.gemv_q2_batched_ws_size(130, 1536, 12288) == 64 * 8 * 1536 * 4
-    assert bd.gemv_q2_batched_ws_size(16, 100, 6144) == 16 * 4 * 100 * 4
-    assert bd.gemv_q2_batched_ws_size(15, 1536, 12288) == 0      # too few products
+    assert bd.gemv_q2_batched_ws_size(8, 100, 6144) == 8 * 4 * 100 * 4
+    assert bd.gemv_q2_batched_ws_size(7, 1536, 12288) == 0       # too few products
     assert bd.gemv_q2_batched_ws_size(40, 12288, 1536) == 0      # short rows
     assert bd.gemv_q2_batched_ws_size(40, 1536, 4608) == 0       # three slices
     assert bd.gemv_q2_batched_ws_size(40, 1536, 12800) == 0      # not a multiple of 1,536
@@ -91,7 +91,7 @@ def test_shapes_distinct_x(M, K):
     _check_all(mats, xs, _run(mats, xs), "%dx%d" % (M, K))
 
 
-@pytest.mark.parametrize("n", [16, 64, 65, 130])
+@pytest.mark.parametrize("n", [8, 64, 65, 130])
 def test_batch_sizes(n):
     """Up to two full launches and a partial third, which reuse the workspace
     in stream order."""
@@ -192,11 +192,11 @@ def test_padded_rows_are_ignored():
 
 @pytest.mark.parametrize("case", ["few", "short", "misaligned_x"])
 def test_batches_that_do_not_cut_rows(case):
-    """Fewer than 16 products, rows below 6,144 columns, or an x off 16 bytes:
+    """Fewer than 8 products, rows below 6,144 columns, or an x off 16 bytes:
     the batch runs gemv_q2_batched's kernels (same bits) and leaves the
     workspace as it was."""
     t = torch()
-    M, K, n = {"few": (500, 12288, 15), "short": (500, 3072, 16),
+    M, K, n = {"few": (500, 12288, 7), "short": (500, 3072, 16),
                "misaligned_x": (500, 6144, 16)}[case]
     mats = _mats(n, M, K, 60)
     rng = np.random.default_rng(61)

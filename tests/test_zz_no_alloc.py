@@ -50,7 +50,7 @@ def test_two_calls_in_a_row_second_smaller():
 
 
 def test_batch_that_does_not_cut_rows():
-    """Fewer than 16 products: no slices, the scratch buffer is not used,
+    """Fewer than 8 products: no slices, the scratch buffer is not used,
     and the result equals gemv_q2_batched's."""
     n, M, K = 5, 300, 12288
     mats = _mats(n, M, K, 3)
