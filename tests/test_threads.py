@@ -1,6 +1,7 @@
-"""GPU check of the header's statement that every entry point may be called
-from several host threads.  Eight threads, each with its own stream, call a
-mix of the entry points at once for several rounds; the ctypes calls release
+"""GPU check of the header's statement that every entry point but the
+allocation-free one may be called from several host threads.  Eight
+threads, each with its own stream (and its own workspace for the sliced
+2-bit batch), call a mix of the entry points at once for several rounds; the ctypes calls release
 the interpreter lock, so argument checks, the per-device cache and the
 launches overlap.  All operands and outputs are allocated and filled before
 the threads start, so the threads make no call but the library's.  The
@@ -36,6 +37,12 @@ def _operands(rng):
         Q = rng.integers(0, 256, (1200, 1536 // 4), dtype=np.uint8)
         S = rng.uniform(0.01, 0.05, (1200, 1536 // 64)).astype(np.float16).view(np.int16)
         d["q"].append((dev(Q), dev(S), dev(inputs.normal(rng, (1536,)))))
+    # a batch whose rows are cut into slices (workspace per call)
+    d["sl"] = []
+    for _ in range(8):
+        Q = rng.integers(0, 256, (100, 6144 // 4), dtype=np.uint8)
+        S = rng.uniform(0.01, 0.05, (100, 6144 // 64)).astype(np.float16).view(np.int16)
+        d["sl"].append((dev(Q), dev(S), dev(inputs.normal(rng, (6144,)))))
     return d
 
 
@@ -46,10 +53,17 @@ def _outputs(d):
     f32 = dict(dtype=t.float32, device="cuda")
     return {"gemm": t.empty((300, 260), **f32), "nt": t.empty((300, 260), **f32),
             "ex": d["C0"].clone(), "gemv": t.empty(1000, **f32), "q2": t.empty(1200, **f32),
-            "q2b": [t.empty(1200, **f32) for _ in range(3)]}
+            "q2b": [t.empty(1200, **f32) for _ in range(3)],
+            "gemvb": [t.empty(1000, **f32) for _ in range(2)],
+            "q2ws": [t.empty(100, **f32) for _ in range(8)]}
 
 
-def _run(d, o, stream):
+def _workspace():
+    t = torch()
+    return t.empty(bd.gemv_q2_batched_ws_size(8, 100, 6144), dtype=t.uint8, device="cuda")
+
+
+def _run(d, o, ws, stream):
     bd.gemm_f32(d["A"], d["B"], o["gemm"], stream=stream)
     bd.gemm_f32_nt(d["A"], d["Bt"], o["nt"], stream=stream)
     bd.gemm_f32_ex(d["A"], d["B"], o["ex"], 0.5, 1.5, stream=stream)
@@ -58,6 +72,9 @@ def _run(d, o, stream):
     bd.gemv_q2(Q, S, x, o["q2"], stream=stream)
     bd.gemv_q2_batched([q[0] for q in d["q"]], [q[1] for q in d["q"]], [q[2] for q in d["q"]],
                        o["q2b"], stream=stream)
+    bd.gemv_f32_batched([d["W"], d["W"]], [d["xv"], d["xv"]], o["gemvb"], stream=stream)
+    bd.gemv_q2_batched_ws([q[0] for q in d["sl"]], [q[1] for q in d["sl"]],
+                          [q[2] for q in d["sl"]], o["q2ws"], workspace=ws, stream=stream)
 
 
 def _flat(o):
@@ -69,11 +86,12 @@ def test_concurrent_calls_from_threads():
     d = _operands(np.random.default_rng(808))
     ref_out = _outputs(d)
     t.cuda.synchronize()
-    _run(d, ref_out, t.cuda.current_stream())
+    _run(d, ref_out, _workspace(), t.cuda.current_stream())
     ref = _flat(ref_out)
 
     streams = [t.cuda.Stream() for _ in range(THREADS)]
     outs = [[_outputs(d) for _ in range(ROUNDS)] for _ in range(THREADS)]
+    wss = [_workspace() for _ in range(THREADS)]   # one per thread: calls on a stream reuse it
     t.cuda.synchronize()
     errors = []
     start = threading.Barrier(THREADS)
@@ -82,7 +100,7 @@ def test_concurrent_calls_from_threads():
         try:
             start.wait()
             for r in range(ROUNDS):
-                _run(d, outs[i][r], streams[i])
+                _run(d, outs[i][r], wss[i], streams[i])
         except Exception as e:   # reported after the join
             errors.append((i, repr(e)))
 
