@@ -1,5 +1,9 @@
 """Helpers shared by the GPU parity tests: host<->device copies, the oracle
-acceptance check with a readable failure message, and guard canaries."""
+acceptance check with a readable failure message, the oracle's whole product
+over all host cores, and guard canaries."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 import oracle
@@ -46,3 +50,21 @@ def guarded(rows, cols, pad=64, fill=np.float32(1.2345e9)):
 def canaries_intact(buf, pad=64, fill=np.float32(1.2345e9)):
     h = host(buf)
     return bool(np.all(h[:pad] == fill) and np.all(h[-pad:] == fill))
+
+
+def oracle_product(layout, A, B):
+    """The oracle's whole product op(A).op(B) (layout "nn", "tn" with A stored
+    K x M, or "nt" with B stored N x K), its output rows split into blocks
+    over every usable host core: threads calling the C oracle, which runs
+    without the interpreter lock.  Each cell is the same plain dot product
+    as in one call.  Returns (C, bound) as fp64 arrays."""
+    fn = {"nn": oracle.gemm_nn, "tn": oracle.gemm_tn, "nt": oracle.gemm_nt}[layout]
+    M = A.shape[1] if layout == "tn" else A.shape[0]
+    cores = len(os.sched_getaffinity(0))
+    blocks = [b for b in np.array_split(np.arange(M), cores) if b.size]
+
+    def part(r):
+        return fn(A[:, r[0]:r[-1] + 1] if layout == "tn" else A[r[0]:r[-1] + 1], B)
+    with ThreadPoolExecutor(max_workers=len(blocks)) as pool:
+        parts = list(pool.map(part, blocks))
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])

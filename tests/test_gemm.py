@@ -11,7 +11,7 @@ import oracle
 from gemv_gemm_f32_amd import binding as bd
 from gemv_gemm_f32_amd import inputs
 from golden_io import load
-from gpu_util import assert_close, canaries_intact, dev, guarded, host, torch
+from gpu_util import assert_close, canaries_intact, dev, guarded, host, oracle_product, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -140,26 +140,35 @@ def _sample_cells(M, N, n=3000):
     return rows, cols
 
 
-def test_large_square_config_sampled():
+def test_large_square_config_every_cell():
+    """The 2048^3 configuration, every cell against the oracle's whole
+    product (split over the host's cores)."""
+    A, B = inputs.large_square(3)
+    C = _run("nn", A, B)
+    ref, bound = oracle_product("nn", A, B)
+    assert_close(C, ref, bound, "2048^3")
+    assert np.all(np.isfinite(C))
+
+
+def test_large_square_config_sampled_cells():
+    """The same product against cells the oracle computes one by one, a check
+    of the split above."""
     A, B = inputs.large_square(3)
     C = _run("nn", A, B)
     rows, cols = _sample_cells(2048, 2048)
     ref, bound = oracle.gemm_cells(A, B, rows, cols)
     assert_close(C[rows, cols], ref, bound, "2048^3")
-    assert np.all(np.isfinite(C))
 
 
 @pytest.mark.parametrize("op", [o[0] for o in inputs.GPT2_OPS])
-def test_gpt2_layer_products_sampled(op):
+def test_gpt2_layer_products_every_cell(op):
     t = _gpt2()
     name, layout, M, N, K, (an, bn) = next(o for o in inputs.GPT2_OPS if o[0] == op)
     A, B = t[an], t[bn]
     C = _run(layout, A, B)
     assert C.shape == (M, N)
-    rows, cols = _sample_cells(M, N)
-    ref, bound = oracle.gemm_cells(A, B, rows, cols, trans_a=layout == "tn",
-                                   trans_b=layout == "nt")
-    assert_close(C[rows, cols], ref, bound, op)
+    ref, bound = oracle_product(layout, A, B)
+    assert_close(C, ref, bound, op)
 
 
 _GPT2 = {}
