@@ -761,7 +761,10 @@ hipError_t launch_chunk(int count, int M, int K, const uint8_t *const *Q, int64_
 template <int WAVES, int T>
 struct IdotSmem {
     static constexpr int CPR = 8 * WAVES, ROWS = 8 * T, PS = CPR + 4;
-    unsigned dig[WAVES][8 * 48];          // per wave: 8 chunks x 8 lanes x 6 digit words
+    // per wave: 8 chunks x 8 lanes x 6 digit words, a chunk's 48 words padded
+    // to DS = 52, so that the 8 chunks' 16-byte reads fall on distinct banks
+    static constexpr int DS = 52;
+    unsigned dig[WAVES][8 * DS];
     uint16_t scl[WAVES][ROWS * 8];        // per wave: row x its 8 chunks' scales
     float part[ROWS * PS];                // row x chunk partial sums
     int bad[WAVES];
@@ -967,7 +970,7 @@ void gemv_q2_idot(int M, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
     }
     // ---- Swap digit words and scales inside the wave through LDS.
     {
-        u2 *dst = reinterpret_cast<u2 *>(&sm.dig[w][cl * 48 + j * 6]);
+        u2 *dst = reinterpret_cast<u2 *>(&sm.dig[w][cl * Sm::DS + j * 6]);
         dst[0] = u2{dg[0], dg[1]};
         dst[1] = u2{dg[2], dg[3]};
         dst[2] = u2{dg[4], dg[5]};
@@ -981,7 +984,7 @@ void gemv_q2_idot(int M, int64_t ldq, int64_t lds, PackedPtrs<NB> ptrs) {
     unsigned D[48];
 #pragma unroll
     for (int q = 0; q < 12; ++q) {
-        const u4 t = *reinterpret_cast<const u4 *>(&sm.dig[w][cl * 48 + 4 * q]);
+        const u4 t = *reinterpret_cast<const u4 *>(&sm.dig[w][cl * Sm::DS + 4 * q]);
         D[4 * q] = t.x;
         D[4 * q + 1] = t.y;
         D[4 * q + 2] = t.z;
